@@ -1,0 +1,247 @@
+"""CPU oracle for the SmoothQuant W8A8 linear -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The product path (``w8a8_int8_gemm_amd``) never
+does, and this package never imports the product.
+
+The arithmetic lives in ``sq_oracle.c`` (plain C loops, fp32 where the pages'
+own code quantizes in fp32, fp64 for the RMSNorm mean and the smoothing
+factor's powers).  This file is argument marshalling for it, plus the fp64
+whole-layer reference and error metric used to judge quantization error
+("SmoothQuant and W8A8", One layer, measured: ||XW - Q(X)Q(W)|| / ||XW||) and
+the fake-quant cross-path of the pages' PyTorch class ("Taming the Outliers",
+Implementation in PyTorch).
+
+Every function here is pinned by tests/test_oracle_pins.py against values the
+pages print, closed forms, brute force and library routines.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sq_oracle.c")
+_LIB = os.environ.get("SQ_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (-O2, OpenMP, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-std=c11", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        _lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I = ctypes.c_int
+        F = ctypes.c_float
+        _lib.oracle_rms_rscale.argtypes = [P, I, I64, I64, I64, F, P]
+        _lib.oracle_act_absmax.argtypes = [P, I, I64, I64, I64, I, P, F, I, P]
+        _lib.oracle_weight_absmax.argtypes = [P, I, I64, I64, I64, P]
+        _lib.oracle_smooth_factor.argtypes = [P, P, I64, F, P]
+        _lib.oracle_fold.argtypes = [P, I64, P, P, P, I, I64, I64, P]
+        _lib.oracle_quant_weight.argtypes = [P, I64, I64, I64, P, P]
+        _lib.oracle_quant_act.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, P, P]
+        _lib.oracle_int_gemm.argtypes = [P, P, I64, I64, I64, P]
+        _lib.oracle_int_gemm.restype = I64
+        _lib.oracle_epilogue.argtypes = [P, P, P, P, I64, I64, P]
+        _lib.oracle_f32_to_bf16.argtypes = [P, I64, P]
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _mat(x: np.ndarray):
+    """(array, is_bf16) for an fp32 or bf16-bits (uint16) matrix, C-contiguous."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return x, 1
+    if x.dtype != np.float32:
+        raise TypeError(f"oracle expects float32 or bf16 bits (uint16), got {x.dtype}")
+    return x, 0
+
+
+def _f32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+
+
+# ---------------------------------------------------------------------------
+# the steps
+# ---------------------------------------------------------------------------
+
+def rms_rscale(h: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    h, bf = _mat(h)
+    T, K = h.shape
+    r = np.empty(T, np.float32)
+    _load().oracle_rms_rscale(_p(h), bf, T, K, K, float(eps), _p(r))
+    return r
+
+
+def act_absmax(x: np.ndarray, *, norm: bool = False, gamma=None, eps: float = 1e-6,
+               a: Optional[np.ndarray] = None) -> np.ndarray:
+    """Per-input-channel absmax over calibration tokens; ``a`` given -> running max."""
+    x, bf = _mat(x)
+    T, K = x.shape
+    acc = a is not None
+    out = np.array(a, dtype=np.float32, copy=True) if acc else np.empty(K, np.float32)
+    g = _f32(gamma)
+    _load().oracle_act_absmax(_p(x), bf, T, K, K, int(norm), _p(g), float(eps), int(acc), _p(out))
+    return out
+
+
+def weight_absmax(w: np.ndarray) -> np.ndarray:
+    w, bf = _mat(w)
+    K, N = w.shape
+    out = np.empty(K, np.float32)
+    _load().oracle_weight_absmax(_p(w), bf, K, N, N, _p(out))
+    return out
+
+
+def smooth_factor(a: np.ndarray, wmax: np.ndarray, alpha: float) -> np.ndarray:
+    a = _f32(a)
+    wmax = _f32(wmax)
+    s = np.empty(a.shape[0], np.float32)
+    _load().oracle_smooth_factor(_p(a), _p(wmax), a.shape[0], float(np.float32(alpha)), _p(s))
+    return s
+
+
+def fold(s: np.ndarray, gamma=None, w: Optional[np.ndarray] = None):
+    """(gamma' = gamma/s, W^ = diag(s) W as fp32 or None)."""
+    s = _f32(s)
+    K = s.shape[0]
+    g = _f32(gamma)
+    gout = np.empty(K, np.float32)
+    what = None
+    wp, bf, N = None, 0, 0
+    if w is not None:
+        wp, bf = _mat(w)
+        N = wp.shape[1]
+        what = np.empty((K, N), np.float32)
+    _load().oracle_fold(_p(s), K, _p(g), _p(gout), _p(wp), bf, N, N, _p(what))
+    return gout, what
+
+
+def quant_weight(w_hat: np.ndarray):
+    """(qw [N,K] int8, w_scale [N] fp32) from the fp32 smoothed weight [K,N]."""
+    w_hat = np.ascontiguousarray(w_hat, dtype=np.float32)
+    K, N = w_hat.shape
+    qw = np.empty((N, K), np.int8)
+    ws = np.empty(N, np.float32)
+    _load().oracle_quant_weight(_p(w_hat), K, N, N, _p(qw), _p(ws))
+    return qw, ws
+
+
+def quant_act(x: np.ndarray, gamma_f=None, *, norm: bool = False, r: Optional[np.ndarray] = None,
+              eps: float = 1e-6):
+    """(q [T,K] int8, x_scale [T] fp32, r [T] fp32 or None)."""
+    x, bf = _mat(x)
+    T, K = x.shape
+    q = np.empty((T, K), np.int8)
+    xs = np.empty(T, np.float32)
+    rout = np.empty(T, np.float32) if norm else None
+    _load().oracle_quant_act(_p(x), bf, T, K, K, int(norm), _p(_f32(r)), float(eps),
+                             _p(_f32(gamma_f)), _p(q), _p(xs), _p(rout))
+    return q, xs, rout
+
+
+def int_gemm(q: np.ndarray, qw: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    qw = np.ascontiguousarray(qw, dtype=np.int8)
+    T, K = q.shape
+    N = qw.shape[0]
+    assert qw.shape[1] == K
+    acc = np.empty((T, N), np.int32)
+    ov = _load().oracle_int_gemm(_p(q), _p(qw), T, K, N, _p(acc))
+    if ov:
+        raise OverflowError(f"{ov} int32 accumulator overflows")
+    return acc
+
+
+def epilogue(acc: np.ndarray, x_scale, w_scale, bias=None) -> np.ndarray:
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    T, N = acc.shape
+    y = np.empty((T, N), np.float32)
+    _load().oracle_epilogue(_p(acc), _p(_f32(x_scale)), _p(_f32(w_scale)), _p(_f32(bias)), T, N, _p(y))
+    return y
+
+
+def to_bf16(y: np.ndarray) -> np.ndarray:
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, np.uint16)
+    _load().oracle_f32_to_bf16(_p(y), y.size, _p(out))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# whole layer
+# ---------------------------------------------------------------------------
+
+def calibrate(x_cal, w, alpha, *, norm=False, gamma=None, eps=1e-6):
+    """(a, wmax, s) -- the offline calibration phase."""
+    a = act_absmax(x_cal, norm=norm, gamma=gamma, eps=eps)
+    wm = weight_absmax(w)
+    return a, wm, smooth_factor(a, wm, alpha)
+
+
+def prepare_weight(w, s, gamma=None):
+    """(gamma', qw [N,K], w_scale [N]) -- fold then per-output-channel quant."""
+    gp, what = fold(s, gamma, w)
+    qw, ws = quant_weight(what)
+    return gp, qw, ws
+
+
+def linear(x, gamma_f, qw, w_scale, bias=None, *, norm=False, r=None, eps=1e-6, out_bf16=True):
+    """The online forward: quantize activations, integer GEMM, epilogue."""
+    q, xs, rr = quant_act(x, gamma_f, norm=norm, r=r, eps=eps)
+    acc = int_gemm(q, qw)
+    y = epilogue(acc, xs, w_scale, bias)
+    return dict(q=q, x_scale=xs, r=rr, acc=acc, y32=y, y=to_bf16(y) if out_bf16 else y)
+
+
+def reference_fp64(x, w, bias=None, *, norm=False, gamma=None, eps=1e-6) -> np.ndarray:
+    """Unsmoothed, unquantized layer in fp64: Y = norm?(X) @ W + b."""
+    xf = (x.astype(np.uint32) << 16).view(np.float32) if x.dtype == np.uint16 else x
+    wf = (w.astype(np.uint32) << 16).view(np.float32) if w.dtype == np.uint16 else w
+    X = xf.astype(np.float64)
+    if norm:
+        ms = (X * X).mean(axis=1, keepdims=True)
+        X = X / np.sqrt(ms + float(np.float32(eps)))
+        if gamma is not None:
+            X = X * np.asarray(gamma, np.float64)[None, :]
+    Y = X @ wf.astype(np.float64)
+    if bias is not None:
+        Y = Y + np.asarray(bias, np.float64)[None, :]
+    return Y
+
+
+def rel_error(y_ref: np.ndarray, y) -> float:
+    """||Y_ref - y||_F / ||Y_ref||_F in fp64 (y may be bf16 bits)."""
+    yf = (y.astype(np.uint32) << 16).view(np.float32) if y.dtype == np.uint16 else y
+    d = y_ref - yf.astype(np.float64)
+    return float(np.sqrt((d * d).sum()) / np.sqrt((y_ref * y_ref).sum()))
+
+
+def fake_quant_fp64(q, x_scale, qw, w_scale) -> np.ndarray:
+    """(q * Delta_t) @ (qw * Delta_n)^T in fp64 -- the dequantize-then-multiply
+    simulation of the pages' PyTorch class, before bias."""
+    A = q.astype(np.float64) * np.asarray(x_scale, np.float64)[:, None]
+    B = qw.astype(np.float64) * np.asarray(w_scale, np.float64)[:, None]
+    return A @ B.T

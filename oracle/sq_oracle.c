@@ -1,0 +1,240 @@
+/*
+ * sq_oracle.c -- plain, slow CPU reference for the SmoothQuant W8A8 linear.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call this code;
+ * only the tests, the smoke check and the benchmark's CPU-baseline leg do.
+ * It shares no code, header or constant with the GPU library.
+ *
+ * Every function is the plain definition of one step of the method, written
+ * as loops in IEEE fp32 (the precision the pages' own code computes the
+ * quantizer in) or fp64 where noted.  Build with -ffp-contract=off so that no
+ * multiply-add is fused.  OpenMP only splits independent rows or columns.
+ *
+ * Steps and where they are defined:
+ *   rms_rscale     RMSNorm reciprocal scale; the norm in front of q/k/v and
+ *                  gate/up ("SmoothQuant and W8A8", The trick).  The pages give
+ *                  no formula: r = 1/sqrt(mean(h^2) + eps), mean in fp64.
+ *   act_absmax     a_j = max_t |X[t,j]| over calibration tokens ("Taming the
+ *                  Outliers", System Architecture step C2 and calibrate()).
+ *   weight_absmax  w_j = max_n |W[j,n]|, j = input channel ("06 -- SmoothQuant",
+ *                  section 3).
+ *   smooth_factor  s_j = a_j^alpha / w_j^(1-alpha), clamped at 1e-5
+ *                  ("06 -- SmoothQuant", section 3; "SmoothQuant and W8A8",
+ *                  The trick; "Taming the Outliers", calibrate()).
+ *   fold           gamma'_j = gamma_j / s_j and W^[j,n] = s_j * W[j,n]
+ *                  ("06 -- SmoothQuant", sections 2 and 7).
+ *   quant_weight   one symmetric scale per output channel, Delta = amax/127,
+ *                  codes = round-half-even(W^/Delta) ("06 -- SmoothQuant",
+ *                  section 7; "Taming the Outliers", the quantization equation).
+ *   quant_act      one dynamic symmetric scale per token, same quantizer
+ *                  ("06 -- SmoothQuant", section 7).
+ *   int_gemm       acc = sum_k q[t,k] * qw[n,k] in int64 ("06 -- SmoothQuant",
+ *                  section 7: INT8 x INT8 -> INT32).
+ *   epilogue       y = (Delta_t * Delta_n) * acc + bias ("06 -- SmoothQuant",
+ *                  section 7; "Taming the Outliers", step I6).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static float bf16_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* element i of an fp32 (is_bf16 == 0) or bf16 (is_bf16 == 1) array */
+static float elem(const void *p, int is_bf16, int64_t i) {
+  return is_bf16 ? bf16_to_f32(((const uint16_t *)p)[i]) : ((const float *)p)[i];
+}
+
+/* symmetric INT8 code of the quotient v = x / Delta: nearest integer, ties to
+   even (the default rounding mode), clamped to [-127, 127]. */
+static int8_t code_of(float v) {
+  float r = nearbyintf(v);
+  if (r > 127.0f) r = 127.0f;
+  if (r < -127.0f) r = -127.0f;
+  return (int8_t)r;
+}
+
+int oracle_version(void) { return 1; }
+
+/* r[t] = fp32( 1 / sqrt( (sum_k h[t,k]^2) / K + eps ) ), sum and root in fp64 */
+void oracle_rms_rscale(const void *h, int is_bf16, int64_t T, int64_t K, int64_t ld,
+                       float eps, float *r) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      double v = (double)elem(h, is_bf16, t * ld + k);
+      acc += v * v;
+    }
+    double ms = acc / (double)K;
+    r[t] = (float)(1.0 / sqrt(ms + (double)eps));
+  }
+}
+
+/* a[j] = max_t |x[t,j]|; in norm mode the calibration activation is the
+   linear's input x = fp32(fp32(h * r_t) * gamma_j).  accumulate != 0 keeps a
+   running maximum across calls. */
+void oracle_act_absmax(const void *x, int is_bf16, int64_t T, int64_t K, int64_t ld,
+                       int norm, const float *gamma, float eps, int accumulate, float *a) {
+  float *r = NULL;
+  if (norm) {
+    r = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1));
+    oracle_rms_rscale(x, is_bf16, T, K, ld, eps, r);
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < K; ++j) {
+    float m = accumulate ? a[j] : 0.0f;
+    for (int64_t t = 0; t < T; ++t) {
+      float v = elem(x, is_bf16, t * ld + j);
+      if (norm) {
+        float hr = v * r[t];
+        v = hr * (gamma ? gamma[j] : 1.0f);
+      }
+      m = fmaxf(m, fabsf(v));
+    }
+    a[j] = m;
+  }
+  free(r);
+}
+
+/* wmax[j] = max_n |W[j,n]|, W row-major [K,N] with leading dimension ld */
+void oracle_weight_absmax(const void *w, int is_bf16, int64_t K, int64_t N, int64_t ld,
+                          float *wmax) {
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < K; ++j) {
+    float m = 0.0f;
+    for (int64_t n = 0; n < N; ++n) m = fmaxf(m, fabsf(elem(w, is_bf16, j * ld + n)));
+    wmax[j] = m;
+  }
+}
+
+/* s[j] = max( fp32( a_j^alpha / w_j^(1-alpha) ), 1e-5 ), quotient in fp64;
+   an all-zero weight row (w_j == 0) gets s_j = 1. */
+void oracle_smooth_factor(const float *a, const float *wmax, int64_t K, float alpha,
+                          float *s) {
+  double al = (double)alpha;
+  for (int64_t j = 0; j < K; ++j) {
+    if (wmax[j] == 0.0f) {
+      s[j] = 1.0f;
+      continue;
+    }
+    double q = pow((double)a[j], al) / pow((double)wmax[j], 1.0 - al);
+    float f = (float)q;
+    s[j] = f < 1e-5f ? 1e-5f : f;
+  }
+}
+
+/* gamma_out[j] = gamma_j / s_j (gamma NULL -> 1); w_hat[j,n] = W[j,n] * s_j
+   (fp32, row-major [K,N], leading dimension N); either output may be NULL. */
+void oracle_fold(const float *s, int64_t K, const float *gamma, float *gamma_out,
+                 const void *w, int is_bf16, int64_t N, int64_t ldw, float *w_hat) {
+  if (gamma_out)
+    for (int64_t j = 0; j < K; ++j) gamma_out[j] = (gamma ? gamma[j] : 1.0f) / s[j];
+  if (w_hat && w) {
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < K; ++j)
+      for (int64_t n = 0; n < N; ++n) w_hat[j * N + n] = elem(w, is_bf16, j * ldw + n) * s[j];
+  }
+}
+
+/* Per-output-channel symmetric INT8 of W^ [K,N] (fp32, leading dimension ld):
+   w_scale[n] = max_j |W^[j,n]| / 127;  qw[n*K + j] = code(W^[j,n] / w_scale[n]).
+   The codes are stored transposed, [N,K] with K contiguous. */
+void oracle_quant_weight(const float *w_hat, int64_t K, int64_t N, int64_t ld, int8_t *qw,
+                         float *w_scale) {
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    float amax = 0.0f;
+    for (int64_t j = 0; j < K; ++j) amax = fmaxf(amax, fabsf(w_hat[j * ld + n]));
+    float d = amax / 127.0f;
+    w_scale[n] = d;
+    for (int64_t j = 0; j < K; ++j)
+      qw[n * K + j] = (d == 0.0f) ? (int8_t)0 : code_of(w_hat[j * ld + n] / d);
+  }
+}
+
+/* Per-token dynamic symmetric INT8 of the smoothed activation.
+     norm == 0:  x^[t,k] = fp32(x[t,k] * gamma_f[k])
+     norm == 1:  x^[t,k] = fp32(fp32(h[t,k] * r_t) * gamma_f[k]),
+                 r_t from r_in if given, else computed as in oracle_rms_rscale
+   gamma_f NULL means 1.  x_scale[t] = max_k |x^| / 127; q = code(x^ / x_scale).
+   r_out (nullable) receives the r_t used. */
+void oracle_quant_act(const void *x, int is_bf16, int64_t T, int64_t K, int64_t ld, int norm,
+                      const float *r_in, float eps, const float *gamma_f, int8_t *q,
+                      float *x_scale, float *r_out) {
+  float *r = NULL;
+  if (norm) {
+    r = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1));
+    if (r_in)
+      memcpy(r, r_in, sizeof(float) * (size_t)T);
+    else
+      oracle_rms_rscale(x, is_bf16, T, K, ld, eps, r);
+    if (r_out) memcpy(r_out, r, sizeof(float) * (size_t)T);
+  }
+#pragma omp parallel
+  {
+    float *xh = (float *)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      float amax = 0.0f;
+      for (int64_t k = 0; k < K; ++k) {
+        float v = elem(x, is_bf16, t * ld + k);
+        if (norm) v = v * r[t];
+        xh[k] = v * (gamma_f ? gamma_f[k] : 1.0f);
+        amax = fmaxf(amax, fabsf(xh[k]));
+      }
+      float d = amax / 127.0f;
+      x_scale[t] = d;
+      for (int64_t k = 0; k < K; ++k)
+        q[t * K + k] = (d == 0.0f) ? (int8_t)0 : code_of(xh[k] / d);
+    }
+    free(xh);
+  }
+  free(r);
+}
+
+/* acc[t,n] = sum_k q[t,k] * qw[n,k] in int64; q is [T,K], qw is [N,K].
+   Returns the number of sums that do not fit in int32 (those are clamped). */
+int64_t oracle_int_gemm(const int8_t *q, const int8_t *qw, int64_t T, int64_t K, int64_t N,
+                        int32_t *acc) {
+  int64_t overflow = 0;
+#pragma omp parallel for schedule(static) reduction(+ : overflow)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t n = 0; n < N; ++n) {
+      int64_t s = 0;
+      for (int64_t k = 0; k < K; ++k) s += (int64_t)q[t * K + k] * (int64_t)qw[n * K + k];
+      if (s > INT32_MAX) { s = INT32_MAX; ++overflow; }
+      if (s < INT32_MIN) { s = INT32_MIN; ++overflow; }
+      acc[t * N + n] = (int32_t)s;
+    }
+  }
+  return overflow;
+}
+
+/* y[t,n] = fp32( fp32(x_scale[t] * w_scale[n]) * fp32(acc[t,n]) ) + bias[n]
+   (bias NULL -> no add), fp32 out [T,N]. */
+void oracle_epilogue(const int32_t *acc, const float *x_scale, const float *w_scale,
+                     const float *bias, int64_t T, int64_t N, float *y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t n = 0; n < N; ++n) {
+      float sc = x_scale[t] * w_scale[n];
+      float v = sc * (float)acc[t * N + n];
+      y[t * N + n] = bias ? v + bias[n] : v;
+    }
+}
+
+/* fp32 -> bf16 bits, round to nearest, ties to even (finite inputs) */
+void oracle_f32_to_bf16(const float *x, int64_t n, uint16_t *out) {
+  for (int64_t i = 0; i < n; ++i) {
+    uint32_t u;
+    memcpy(&u, &x[i], sizeof u);
+    uint32_t lsb = (u >> 16) & 1u;
+    out[i] = (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+  }
+}

@@ -1,0 +1,430 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values the
+pages print (tests/golden/), closed forms, brute force on tiny inputs, an
+independent high-precision evaluation, or a library routine for a step that
+reduces to one.  None of these needs a GPU.
+"""
+import math
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32 = np.float32
+
+
+def _codes_for(values, amax):
+    """Quantize a one-token row whose absmax is ``amax`` through the oracle."""
+    row = np.array([amax] + list(values), dtype=np.float32)[None, :]
+    q, xs, _ = oracle.quant_act(row, np.ones(row.shape[1], np.float32))
+    return q[0, 1:], float(xs[0])
+
+
+# ---------------------------------------------------------------------------
+# worked values printed on the pages
+# ---------------------------------------------------------------------------
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line)
+    return rows
+
+
+def _weight_codes_for(values, amax):
+    """Quantize a one-output-channel weight column whose absmax is ``amax``."""
+    col = np.array([amax] + list(values), dtype=np.float32)[:, None]
+    qw, ws = oracle.quant_weight(col)
+    return qw[0, 1:], float(ws[0])
+
+
+@pytest.mark.parametrize("path", ["activation", "weight"])
+def test_quantizer_worked_values(path):
+    rows = _golden_rows("quantizer_worked.txt")
+    assert len(rows) >= 9
+    fn = _codes_for if path == "activation" else _weight_codes_for
+    for r in rows:
+        amax, value, delta_printed, tol, code = r.split()
+        q, d = fn([float(value)], float(amax))
+        assert abs(d - float(delta_printed)) <= float(tol), r
+        assert int(q[0]) == int(code), (r, int(q[0]))
+
+
+def test_smoothing_worked_values():
+    for r in _golden_rows("smoothing_worked.txt"):
+        _, rest = r.split(None, 1)
+        vec, s, ch, expect = [p.strip() for p in rest.split(";")]
+        x = np.array([float(v) for v in vec.split()], np.float32)
+        s = np.array([float(v) for v in s.split()], np.float32)
+        ch = int(ch)
+        gp, _ = oracle.fold(s)
+        # activations are divided by s: x * (1/s)
+        smoothed = F32(x[ch] * gp[ch])
+        assert abs(abs(float(smoothed)) - float(expect)) < 2e-6, r
+        # the matching weight row is multiplied by s, the other rows untouched
+        w = np.arange(len(x) * 3, dtype=np.float32).reshape(len(x), 3) + 1
+        _, what = oracle.fold(s, None, w)
+        np.testing.assert_array_equal(what[ch], w[ch] * s[ch])
+        for j in range(len(x)):
+            if s[j] == 1:
+                np.testing.assert_array_equal(what[j], w[j])
+
+
+# ---------------------------------------------------------------------------
+# closed forms of the smoothing factor ("06 -- SmoothQuant" section 3;
+# "SmoothQuant and W8A8", The trick; "SmoothQuant: Weight-Only vs W8A8",
+# Migration Strength)
+# ---------------------------------------------------------------------------
+
+def _tiny():
+    return synth.make_inputs(synth.WORKLOADS["tiny"])
+
+
+def test_alpha_one_every_channel_peaks_at_one():
+    inp = _tiny()
+    a, wm, s = oracle.calibrate(inp.x_cal, inp.w, 1.0)
+    np.testing.assert_array_equal(s, np.maximum(a, F32(1e-5)))
+    # dividing form (the pages' x / s): the peak is exactly 1 for every channel
+    xc = inp.as_f32(inp.x_cal)
+    peaks = np.abs(xc / s[None, :]).max(axis=0)
+    np.testing.assert_array_equal(peaks, np.ones_like(peaks))
+    # folded form x * fp32(1/s): within one rounding of 1
+    gp, _ = oracle.fold(s)
+    peaks_f = np.abs(xc * gp[None, :]).max(axis=0)
+    assert np.all(np.abs(peaks_f - 1) <= 2 ** -23)
+
+
+def test_alpha_zero_is_inverse_weight_max():
+    inp = _tiny()
+    a, wm, s = oracle.calibrate(inp.x_cal, inp.w, 0.0)
+    # s_j = 1 / max|W_j| (not "no smoothing")
+    np.testing.assert_array_equal(s, F32(1.0) / wm)
+    assert not np.allclose(s, 1.0)
+
+
+def test_weight_absmax_indexes_input_rows():
+    w = np.zeros((5, 7), np.float32)
+    w[2, 6] = -3.0   # input channel 2
+    w[4, 0] = 0.5
+    wm = oracle.weight_absmax(w)
+    np.testing.assert_array_equal(wm, np.array([0, 0, 3.0, 0, 0.5], np.float32))
+
+
+def test_smoothing_factor_matches_high_precision():
+    """s_j against an independent 40-digit evaluation of a^alpha / w^(1-alpha)."""
+    getcontext().prec = 40
+    rng = np.random.default_rng(7)
+    a = (rng.uniform(0.01, 200.0, 300)).astype(np.float32)
+    w = (rng.uniform(0.001, 0.5, 300)).astype(np.float32)
+    for alpha in (0.1, 0.25, 0.5, 0.75, 0.85, 1.0):
+        s = oracle.smooth_factor(a, w, alpha)
+        al = Decimal(float(F32(alpha)))
+        for j in range(len(a)):
+            A = Decimal(float(a[j]))
+            W = Decimal(float(w[j]))
+            exact = (al * A.ln()).exp() / ((Decimal(1) - al) * W.ln()).exp()
+            ref = F32(float(exact))
+            # exact equality unless the value sits on an fp32 rounding boundary
+            if s[j] != ref:
+                assert abs(float(s[j]) - float(exact)) <= 0.5000001 * np.spacing(s[j]), (alpha, j)
+
+
+def test_smoothing_factor_guards():
+    a = np.array([0.0, 5.0, 3.0], np.float32)
+    w = np.array([0.2, 0.0, 1e12], np.float32)
+    s = oracle.smooth_factor(a, w, 0.5)
+    assert s[0] == F32(1e-5)            # dead channel: clamp at 1e-5
+    assert s[1] == 1.0                  # all-zero weight row: s = 1
+    assert s[2] == F32(1e-5)            # tiny quotient clamps too
+
+
+# ---------------------------------------------------------------------------
+# the invariance Y = (X diag(s)^-1)(diag(s) W)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("alpha", [0.1, 0.5, 0.85, 1.0])
+def test_invariance_fp64_and_folded(alpha):
+    inp = _tiny()
+    _, _, s = oracle.calibrate(inp.x_cal, inp.w, alpha)
+    X = inp.as_f32(inp.x).astype(np.float64)
+    W = inp.as_f32(inp.w).astype(np.float64)
+    Y = X @ W
+    sd = s.astype(np.float64)
+    Y2 = (X / sd[None, :]) @ (sd[:, None] * W)
+    assert np.linalg.norm(Y2 - Y) / np.linalg.norm(Y) < 1e-12
+    # the oracle's folded fp32 tensors: gamma' = 1/s on X, W^ = diag(s) W
+    gp, what = oracle.fold(s, None, inp.w)
+    Y3 = (X * gp.astype(np.float64)[None, :]) @ what.astype(np.float64)
+    assert np.linalg.norm(Y3 - Y) / np.linalg.norm(Y) < 1e-5
+
+
+def test_fold_into_norm_weight():
+    rng = np.random.default_rng(3)
+    s = rng.uniform(0.1, 30, 64).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, 64).astype(np.float32)
+    gp, _ = oracle.fold(s, g)
+    np.testing.assert_array_equal(gp, g / s)
+
+
+# ---------------------------------------------------------------------------
+# quantizer: brute force and invariants ("Taming the Outliers", the
+# quantization equation; "SmoothQuant: Weight-Only vs W8A8", Step Size)
+# ---------------------------------------------------------------------------
+
+def _nearest_code_bruteforce(v, d):
+    """Search all 255 codes for the one nearest v (exact in fp64), ties to even."""
+    best, berr = None, None
+    for c in range(-127, 128):
+        e = abs(float(v) - c * float(d))
+        if best is None or e < berr or (e == berr and c % 2 == 0):
+            best, berr = c, e
+    return best, berr
+
+
+def test_bruteforce_8x8x8_whole_layer():
+    rng = np.random.default_rng(11)
+    T = K = N = 8
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    x[:, 2] *= 30
+    w = (rng.standard_normal((K, N)) * 0.1).astype(np.float32)
+    xc = rng.standard_normal((16, K)).astype(np.float32)
+    xc[:, 2] *= 30
+    a, wm, s = oracle.calibrate(xc, w, 0.5)
+    gp, qw, ws = oracle.prepare_weight(w, s)
+    _, what = oracle.fold(s, None, w)
+    out = oracle.linear(x, gp, qw, ws, None, out_bf16=False)
+    q, xs = out["q"], out["x_scale"]
+    # activation codes: nearest code on the grid, unless the fp32 quotient sits
+    # on a half-integer boundary (not the case for this draw; checked)
+    for t in range(T):
+        for k in range(K):
+            xh = F32(x[t, k] * gp[k])
+            c, _ = _nearest_code_bruteforce(xh, xs[t])
+            qq = float(xh) / float(xs[t])
+            assert abs(abs(qq - math.floor(qq)) - 0.5) > 1e-4
+            assert q[t, k] == c
+    for n in range(N):
+        for k in range(K):
+            c, _ = _nearest_code_bruteforce(what[k, n], ws[n])
+            assert qw[n, k] == c
+    # integer GEMM: plain triple loop in Python integers
+    for t in range(T):
+        for n in range(N):
+            assert out["acc"][t, n] == sum(int(q[t, k]) * int(qw[n, k]) for k in range(K))
+    # absmax against Python max
+    for j in range(K):
+        assert a[j] == max(abs(float(v)) for v in xc[:, j])
+        assert wm[j] == max(abs(float(v)) for v in w[j, :])
+
+
+def test_quantizer_ties_to_even_and_range():
+    # amax 127 -> Delta = 1 exactly, so quotients are the values themselves
+    vals = [2.5, 3.5, -2.5, -0.5, 0.5, 1.5, 126.5, -126.5, 0.49999997]
+    q, d = _codes_for(vals, 127.0)
+    assert d == 1.0
+    assert list(q) == [2, 4, -2, 0, 0, 2, 126, -126, 0]
+    # the largest magnitude maps to exactly +-127 and -128 never appears
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((50, 300)).astype(np.float32) * rng.uniform(0.01, 100, (50, 1)).astype(np.float32)
+    q, xs, _ = oracle.quant_act(x, np.ones(300, np.float32))
+    assert q.min() >= -127 and q.max() <= 127
+    np.testing.assert_array_equal(np.abs(q).max(axis=1), np.full(50, 127))
+
+
+def test_quantizer_half_step_bound_and_power_of_two_scaling():
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((40, 512)) * rng.uniform(0.1, 10, (40, 1))).astype(np.float32)
+    x[:, 17] *= 25
+    q, xs, _ = oracle.quant_act(x, np.ones(512, np.float32))
+    err = np.abs(x.astype(np.float64) - q.astype(np.float64) * xs[:, None].astype(np.float64))
+    bound = xs[:, None].astype(np.float64) * (0.5 + 2.0 ** -17)
+    assert np.all(err <= bound)
+    for k in (-3, 1, 6):
+        q2, xs2, _ = oracle.quant_act((x * F32(2.0 ** k)).astype(np.float32), np.ones(512, np.float32))
+        np.testing.assert_array_equal(q2, q)
+        np.testing.assert_array_equal(xs2, xs * F32(2.0 ** k))
+
+
+def test_weight_quant_half_step_bound():
+    rng = np.random.default_rng(10)
+    what = (rng.standard_normal((300, 40)) * rng.uniform(0.01, 3, (1, 40))).astype(np.float32)
+    what[17] *= 20
+    qw, ws = oracle.quant_weight(what)
+    err = np.abs(what.T.astype(np.float64) - qw.astype(np.float64) * ws[:, None].astype(np.float64))
+    assert np.all(err <= ws[:, None].astype(np.float64) * (0.5 + 2.0 ** -17))
+    np.testing.assert_array_equal(np.abs(qw).max(axis=1), np.full(40, 127))
+
+
+def test_zero_rows_and_columns():
+    x = np.zeros((3, 64), np.float32)
+    x[1, 5] = 2.0
+    q, xs, _ = oracle.quant_act(x, np.ones(64, np.float32))
+    assert xs[0] == 0 and xs[2] == 0 and np.all(q[0] == 0) and np.all(q[2] == 0)
+    assert q[1, 5] == 127
+    what = np.zeros((64, 4), np.float32)
+    what[3, 1] = -0.5
+    qw, ws = oracle.quant_weight(what)
+    assert ws[0] == 0 and np.all(qw[0] == 0) and qw[1, 3] == -127
+    acc = oracle.int_gemm(q, qw)
+    y = oracle.epilogue(acc, xs, ws, np.array([1, 2, 3, 4], np.float32))
+    np.testing.assert_array_equal(y[0], [1, 2, 3, 4])
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm reciprocal scale (norm named in "SmoothQuant and W8A8", The trick)
+# ---------------------------------------------------------------------------
+
+def test_rms_rscale_closed_forms():
+    eps = 1e-6
+    h = np.full((1, 256), 3.0, np.float32)
+    r = oracle.rms_rscale(h, eps)
+    assert r[0] == F32(1.0 / math.sqrt(9.0 + float(F32(eps))))
+    h = np.tile(np.array([1.0, -1.0], np.float32), (2, 64))
+    h[1] *= 4
+    r = oracle.rms_rscale(h, eps)
+    assert r[0] == F32(1.0 / math.sqrt(1.0 + float(F32(eps))))
+    assert r[1] == F32(1.0 / math.sqrt(16.0 + float(F32(eps))))
+    # bf16 input is widened exactly
+    hb = synth.f32_to_bf16_bits(h)
+    np.testing.assert_array_equal(oracle.rms_rscale(hb, eps), r)
+
+
+def test_rms_rscale_against_fsum():
+    rng = np.random.default_rng(2)
+    h = rng.standard_normal((20, 1000)).astype(np.float32)
+    h[:, 7] *= 50
+    r = oracle.rms_rscale(h, 1e-6)
+    for t in range(20):
+        ms = math.fsum(float(v) * float(v) for v in h[t]) / 1000
+        ref = F32(1.0 / math.sqrt(ms + float(F32(1e-6))))
+        assert abs(float(r[t]) - float(ref)) <= float(np.spacing(ref))
+
+
+def test_norm_mode_activation_order():
+    """x^ = fp32(fp32(h * r) * gamma') in norm mode, for quant and calibration."""
+    rng = np.random.default_rng(4)
+    h = rng.standard_normal((6, 128)).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, 128).astype(np.float32)
+    r = oracle.rms_rscale(h)
+    q, xs, rr = oracle.quant_act(h, g, norm=True)
+    np.testing.assert_array_equal(rr, r)
+    xh = ((h * r[:, None]).astype(np.float32) * g[None, :]).astype(np.float32)
+    q2, xs2, _ = oracle.quant_act(xh, None)
+    np.testing.assert_array_equal(q, q2)
+    np.testing.assert_array_equal(xs, xs2)
+    a = oracle.act_absmax(h, norm=True, gamma=g)
+    np.testing.assert_array_equal(a, np.abs(xh).max(axis=0))
+
+
+def test_calibration_running_max():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((100, 64)).astype(np.float32)
+    a1 = oracle.act_absmax(x[:40])
+    a2 = oracle.act_absmax(x[40:], a=a1)
+    np.testing.assert_array_equal(a2, np.abs(x).max(axis=0))
+
+
+# ---------------------------------------------------------------------------
+# integer GEMM and epilogue
+# ---------------------------------------------------------------------------
+
+def test_int_gemm_matches_numpy_int64():
+    rng = np.random.default_rng(12)
+    q = rng.integers(-127, 128, (37, 320), dtype=np.int8)
+    qw = rng.integers(-127, 128, (53, 320), dtype=np.int8)
+    acc = oracle.int_gemm(q, qw)
+    ref = q.astype(np.int64) @ qw.astype(np.int64).T
+    np.testing.assert_array_equal(acc, ref)
+
+
+def test_int_gemm_extreme_fits_int32():
+    K = 8192
+    q = np.full((2, K), 127, np.int8)
+    q[1] = -127
+    qw = np.full((3, K), 127, np.int8)
+    acc = oracle.int_gemm(q, qw)
+    assert acc[0, 0] == 127 * 127 * K and acc[1, 2] == -127 * 127 * K
+
+
+def test_epilogue_equals_fake_quant_and_bound():
+    inp = _tiny()
+    _, _, s = oracle.calibrate(inp.x_cal, inp.w, 0.5)
+    gp, qw, ws = oracle.prepare_weight(inp.w, s)
+    out = oracle.linear(inp.x, gp, qw, ws, inp.bias, out_bf16=False)
+    y_sim = oracle.fake_quant_fp64(out["q"], out["x_scale"], qw, ws) + inp.bias[None, :].astype(np.float64)
+    y = out["y32"].astype(np.float64)
+    tol = 4 * 2.0 ** -24 * (np.abs(y_sim) + np.abs(inp.bias)[None, :]) + 1e-30
+    assert np.all(np.abs(y - y_sim) <= tol)
+    # a-priori quantization error bound against the exact smoothed product
+    X = inp.as_f32(inp.x)
+    xh = (X * gp[None, :]).astype(np.float64)
+    _, what = oracle.fold(s, None, inp.w)
+    Wh = what.astype(np.float64)
+    exact = xh @ Wh + inp.bias[None, :]
+    xsd = out["x_scale"].astype(np.float64)[:, None]
+    wsd = ws.astype(np.float64)[None, :]
+    bound = (np.abs(xh).sum(1, keepdims=True) * wsd / 2 + xsd * np.abs(Wh).sum(0, keepdims=True) / 2
+             + X.shape[1] * xsd * wsd / 4) * (1 + 1e-5) + 1e-6 * np.abs(exact)
+    assert np.all(np.abs(y - exact) <= bound)
+
+
+def test_bf16_rounding_of_output():
+    y = np.array([1.0, 1.00390625, 1.01171875, -2.5, 3.0e-3, 1.0 + 2 ** -8 + 2 ** -20], np.float32)
+    b = oracle.to_bf16(y)
+    back = synth.bf16_bits_to_f32(b)
+    # ties to even at 1 + 2^-8 (-> 1.0) and 1 + 3*2^-8 (-> 1 + 2^-6); above the tie rounds up
+    assert back[0] == 1.0 and back[1] == 1.0 and back[2] == F32(1.015625)
+    assert back[3] == -2.5 and back[5] == F32(1.0078125)
+    assert abs(back[4] - 3.0e-3) <= 3.0e-3 * 2 ** -8
+
+
+# ---------------------------------------------------------------------------
+# qualitative claims: smoothing cuts INT8 error on outlier data
+# ("SmoothQuant and W8A8", One layer, measured; "Taming the Outliers",
+#  evaluation script)
+# ---------------------------------------------------------------------------
+
+def _layer_error(inp, alpha):
+    X, W = inp.x, inp.w
+    if alpha is None:       # unsmoothed point: s = 1
+        s = np.ones(inp.wl.K, np.float32)
+    else:
+        _, _, s = oracle.calibrate(inp.x_cal, W, alpha)
+    gp, qw, ws = oracle.prepare_weight(W, s)
+    out = oracle.linear(X, gp, qw, ws, None, out_bf16=False)
+    ref = oracle.reference_fp64(X, W)
+    return oracle.rel_error(ref, out["y32"])
+
+
+def test_smoothing_reduces_error_tiny():
+    inp = _tiny()
+    e0 = _layer_error(inp, None)
+    e5 = _layer_error(inp, 0.5)
+    assert e5 < e0 / 2, (e0, e5)
+
+
+def test_evaluation_script_shape():
+    """128 -> 64 linear, 100 calibration and 10 test samples, 5% of the
+    channels multiplied by 50, alpha 0.5: smoothed error below unsmoothed."""
+    rng = np.random.default_rng(0)
+    xc = rng.standard_normal((100, 128)).astype(np.float32)
+    xt = rng.standard_normal((10, 128)).astype(np.float32)
+    idx = rng.permutation(128)[: int(128 * 0.05)]
+    xc[:, idx] *= 50
+    xt[:, idx] *= 50
+    W = rng.standard_normal((128, 64)).astype(np.float32)
+    ref = oracle.reference_fp64(xt, W)
+    errs = []
+    for s in (np.ones(128, np.float32), oracle.calibrate(xc, W, 0.5)[2]):
+        gp, qw, ws = oracle.prepare_weight(W, s)
+        errs.append(oracle.rel_error(ref, oracle.linear(xt, gp, qw, ws, out_bf16=False)["y32"]))
+    assert errs[1] < errs[0], errs
