@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Benchmark of the SmoothQuant W8A8 linear on one MI355X.
+
+One step is one pass of the whole path over one batch of the 4096-wide
+query-projection prefill workload (T = 8192 tokens, K = N = 4096, 8192
+calibration tokens, alpha 0.5, bf16 in and out), inputs resident in HBM:
+
+  sq_calibrate    activation absmax over X_cal, weight absmax, s
+  sq_smooth_fold  gamma' = 1/s
+  sq_quant_weight per-output-channel INT8 weight (fold fused)
+  sq_quant_act    per-token INT8 activations          } together: sq_w8a8_linear
+  sq_gemm_w8a8    INT8 MFMA GEMM + dequant/bias epilogue }
+
+`value` is 2*T*K*N integer ops per step / step time (TOPS).  Every kernel is
+also timed on its own with HIP events on the stream it runs on; the roofline
+object is for the GEMM (MFMA bound, against the INT8 dense peak).  The CPU
+oracle is timed on the host on the same inputs (a bounded sample of tokens).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W8A8 smoothed linear TOPS + % of MI355X INT8 MFMA peak (T=8192,K=N=4096)"
+PEAK_INT8_TOPS = 5000.0     # MI355X dense INT8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+WORKLOAD = "qproj_prefill"
+COUNTERS = os.path.join(ROOT, "profiles", "gemm_w8a8_qproj_prefill_counters.json")
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def _kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("k_gemm.hip", "sq_common.h"):
+        with open(os.path.join(ROOT, "w8a8_int8_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(gemm_launch_bytes_alg: float):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256_16") != _kernel_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, wl, target_s: float):
+    import numpy as np  # noqa: F401
+
+    import oracle
+    threads = oracle.max_threads()
+
+    def run(rows):
+        t = time.perf_counter()
+        _, _, s = oracle.calibrate(inp.x_cal[:rows], inp.w, wl.alpha)
+        gp, qw, ws = oracle.prepare_weight(inp.w, s)
+        oracle.linear(inp.x[:rows], gp, qw, ws, inp.bias)
+        return time.perf_counter() - t
+
+    probe = min(wl.T, 256)
+    tp = run(probe)
+    t_fixed = run(8)
+    per_row = max((tp - t_fixed) / max(probe - 8, 1), 1e-9)
+    rows = int(min(wl.T, max(probe, (target_s - t_fixed) / per_row)))
+    rows = max(64, rows // 64 * 64) if rows < wl.T else wl.T
+    secs = run(rows)
+    ops = 2.0 * rows * wl.K * wl.N
+    return {
+        "value": ops / secs / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+        "seconds": secs,
+        "sample": (f"the whole step (calibration over {rows} tokens, fold and quantization of the "
+                   f"full {wl.K}x{wl.N} weight, forward of {rows} of the {wl.T} tokens); "
+                   f"value = 2*{rows}*K*N ops / wall time, plain-C oracle with OpenMP"),
+    }
+
+
+def main():
+    args = _parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only: the layer's multi-GPU "
+                          "sharding is a design note, not built; run with --gpus 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import w8a8_int8_gemm_amd as sq
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (cuda:0)")
+    sq.lib()   # fails loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[WORKLOAD]
+    T, K, N, Tc = wl.T, wl.K, wl.N, wl.Tc
+    print(f"generating {WORKLOAD}: T={T} K={K} N={N} Tc={Tc}", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(wl)
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    x_cal, x, w, bias = d(inp.x_cal), d(inp.x), d(inp.w), d(inp.bias)
+    f = lambda n: torch.empty(n, dtype=torch.float32, device=dev)  # noqa: E731
+    a, wm, s, gp, wsc, xs = f(K), f(K), f(K), f(K), f(N), f(T)
+    wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    xq = torch.empty((T, K), dtype=torch.int8, device=dev)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    names = ["calibrate", "smooth_fold", "quant_weight", "quant_act", "gemm"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sq.sq_calibrate(x_cal, w, wl.alpha, a, wm, s, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        sq.sq_smooth_fold(s, None, gp, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        sq.sq_quant_weight(w, s, wq, wsc, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        sq.sq_quant_act(x, gp, xq, xs, stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+        sq.sq_gemm_w8a8(xq, xs, wq, wsc, y, bias=bias, stream=stream)
+        if ev is not None:
+            ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
+               for j, n in enumerate(names)}
+    print(f"timed {args.steps} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    ops = 2.0 * T * K * N
+    value = ops / (ms_step * 1e-3) / 1e12
+    # algorithmic bytes (or ops) per launch of each call
+    alg = {
+        "calibrate": ("GB/s", 2.0 * Tc * K + 2.0 * K * N + 12.0 * K),
+        "smooth_fold": ("GB/s", 8.0 * K),
+        "quant_weight": ("GB/s", 2.0 * K * N + 1.0 * K * N + 4.0 * N + 4.0 * K),
+        "quant_act": ("GB/s", 2.0 * T * K + 1.0 * T * K + 4.0 * T + 4.0 * K),
+        "gemm": ("TOPS", ops),
+    }
+    kernels = {}
+    for n in names:
+        unit, amount = alg[n]
+        secs = kern_ms[n] * 1e-3
+        ach = amount / secs / (1e9 if unit == "GB/s" else 1e12)
+        peak = PEAK_HBM_GBS if unit == "GB/s" else PEAK_INT8_TOPS
+        kernels[n] = {"us": kern_ms[n] * 1e3, "achieved": ach, "unit": unit, "frac_of_peak": ach / peak}
+
+    gemm_s = kern_ms["gemm"] * 1e-3
+    g_ach = ops / gemm_s / 1e12
+    roofline = {"bound": "mfma", "achieved": g_ach, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                "frac": g_ach / PEAK_INT8_TOPS, "traffic": _traffic(T * K + N * K + 2.0 * T * N),
+                "kernel": "k_gemm_w8a8 (sq_gemm_w8a8)",
+                "algorithmic": f"2*T*K*N = {ops:.4g} int8 ops per launch"}
+    linear_s = (kern_ms["quant_act"] + kern_ms["gemm"]) * 1e-3
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": WORKLOAD, "T": T, "K": K, "N": N, "calib_tokens": Tc,
+                   "alpha": wl.alpha, "x_dtype": "bf16", "w_dtype": "bf16", "y_dtype": "bf16",
+                   "bias": True,
+                   "step": "sq_calibrate + sq_smooth_fold + sq_quant_weight + sq_quant_act + "
+                           "sq_gemm_w8a8"},
+        "pct_of_int8_peak": 100.0 * value / PEAK_INT8_TOPS,
+        "linear_tops": ops / linear_s / 1e12,
+        "roofline": roofline,
+        "kernels": kernels,
+        "device": torch.cuda.get_device_properties(0).name,
+    }
+    if not args.no_cpu_baseline:
+        print("timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+/*
+ * sq_w8a8.h -- C ABI of libsqw8a8.so, a SmoothQuant W8A8 INT8 linear layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (the pages cited are the published descriptions of SmoothQuant):
+ *   Y = X W = (X diag(s)^-1) (diag(s) W) for any positive per-input-channel s
+ *   ("06 -- SmoothQuant" section 2; "Taming the Outliers", The Solution;
+ *   "SmoothQuant and W8A8", The trick).  s moves the activation outliers into
+ *   the weights; both sides are then quantized to symmetric INT8 and multiplied
+ *   on the integer matrix cores with int32 accumulation, and the product is
+ *   dequantized with one scale per token and one per output channel
+ *   ("06 -- SmoothQuant" section 7).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless stated otherwise.  The caller owns
+ *     every buffer; the library allocates nothing, keeps no state between
+ *     calls, and never synchronizes.  Calls are stream-ordered and
+ *     asynchronous on `stream` (NULL = the null stream); results are valid once
+ *     the stream has been synchronized.
+ *   - Matrices are row-major.  X is [T, K] (token t = row t); the weight W is
+ *     [K, N] (input channel j = row j, output channel n = column n), as in
+ *     Y = X W.  `ld*` arguments are leading dimensions in elements.
+ *   - Argument checks run on the host before any launch and return a status;
+ *     nothing is launched when a check fails.  A launch failure reported by
+ *     the HIP runtime returns SQ_ERR_HIP.  No call throws across the ABI.
+ *   - Supported shapes: K % 64 == 0 and 64 <= K <= 65536; T, N >= 0 (0 launches
+ *     nothing); every matrix pointer 16-byte aligned and every leading
+ *     dimension a multiple of 16 bytes.  Anything else is SQ_ERR_UNSUPPORTED.
+ *   - Scales are fp32.  Rounding is IEEE round-to-nearest-even throughout and
+ *     no multiply-add is fused, so results are reproducible bit for bit.
+ */
+#ifndef SQ_W8A8_H
+#define SQ_W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SQ_OK = 0,
+  SQ_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  SQ_ERR_SHAPE = 2,       /* negative size, or leading dimension too small    */
+  SQ_ERR_DTYPE = 3,       /* dtype not accepted for this argument             */
+  SQ_ERR_ALPHA = 4,       /* migration strength outside [0, 1] or not finite  */
+  SQ_ERR_UNSUPPORTED = 5, /* valid but outside the supported shapes/alignment */
+  SQ_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required       */
+  SQ_ERR_HIP = 7          /* the HIP runtime reported an error                */
+} sq_status;
+
+typedef enum { SQ_F32 = 0, SQ_BF16 = 1, SQ_I8 = 2, SQ_I32 = 3 } sq_dtype;
+
+typedef enum { SQ_NORM_NONE = 0, SQ_NORM_RMS = 1 } sq_norm;
+
+/* sq_calibrate flag: a[] holds a running maximum from earlier calls and is
+   only raised (otherwise it is overwritten). */
+#define SQ_CALIB_ACCUMULATE 1u
+
+/*
+ * (a) Calibration: per-input-channel activation absmax, per-input-channel
+ * weight absmax, and the smoothing factor.
+ *   a[j]    = max_t |X_cal[t, j]|                 ("Taming the Outliers",
+ *             System Architecture step C2; "06 -- SmoothQuant" section 3)
+ *   wmax[j] = max_n |W[j, n]|                     (same, step C4)
+ *   s[j]    = max( fp32( a_j^alpha / wmax_j^(1 - alpha) ), 1e-5 ), the powers
+ *             and quotient in fp64; s[j] = 1 when wmax[j] == 0
+ *             ("06 -- SmoothQuant" section 3; "SmoothQuant and W8A8", The
+ *             trick; the 1e-5 floor is the clamp of the pages' PyTorch class)
+ * In norm == SQ_NORM_RMS mode X_cal holds the norm's input h and the absmax is
+ * taken of the linear's input x = fp32(fp32(h * r_t) * gamma_j), with
+ * r_t = fp32(1 / sqrt(mean_k h[t,k]^2 + eps)) (mean and root in fp64) and
+ * gamma the norm's own weight ("SmoothQuant and W8A8", The trick: the smoothed
+ * linears read the output of an RMSNorm).
+ *
+ *   x_cal  [t_cal, k] fp32 or bf16, leading dimension ldx; NULL skips the
+ *          activation pass and a[] is used as given (e.g. an alpha sweep)
+ *   gamma  [k] fp32, norm mode only (NULL = ones)
+ *   w      [k, n] fp32 or bf16, leading dimension ldw; NULL skips wmax and s
+ *   alpha  migration strength in [0, 1]
+ *   a      [k] fp32, out (in/out with SQ_CALIB_ACCUMULATE or x_cal == NULL)
+ *   wmax   [k] fp32 out, s [k] fp32 out (both required when w != NULL)
+ * Norm mode requires k <= 8192.
+ */
+sq_status sq_calibrate(const void *x_cal, sq_dtype x_dt, int64_t t_cal, int64_t k, int64_t ldx,
+                       sq_norm norm, const float *gamma, float eps,
+                       const void *w, sq_dtype w_dt, int64_t n, int64_t ldw, float alpha,
+                       unsigned flags, float *a, float *wmax, float *s, hipStream_t stream);
+
+/*
+ * (b1) Offline fold ("06 -- SmoothQuant" sections 2 and 7; "SmoothQuant:
+ * Weight-Only vs W8A8", Integration with Transformers):
+ *   gamma_out[j] = fp32(gamma_j / s_j)     (gamma NULL = ones: gamma_out = 1/s,
+ *                                           the factor the activations are
+ *                                           multiplied by when no norm exists)
+ *   w_out[j, n]  = fp32(W[j, n] * s_j)     fp32 [k, n], leading dimension n;
+ *                                           w == NULL or w_out == NULL skips it
+ */
+sq_status sq_smooth_fold(const float *s, int64_t k, const float *gamma, float *gamma_out,
+                         const void *w, sq_dtype w_dt, int64_t n, int64_t ldw, float *w_out,
+                         hipStream_t stream);
+
+/*
+ * (b2) Per-output-channel symmetric INT8 weight quantization ("06 --
+ * SmoothQuant" section 7: one scale per output channel; "Taming the
+ * Outliers", The Problem: Delta = max|W| / (2^(N-1) - 1), codes rounded to
+ * nearest):
+ *   W^[j, n]   = W[j, n] * s_j in fp32 when s != NULL (fused fold), else W[j, n]
+ *   w_scale[n] = fp32( max_j |W^[j, n]| / 127 )
+ *   wq[n, j]   = clamp( round_half_even( fp32(W^[j, n] / w_scale[n]) ), -127, 127 )
+ *                (0 when w_scale[n] == 0)
+ *   w        [k, n] fp32 or bf16, leading dimension ldw
+ *   wq       [n, k] int8 out, K contiguous (the layout the GEMM reads)
+ *   w_scale  [n] fp32 out
+ */
+sq_status sq_quant_weight(const void *w, sq_dtype w_dt, int64_t k, int64_t n, int64_t ldw,
+                          const float *s, int8_t *wq, float *w_scale, hipStream_t stream);
+
+/*
+ * (c) Fused RMSNorm -> smooth -> per-token dynamic INT8 quantization
+ * ("06 -- SmoothQuant" section 7: one scale per token; "SmoothQuant and
+ * W8A8", The trick: 1/s folded into the norm weight):
+ *   norm == SQ_NORM_NONE: x^[t, k] = fp32(x[t, k] * gamma_f[k])
+ *   norm == SQ_NORM_RMS:  x^[t, k] = fp32(fp32(x[t, k] * r_t) * gamma_f[k]),
+ *                         r_t = fp32(1 / sqrt(mean_k x[t,k]^2 + eps)) (fp64 mean)
+ *   x_scale[t] = fp32( max_k |x^[t, k]| / 127 )
+ *   xq[t, k]   = clamp( round_half_even( fp32(x^[t, k] / x_scale[t]) ), -127, 127 )
+ *                (0 when x_scale[t] == 0)
+ *   x        [t, k] fp32 or bf16, leading dimension ldx
+ *   gamma_f  [k] fp32, the folded factor from sq_smooth_fold (NULL = ones)
+ *   xq       [t, k] int8 out (leading dimension k); x_scale [t] fp32 out
+ *   row_rscale [t] fp32 out, optional (norm mode): the r_t used
+ */
+sq_status sq_quant_act(const void *x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                       sq_norm norm, const float *gamma_f, float eps,
+                       int8_t *xq, float *x_scale, float *row_rscale, hipStream_t stream);
+
+/*
+ * (d) INT8 GEMM with int32 accumulation and the fused dequantization epilogue
+ * ("06 -- SmoothQuant" section 7: INT8 x INT8 -> INT32, then
+ * Y = scale_x * scale_w * Y_int32; "Taming the Outliers", step I6, add bias
+ * and dequantize):
+ *   acc[t, n] = sum_k xq[t, k] * wq[n, k]            (exact int32)
+ *   y[t, n]   = fp32( fp32(x_scale[t] * w_scale[n]) * fp32(acc[t, n]) ) + bias[n]
+ *               rounded to y_dt (bf16: nearest-even)
+ *   xq [t, k] int8, wq [n, k] int8 (both K contiguous), x_scale [t], w_scale [n]
+ *   bias [n] fp32 or NULL;  y [t, n] in y_dt (SQ_F32 or SQ_BF16), leading dim ldy
+ *   acc_out: NULL, or int32 [t, n] (leading dimension n) -- then the raw
+ *            accumulators are written there and y is not touched
+ */
+sq_status sq_gemm_w8a8(const int8_t *xq, const float *x_scale, int64_t t, int64_t k,
+                       const int8_t *wq, const float *w_scale, int64_t n, const float *bias,
+                       void *y, sq_dtype y_dt, int64_t ldy, int32_t *acc_out,
+                       hipStream_t stream);
+
+/* Optional outputs of sq_w8a8_linear; any field may be NULL. */
+typedef struct {
+  int8_t *xq;          /* [t, k] activation codes (replaces the workspace copy)  */
+  float *x_scale;      /* [t] per-token scales                                    */
+  float *row_rscale;   /* [t] RMSNorm reciprocal scales (norm mode)               */
+  int32_t *acc;        /* [t, n] int32 accumulators; y is then not written        */
+} sq_debug_out;
+
+/* Workspace sq_w8a8_linear needs for T tokens of width K: the int8 codes and
+   the per-token scales, each 256-byte aligned. */
+size_t sq_linear_workspace_bytes(int64_t t, int64_t k);
+
+/*
+ * (c) + (d): the online forward of the smoothed linear.
+ *   Y = dequant( Q( norm?(X) * gamma_f ) @ wq^T ) + bias
+ * equal to sq_quant_act followed by sq_gemm_w8a8, with the codes and scales
+ * kept in `workspace` (sq_linear_workspace_bytes(t, k) bytes, 256-byte
+ * aligned) unless dbg supplies both dbg->xq and dbg->x_scale.
+ */
+sq_status sq_w8a8_linear(const void *x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                         sq_norm norm, const float *gamma_f, float eps,
+                         const int8_t *wq, const float *w_scale, int64_t n, const float *bias,
+                         void *y, sq_dtype y_dt, int64_t ldy,
+                         void *workspace, size_t ws_bytes, const sq_debug_out *dbg,
+                         hipStream_t stream);
+
+/* Static description of a status code (host memory, never NULL). */
+const char *sq_status_string(sq_status status);
+
+/* ABI version of this header: 1. */
+int sq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQ_W8A8_H */

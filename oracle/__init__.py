@@ -62,7 +62,13 @@ def _load():
         _lib.oracle_int_gemm.restype = I64
         _lib.oracle_epilogue.argtypes = [P, P, P, P, I64, I64, P]
         _lib.oracle_f32_to_bf16.argtypes = [P, I64, P]
+        _lib.oracle_max_threads.restype = I
     return _lib
+
+
+def max_threads() -> int:
+    """Number of host threads the oracle's parallel loops use."""
+    return int(_load().oracle_max_threads())
 
 
 def _p(a: Optional[np.ndarray]):

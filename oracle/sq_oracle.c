@@ -37,6 +37,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <omp.h>
 
 static float bf16_to_f32(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;
@@ -60,6 +61,17 @@ static int8_t code_of(float v) {
 }
 
 int oracle_version(void) { return 1; }
+
+/* threads an OpenMP parallel region of the oracle uses */
+int oracle_max_threads(void) {
+  int n = 1;
+#pragma omp parallel
+  {
+#pragma omp single
+    n = omp_get_num_threads();
+  }
+  return n;
+}
 
 /* r[t] = fp32( 1 / sqrt( (sum_k h[t,k]^2) / K + eps ) ), sum and root in fp64 */
 void oracle_rms_rscale(const void *h, int is_bf16, int64_t T, int64_t K, int64_t ld,

@@ -1,0 +1,71 @@
+"""Helpers shared by the GPU parity tests: host <-> device copies of the
+canonical input bytes, and the GPU pipeline driven through the C ABI."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import w8a8_int8_gemm_amd as sq
+
+DEV = torch.device("cuda:0")
+
+
+def say(msg: str) -> None:
+    """Name the case about to run on the GPU (flushed, so it survives a crash)."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:   # bf16 bit patterns
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def f32(n, fill=None):
+    t = torch.empty(n, dtype=torch.float32, device=DEV)
+    if fill is not None:
+        t.fill_(fill)
+    return t
+
+
+def gpu_calibrate(x_cal, w, alpha, *, norm=False, gamma=None, eps=1e-6):
+    K = x_cal.shape[1]
+    a, wm, s = f32(K), f32(K), f32(K)
+    sq.sq_calibrate(x_cal, w, alpha, a, wm, s, norm=norm, gamma=gamma, eps=eps)
+    return a, wm, s
+
+
+def gpu_prepare_weight(w, s, gamma=None):
+    K, N = w.shape
+    gp = f32(K)
+    sq.sq_smooth_fold(s, gamma, gp)
+    wq = torch.empty((N, K), dtype=torch.int8, device=DEV)
+    ws = f32(N)
+    sq.sq_quant_weight(w, s, wq, ws)
+    return gp, wq, ws
+
+
+def gpu_linear(x, gp, wq, ws, bias=None, *, norm=False, eps=1e-6, out_dtype=torch.bfloat16,
+               debug=True):
+    T, K = x.shape
+    N = wq.shape[0]
+    y = torch.empty((T, N), dtype=out_dtype, device=DEV)
+    ws_bytes = sq.sq_linear_workspace_bytes(T, K)
+    work = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=DEV)
+    kw = {}
+    if debug:
+        kw = dict(dbg_xq=torch.empty((T, K), dtype=torch.int8, device=DEV), dbg_x_scale=f32(T),
+                  dbg_row_rscale=f32(T) if norm else None)
+    sq.sq_w8a8_linear(x, gp, wq, ws, y, work, norm=norm, eps=eps, bias=bias, **kw)
+    return y, kw

@@ -1,0 +1,136 @@
+"""Host-side checks of libsqw8a8.so that need no GPU: the library loads, it
+exports every function include/sq_w8a8.h declares, and argument validation
+returns the documented status before anything is launched.  Only arguments
+that fail validation are passed, so no kernel is ever launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sq_w8a8.h")
+
+import w8a8_int8_gemm_amd as sq  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(sq.LIB_PATH):
+        from w8a8_int8_gemm_amd import build
+        build.build()
+    return sq.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(sq_[a-z0-9_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("sq_calibrate", "sq_smooth_fold", "sq_quant_weight", "sq_w8a8_linear",
+              "sq_quant_act", "sq_gemm_w8a8", "sq_linear_workspace_bytes", "sq_status_string",
+              "sq_abi_version"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in _declared_functions():
+        assert hasattr(L, n), f"libsqw8a8.so does not export {n}"
+    assert L.sq_abi_version() == 1
+
+
+def test_status_strings(L):
+    for code in range(8):
+        s = sq.status_string(code)
+        assert s.startswith("SQ_")
+    assert "unknown" in sq.status_string(99)
+
+
+def test_workspace_size(L):
+    assert sq.sq_linear_workspace_bytes(0, 4096) == 0
+    assert sq.sq_linear_workspace_bytes(1, 64) == 256 + 256
+    assert sq.sq_linear_workspace_bytes(8192, 4096) == 8192 * 4096 + 8192 * 4
+
+
+# fake, never-dereferenced device addresses; every call below fails validation
+A16 = 0x7F0000000000
+MIS = A16 + 8
+
+
+def test_calibrate_validation(L):
+    c = L.sq_calibrate
+    # K rules
+    assert c(A16, sq.SQ_BF16, 10, 0, 0, 0, None, 1e-6, None, 0, 0, 0, 0.5, 0, A16, None, None, None) == sq.SQ_ERR_SHAPE
+    assert c(A16, sq.SQ_BF16, 10, 96, 96, 0, None, 1e-6, None, 0, 0, 0, 0.5, 0, A16, None, None, None) == sq.SQ_ERR_UNSUPPORTED
+    assert c(A16, sq.SQ_BF16, 10, 65536 + 64, 65600, 0, None, 1e-6, None, 0, 0, 0, 0.5, 0, A16, None, None, None) == sq.SQ_ERR_UNSUPPORTED
+    # a required
+    assert c(A16, sq.SQ_BF16, 10, 64, 64, 0, None, 1e-6, None, 0, 0, 0, 0.5, 0, None, None, None, None) == sq.SQ_ERR_NULL
+    # dtype, leading dimension, alignment
+    assert c(A16, sq.SQ_I8, 10, 64, 64, 0, None, 1e-6, None, 0, 0, 0, 0.5, 0, A16, None, None, None) == sq.SQ_ERR_DTYPE
+    assert c(A16, sq.SQ_BF16, 10, 64, 32, 0, None, 1e-6, None, 0, 0, 0, 0.5, 0, A16, None, None, None) == sq.SQ_ERR_SHAPE
+    assert c(A16, sq.SQ_BF16, -1, 64, 64, 0, None, 1e-6, None, 0, 0, 0, 0.5, 0, A16, None, None, None) == sq.SQ_ERR_SHAPE
+    assert c(MIS, sq.SQ_BF16, 10, 64, 64, 0, None, 1e-6, None, 0, 0, 0, 0.5, 0, A16, None, None, None) == sq.SQ_ERR_UNSUPPORTED
+    assert c(A16, sq.SQ_BF16, 10, 64, 68, 0, None, 1e-6, None, 0, 0, 0, 0.5, 0, A16, None, None, None) == sq.SQ_ERR_UNSUPPORTED
+    # norm mode limits and flags
+    assert c(A16, sq.SQ_BF16, 10, 8192 + 64, 8256, 1, None, 1e-6, None, 0, 0, 0, 0.5, 0, A16, None, None, None) == sq.SQ_ERR_UNSUPPORTED
+    assert c(A16, sq.SQ_BF16, 10, 64, 64, 1, None, -1.0, None, 0, 0, 0, 0.5, 0, A16, None, None, None) == sq.SQ_ERR_SHAPE
+    assert c(A16, sq.SQ_BF16, 10, 64, 64, 7, None, 1e-6, None, 0, 0, 0, 0.5, 0, A16, None, None, None) == sq.SQ_ERR_UNSUPPORTED
+    assert c(A16, sq.SQ_BF16, 10, 64, 64, 0, None, 1e-6, None, 0, 0, 0, 0.5, 4, A16, None, None, None) == sq.SQ_ERR_UNSUPPORTED
+    # weight side: alpha range, wmax/s required, N % 8
+    for bad in (-0.1, 1.5, float("nan"), float("inf")):
+        assert c(None, 0, 0, 64, 64, 0, None, 1e-6, A16, sq.SQ_BF16, 64, 64, bad, 0, A16, A16, A16, None) == sq.SQ_ERR_ALPHA
+    assert c(None, 0, 0, 64, 64, 0, None, 1e-6, A16, sq.SQ_BF16, 64, 64, 0.5, 0, A16, None, A16, None) == sq.SQ_ERR_NULL
+    assert c(None, 0, 0, 64, 64, 0, None, 1e-6, A16, sq.SQ_BF16, 60, 64, 0.5, 0, A16, A16, A16, None) == sq.SQ_ERR_UNSUPPORTED
+
+
+def test_fold_and_quant_weight_validation(L):
+    assert L.sq_smooth_fold(None, 64, None, A16, None, 0, 0, 0, None, None) == sq.SQ_ERR_NULL
+    assert L.sq_smooth_fold(A16, 100, None, A16, None, 0, 0, 0, None, None) == sq.SQ_ERR_UNSUPPORTED
+    assert L.sq_smooth_fold(A16, 64, None, A16, A16, sq.SQ_BF16, 64, 64, MIS, None) == sq.SQ_ERR_UNSUPPORTED
+    q = L.sq_quant_weight
+    assert q(None, sq.SQ_BF16, 64, 64, 64, None, A16, A16, None) == sq.SQ_ERR_NULL
+    assert q(A16, sq.SQ_BF16, 64, 64, 64, None, None, A16, None) == sq.SQ_ERR_NULL
+    assert q(A16, sq.SQ_BF16, 64, 12, 16, None, A16, A16, None) == sq.SQ_ERR_UNSUPPORTED
+    assert q(A16, sq.SQ_F32, 64, 64, 32, None, A16, A16, None) == sq.SQ_ERR_SHAPE
+    assert q(A16, sq.SQ_BF16, 64, 64, 64, None, MIS, A16, None) == sq.SQ_ERR_UNSUPPORTED
+    assert q(A16, sq.SQ_I32, 64, 64, 64, None, A16, A16, None) == sq.SQ_ERR_DTYPE
+
+
+def test_act_gemm_linear_validation(L):
+    a = L.sq_quant_act
+    assert a(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, None, A16, None, None) == sq.SQ_ERR_NULL
+    assert a(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, MIS, A16, None, None) == sq.SQ_ERR_UNSUPPORTED
+    g = L.sq_gemm_w8a8
+    assert g(None, A16, 4, 64, A16, A16, 8, None, A16, sq.SQ_BF16, 8, None, None) == sq.SQ_ERR_NULL
+    assert g(A16, A16, 4, 64, A16, A16, 8, None, None, sq.SQ_BF16, 8, None, None) == sq.SQ_ERR_NULL
+    assert g(A16, A16, 4, 64, A16, A16, 8, None, A16, sq.SQ_I8, 8, None, None) == sq.SQ_ERR_DTYPE
+    assert g(A16, A16, 4, 64, A16, A16, 8, None, A16, sq.SQ_BF16, 4, None, None) == sq.SQ_ERR_SHAPE
+    assert g(A16, A16, 4, 64, A16, A16, 8, None, A16, sq.SQ_BF16, 12, None, None) == sq.SQ_ERR_UNSUPPORTED
+    assert g(A16, A16, 4, 80, A16, A16, 8, None, A16, sq.SQ_BF16, 8, None, None) == sq.SQ_ERR_UNSUPPORTED
+    assert g(A16, A16, 4, 64, A16, A16, 8, None, None, sq.SQ_BF16, 8, MIS, None) == sq.SQ_ERR_UNSUPPORTED
+    lin = L.sq_w8a8_linear
+    # workspace missing, too small, misaligned
+    assert lin(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, A16, A16, 8, None, A16, sq.SQ_BF16, 8,
+               None, 0, None, None) == sq.SQ_ERR_WORKSPACE
+    assert lin(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, A16, A16, 8, None, A16, sq.SQ_BF16, 8,
+               A16, 16, None, None) == sq.SQ_ERR_WORKSPACE
+    assert lin(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, A16, A16, 8, None, A16, sq.SQ_BF16, 8,
+               A16 + 16, 1 << 20, None, None) == sq.SQ_ERR_WORKSPACE
+    assert lin(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, None, A16, 8, None, A16, sq.SQ_BF16, 8,
+               A16, 1 << 20, None, None) == sq.SQ_ERR_NULL
+    # empty inputs are accepted and launch nothing
+    assert a(A16, sq.SQ_BF16, 0, 64, 64, 0, None, 1e-6, A16, A16, None, None) == sq.SQ_OK
+    assert g(A16, A16, 0, 64, A16, A16, 8, None, A16, sq.SQ_BF16, 8, None, None) == sq.SQ_OK
+    assert lin(A16, sq.SQ_BF16, 0, 64, 64, 0, None, 1e-6, A16, A16, 8, None, A16, sq.SQ_BF16, 8,
+               None, 0, None, None) == sq.SQ_OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(sq, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(sq, "_lib", None)
+    with pytest.raises(ImportError):
+        sq.lib()

@@ -1,0 +1,183 @@
+"""SmoothQuant W8A8 INT8 linear for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding of libsqw8a8.so (C ABI in include/sq_w8a8.h).  Every
+function here has the name of the C entry point it wraps and only marshals
+arguments: tensors become device pointers, shapes and leading dimensions are
+read off the tensors, and the current HIP stream is passed along.  All the
+work runs in the library's gfx950 kernels; there is no fallback.  If the
+library has not been built, every call raises.
+
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libsqw8a8.so")
+
+SQ_OK, SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_DTYPE, SQ_ERR_ALPHA, SQ_ERR_UNSUPPORTED, \
+    SQ_ERR_WORKSPACE, SQ_ERR_HIP = range(8)
+SQ_F32, SQ_BF16, SQ_I8, SQ_I32 = range(4)
+SQ_NORM_NONE, SQ_NORM_RMS = 0, 1
+SQ_CALIB_ACCUMULATE = 1
+
+_lib = None
+
+
+class SQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class _DebugOut(ctypes.Structure):
+    _fields_ = [("xq", ctypes.c_void_p), ("x_scale", ctypes.c_void_p),
+                ("row_rscale", ctypes.c_void_p), ("acc", ctypes.c_void_p)]
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libsqw8a8.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m w8a8_int8_gemm_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, F, U, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_uint, ctypes.c_int
+        L.sq_calibrate.argtypes = [P, I, I64, I64, I64, I, P, F, P, I, I64, I64, F, U, P, P, P, P]
+        L.sq_smooth_fold.argtypes = [P, I64, P, P, P, I, I64, I64, P, P]
+        L.sq_quant_weight.argtypes = [P, I, I64, I64, I64, P, P, P, P]
+        L.sq_quant_act.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, P, P]
+        L.sq_gemm_w8a8.argtypes = [P, P, I64, I64, P, P, I64, P, P, I, I64, P, P]
+        L.sq_linear_workspace_bytes.argtypes = [I64, I64]
+        L.sq_linear_workspace_bytes.restype = ctypes.c_size_t
+        L.sq_w8a8_linear.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, I64, P, P, I, I64, P,
+                                     ctypes.c_size_t, ctypes.POINTER(_DebugOut), P]
+        L.sq_status_string.argtypes = [I]
+        L.sq_status_string.restype = ctypes.c_char_p
+        L.sq_abi_version.restype = I
+        for name in ("sq_calibrate", "sq_smooth_fold", "sq_quant_weight", "sq_quant_act",
+                     "sq_gemm_w8a8", "sq_w8a8_linear"):
+            getattr(L, name).restype = I
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().sq_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != SQ_OK:
+        raise SQError(status, where)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return SQ_F32
+    if t.dtype == torch.bfloat16:
+        return SQ_BF16
+    if t.dtype == torch.int8:
+        return SQ_I8
+    if t.dtype == torch.int32:
+        return SQ_I32
+    return -1
+
+
+def _ld(t) -> int:
+    """Leading dimension of a row-major 2-D tensor (unit inner stride required)."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("expected a 2-D row-major tensor with unit inner stride")
+    return t.stride(0)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# the C entry points
+# ---------------------------------------------------------------------------
+
+def sq_calibrate(x_cal, w, alpha: float, a, wmax=None, s=None, *, norm: bool = False, gamma=None,
+                 eps: float = 1e-6, accumulate: bool = False, stream=None) -> None:
+    """a[K] (running) activation absmax, wmax[K], s[K] -- see sq_calibrate in sq_w8a8.h."""
+    K = a.shape[0]
+    xt, xdt, xld = (0, SQ_BF16, K) if x_cal is None else (x_cal.shape[0], _dtype(x_cal), _ld(x_cal))
+    N, wdt, wld = (0, SQ_BF16, 0) if w is None else (w.shape[1], _dtype(w), _ld(w))
+    flags = SQ_CALIB_ACCUMULATE if accumulate else 0
+    _check(lib().sq_calibrate(_ptr(x_cal), xdt, xt, K, xld, SQ_NORM_RMS if norm else SQ_NORM_NONE,
+                              _ptr(gamma), eps, _ptr(w), wdt, N, wld, alpha, flags, _ptr(a),
+                              _ptr(wmax), _ptr(s), _stream(stream)), "sq_calibrate")
+
+
+def sq_smooth_fold(s, gamma=None, gamma_out=None, w=None, w_out=None, *, stream=None) -> None:
+    """gamma_out = gamma / s, w_out = diag(s) W -- see sq_smooth_fold."""
+    K = s.shape[0]
+    N, wdt, wld = (0, SQ_BF16, 0) if w is None else (w.shape[1], _dtype(w), _ld(w))
+    _check(lib().sq_smooth_fold(_ptr(s), K, _ptr(gamma), _ptr(gamma_out), _ptr(w), wdt, N, wld,
+                                _ptr(w_out), _stream(stream)), "sq_smooth_fold")
+
+
+def sq_quant_weight(w, s, wq, w_scale, *, stream=None) -> None:
+    """wq[N, K] int8 and w_scale[N] of diag(s) W (s may be None) -- see sq_quant_weight."""
+    K, N = w.shape
+    _check(lib().sq_quant_weight(_ptr(w), _dtype(w), K, N, _ld(w), _ptr(s), _ptr(wq),
+                                 _ptr(w_scale), _stream(stream)), "sq_quant_weight")
+
+
+def sq_quant_act(x, gamma_f, xq, x_scale, *, norm: bool = False, eps: float = 1e-6,
+                 row_rscale=None, stream=None) -> None:
+    """xq[T, K] int8 and x_scale[T] of norm?(x) * gamma_f -- see sq_quant_act."""
+    T, K = x.shape
+    _check(lib().sq_quant_act(_ptr(x), _dtype(x), T, K, _ld(x),
+                              SQ_NORM_RMS if norm else SQ_NORM_NONE, _ptr(gamma_f), eps, _ptr(xq),
+                              _ptr(x_scale), _ptr(row_rscale), _stream(stream)), "sq_quant_act")
+
+
+def sq_gemm_w8a8(xq, x_scale, wq, w_scale, y=None, *, bias=None, acc_out=None, stream=None) -> None:
+    """y = dequant(xq @ wq^T) + bias, or the int32 accumulators -- see sq_gemm_w8a8."""
+    T, K = xq.shape
+    N = wq.shape[0]
+    ydt, yld = (SQ_BF16, N) if y is None else (_dtype(y), _ld(y))
+    _check(lib().sq_gemm_w8a8(_ptr(xq), _ptr(x_scale), T, K, _ptr(wq), _ptr(w_scale), N,
+                              _ptr(bias), _ptr(y), ydt, yld, _ptr(acc_out), _stream(stream)),
+           "sq_gemm_w8a8")
+
+
+def sq_linear_workspace_bytes(t: int, k: int) -> int:
+    return int(lib().sq_linear_workspace_bytes(t, k))
+
+
+def sq_w8a8_linear(x, gamma_f, wq, w_scale, y, workspace, *, norm: bool = False,
+                   eps: float = 1e-6, bias=None, dbg_xq=None, dbg_x_scale=None,
+                   dbg_row_rscale=None, dbg_acc=None, stream=None) -> None:
+    """The online forward: sq_quant_act then sq_gemm_w8a8 -- see sq_w8a8_linear."""
+    T, K = x.shape
+    N = wq.shape[0]
+    dbg = None
+    if any(v is not None for v in (dbg_xq, dbg_x_scale, dbg_row_rscale, dbg_acc)):
+        dbg = ctypes.byref(_DebugOut(_ptr(dbg_xq), _ptr(dbg_x_scale), _ptr(dbg_row_rscale),
+                                     _ptr(dbg_acc)))
+    ydt, yld = (SQ_BF16, N) if y is None else (_dtype(y), _ld(y))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().sq_w8a8_linear(_ptr(x), _dtype(x), T, K, _ld(x),
+                                SQ_NORM_RMS if norm else SQ_NORM_NONE, _ptr(gamma_f), eps,
+                                _ptr(wq), _ptr(w_scale), N, _ptr(bias), _ptr(y), ydt, yld,
+                                _ptr(workspace), ws_bytes, dbg, _stream(stream)),
+           "sq_w8a8_linear")
+
+
+def sq_abi_version() -> int:
+    return int(lib().sq_abi_version())

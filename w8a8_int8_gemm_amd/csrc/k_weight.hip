@@ -1,0 +1,169 @@
+// k_weight.hip -- offline fold and per-output-channel INT8 weight quantization
+// for gfx950.
+//
+//  * k_fold_gamma: gamma'_j = gamma_j / s_j -- 1/s folded into the preceding
+//    norm's weight ("06 -- SmoothQuant", section 7; "SmoothQuant and W8A8",
+//    The trick).
+//  * k_fold_w: W^[j, n] = W[j, n] * s_j -- s folded into the weight's input
+//    rows ("06 -- SmoothQuant", section 2).
+//  * k_div127: Delta_n = amax_n / 127 (the symmetric 8-bit step, "Taming the
+//    Outliers", The Problem).
+//  * k_quant_weight_t: codes = round-half-even(W^ / Delta_n), written
+//    transposed to the [N, K] K-contiguous layout the GEMM streams.
+// The per-output-channel absmax between fold and quant is k_col_absmax with
+// the row scale s (k_calib.hip), so W^ is never materialised.
+#include "sq_common.h"
+#include "sq_internal.h"
+
+namespace sqk {
+
+__global__ void k_fold_gamma(const float* __restrict__ s, const float* __restrict__ gamma,
+                             float* __restrict__ gout, int64_t K) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j < K) gout[j] = (gamma ? gamma[j] : 1.0f) / s[j];
+}
+
+// 8 consecutive elements of one row per thread
+template <class In>
+__global__ __launch_bounds__(256) void k_fold_w(const typename In::elem* __restrict__ w,
+                                                int64_t K, int64_t N, int64_t ld,
+                                                const float* __restrict__ s,
+                                                float* __restrict__ wout) {
+  const int64_t chunks_per_row = N >> 3;
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= K * chunks_per_row) return;
+  const int64_t j = c / chunks_per_row;
+  const int64_t n0 = (c - j * chunks_per_row) * 8;
+  float v[8];
+  In::load8(w + j * ld + n0, v);
+  const float sj = s[j];
+  f32x4 o0, o1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o0[i] = v[i] * sj;
+    o1[i] = v[4 + i] * sj;
+  }
+  *reinterpret_cast<f32x4*>(wout + j * N + n0) = o0;
+  *reinterpret_cast<f32x4*>(wout + j * N + n0 + 4) = o1;
+}
+
+__global__ void k_div127(float* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = p[i] / 127.0f;
+}
+
+// Tile of 128 input channels (k) x 64 output channels (n).  Thread (tx, ty),
+// tx = tid % 8, ty = tid / 8: columns n0 + 8*tx .. +7 of rows k0 + 4*ty .. +3.
+// Each thread packs its 4 codes per column (4 consecutive k) into one dword of
+// the LDS tile [n][k]; the tile is then written out 32 bytes per thread along k.
+template <class In, bool kRowScale>
+__global__ __launch_bounds__(256) void k_quant_weight_t(const typename In::elem* __restrict__ w,
+                                                        int64_t K, int64_t N, int64_t ld,
+                                                        const float* __restrict__ s,
+                                                        const float* __restrict__ wscale,
+                                                        int8_t* __restrict__ wq) {
+  constexpr int KT = 128, NT = 64, LDT = KT + 4;   // padded row of the [n][k] tile
+  __shared__ uint32_t tile[NT * LDT / 4];
+  const int tid = threadIdx.x;
+  const int tx = tid & 7, ty = tid >> 3;
+  const int64_t n0 = (int64_t)blockIdx.x * NT;
+  const int64_t k0 = (int64_t)blockIdx.y * KT;
+  const int64_t nb = n0 + tx * 8;
+  const bool ncol = nb < N;   // N % 8 == 0: a thread's 8 columns are all valid or none
+
+  float d[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) d[i] = ncol ? wscale[nb + i] : 0.0f;
+
+  uint32_t packed[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) packed[i] = 0u;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t k = k0 + ty * 4 + r;
+    if (ncol && k < K) {
+      float v[8];
+      In::load8(w + k * ld + nb, v);
+      const float sk = kRowScale ? s[k] : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float wh = kRowScale ? v[i] * sk : v[i];
+        float q = 0.0f;
+        if (d[i] != 0.0f) {
+          q = rintf(wh / d[i]);
+          q = fminf(fmaxf(q, -127.0f), 127.0f);
+        }
+        packed[i] |= code_byte(q) << (8 * r);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) tile[((tx * 8 + i) * LDT + ty * 4) / 4] = packed[i];
+  __syncthreads();
+  // write out: 64 rows (n) x 128 bytes (k); thread -> row tid/4, 32 bytes at (tid%4)*32
+  const int nr = tid >> 2;
+  const int seg = (tid & 3) * 32;
+  const int64_t n = n0 + nr;
+  if (n < N && k0 + seg < K) {
+    const uint32_t* src = &tile[(nr * LDT + seg) / 4];
+    u32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = src[i];
+      b[i] = src[4 + i];
+    }
+    int8_t* dst = wq + n * K + k0 + seg;
+    *reinterpret_cast<u32x4*>(dst) = a;
+    *reinterpret_cast<u32x4*>(dst + 16) = b;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+
+void launch_fold_gamma(const float* s, const float* gamma, float* gout, int64_t K, hipStream_t st) {
+  if (K <= 0) return;
+  hipLaunchKernelGGL(k_fold_gamma, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, s, gamma,
+                     gout, K);
+}
+
+void launch_fold_w(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, const float* s,
+                   float* wout, hipStream_t st) {
+  const int64_t chunks = K * (N >> 3);
+  if (chunks <= 0) return;
+  const dim3 grid((unsigned)((chunks + 255) / 256));
+  if (bf16)
+    hipLaunchKernelGGL(k_fold_w<Bf16In>, grid, dim3(256), 0, st, (const uint16_t*)w, K, N, ld, s,
+                       wout);
+  else
+    hipLaunchKernelGGL(k_fold_w<F32In>, grid, dim3(256), 0, st, (const float*)w, K, N, ld, s, wout);
+}
+
+void launch_div127(float* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_div127, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+}
+
+void launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
+                           const float* s, const float* wscale, int8_t* wq, hipStream_t st) {
+  if (K <= 0 || N <= 0) return;
+  const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((K + 127) / 128));
+  if (bf16) {
+    if (s)
+      hipLaunchKernelGGL((k_quant_weight_t<Bf16In, true>), grid, dim3(256), 0, st,
+                         (const uint16_t*)w, K, N, ld, s, wscale, wq);
+    else
+      hipLaunchKernelGGL((k_quant_weight_t<Bf16In, false>), grid, dim3(256), 0, st,
+                         (const uint16_t*)w, K, N, ld, s, wscale, wq);
+  } else {
+    if (s)
+      hipLaunchKernelGGL((k_quant_weight_t<F32In, true>), grid, dim3(256), 0, st,
+                         (const float*)w, K, N, ld, s, wscale, wq);
+    else
+      hipLaunchKernelGGL((k_quant_weight_t<F32In, false>), grid, dim3(256), 0, st,
+                         (const float*)w, K, N, ld, s, wscale, wq);
+  }
+}
+
+}  // namespace sqk

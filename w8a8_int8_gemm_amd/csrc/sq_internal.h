@@ -1,0 +1,40 @@
+// sq_internal.h -- launchers of the gfx950 kernels, called by the C ABI layer
+// (sq_w8a8.hip) after it has validated the arguments.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sqk {
+
+// k_calib.hip
+void launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
+void launch_col_absmax(const void* m, bool bf16, int64_t rows, int64_t cols, int64_t ld,
+                       const float* row_scale, float* out, hipStream_t st);
+void launch_rms_act_absmax(const void* h, bool bf16, int64_t rows, int64_t K, int64_t ld,
+                           const float* gamma, float eps, float* out, hipStream_t st);
+void launch_wrow_absmax_s(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
+                          const float* a, float alpha, float* wmax, float* s, hipStream_t st);
+
+// k_weight.hip
+void launch_fold_gamma(const float* s, const float* gamma, float* gout, int64_t K, hipStream_t st);
+void launch_fold_w(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, const float* s,
+                   float* wout, hipStream_t st);
+void launch_div127(float* p, int64_t n, hipStream_t st);
+void launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
+                           const float* s, const float* wscale, int8_t* wq, hipStream_t st);
+
+// k_actquant.hip
+void launch_quant_act(const void* x, bool bf16, int64_t T, int64_t K, int64_t ld, bool norm,
+                      const float* gamma_f, float eps, int8_t* xq, float* xscale, float* rrow,
+                      hipStream_t st);
+
+// k_gemm.hip / k_gemm_decode.hip; out: 0 = bf16, 1 = fp32, 2 = int32 accumulators
+void launch_gemm(const int8_t* xq, const float* xs, int64_t T, int64_t K, const int8_t* wq,
+                 const float* ws, int64_t N, const float* bias, void* y, int64_t ldy, int out,
+                 hipStream_t st);
+void launch_gemm_decode(const int8_t* xq, const float* xs, int64_t T, int64_t K, const int8_t* wq,
+                        const float* ws, int64_t N, const float* bias, void* y, int64_t ldy,
+                        int out, hipStream_t st);
+
+}  // namespace sqk

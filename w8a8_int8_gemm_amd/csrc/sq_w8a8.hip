@@ -1,0 +1,222 @@
+// sq_w8a8.hip -- the C ABI of libsqw8a8.so (declared in include/sq_w8a8.h).
+// Host side only: argument checks, then stream-ordered kernel launches.  The
+// library allocates nothing and keeps no state.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "sq_internal.h"
+#include "sq_w8a8.h"
+
+namespace {
+
+constexpr int64_t kMaxK = 65536;
+constexpr int64_t kMaxNormCalibK = 8192;
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool is_fp(sq_dtype d) { return d == SQ_F32 || d == SQ_BF16; }
+inline int64_t esize(sq_dtype d) { return d == SQ_F32 ? 4 : d == SQ_BF16 ? 2 : d == SQ_I32 ? 4 : 1; }
+inline int64_t round256(int64_t b) { return (b + 255) & ~int64_t(255); }
+
+// K rules shared by every call
+inline sq_status check_k(int64_t k) {
+  if (k <= 0) return SQ_ERR_SHAPE;
+  if (k % 64 != 0 || k > kMaxK) return SQ_ERR_UNSUPPORTED;
+  return SQ_OK;
+}
+
+// a row-major matrix of `rows` x `cols` elements with leading dimension ld
+inline sq_status check_mat(const void* p, sq_dtype dt, int64_t rows, int64_t cols, int64_t ld) {
+  if (p == nullptr) return SQ_ERR_NULL;
+  if (!is_fp(dt)) return SQ_ERR_DTYPE;
+  if (rows < 0 || cols < 0 || ld < cols) return SQ_ERR_SHAPE;
+  if (!aligned16(p) || (ld * esize(dt)) % 16 != 0) return SQ_ERR_UNSUPPORTED;
+  return SQ_OK;
+}
+
+inline sq_status hip_status() {
+  return hipGetLastError() == hipSuccess ? SQ_OK : SQ_ERR_HIP;
+}
+
+#define SQ_TRY(expr)                 \
+  do {                               \
+    const sq_status st__ = (expr);   \
+    if (st__ != SQ_OK) return st__;  \
+  } while (0)
+
+sq_status check_act(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx, sq_norm norm,
+                    float eps) {
+  SQ_TRY(check_k(k));
+  SQ_TRY(check_mat(x, x_dt, t, k, ldx));
+  if (norm != SQ_NORM_NONE && norm != SQ_NORM_RMS) return SQ_ERR_UNSUPPORTED;
+  if (norm == SQ_NORM_RMS && !(eps >= 0.0f && isfinite(eps))) return SQ_ERR_SHAPE;
+  return SQ_OK;
+}
+
+sq_status check_gemm(const int8_t* xq, const float* xs, int64_t t, int64_t k, const int8_t* wq,
+                     const float* ws, int64_t n, void* y, sq_dtype y_dt, int64_t ldy,
+                     const int32_t* acc_out) {
+  SQ_TRY(check_k(k));
+  if (xq == nullptr || wq == nullptr) return SQ_ERR_NULL;
+  if (t < 0 || n < 0) return SQ_ERR_SHAPE;
+  if (t > INT32_MAX || n > INT32_MAX) return SQ_ERR_UNSUPPORTED;
+  if (!aligned16(xq) || !aligned16(wq)) return SQ_ERR_UNSUPPORTED;
+  if (acc_out != nullptr) {
+    if (!aligned16(acc_out)) return SQ_ERR_UNSUPPORTED;
+    return SQ_OK;
+  }
+  if (xs == nullptr || ws == nullptr || y == nullptr) return SQ_ERR_NULL;
+  if (!is_fp(y_dt)) return SQ_ERR_DTYPE;
+  if (ldy < n) return SQ_ERR_SHAPE;
+  if (ldy > INT32_MAX) return SQ_ERR_UNSUPPORTED;
+  if (!aligned16(y) || (ldy * esize(y_dt)) % 16 != 0) return SQ_ERR_UNSUPPORTED;
+  return SQ_OK;
+}
+
+inline int gemm_out(sq_dtype y_dt, const int32_t* acc_out) {
+  return acc_out != nullptr ? 2 : (y_dt == SQ_BF16 ? 0 : 1);
+}
+
+}  // namespace
+
+extern "C" {
+
+int sq_abi_version(void) { return 1; }
+
+const char* sq_status_string(sq_status status) {
+  switch (status) {
+    case SQ_OK: return "SQ_OK";
+    case SQ_ERR_NULL: return "SQ_ERR_NULL: a required pointer is NULL";
+    case SQ_ERR_SHAPE: return "SQ_ERR_SHAPE: negative size or leading dimension too small";
+    case SQ_ERR_DTYPE: return "SQ_ERR_DTYPE: dtype not accepted for this argument";
+    case SQ_ERR_ALPHA: return "SQ_ERR_ALPHA: alpha must be a finite value in [0, 1]";
+    case SQ_ERR_UNSUPPORTED:
+      return "SQ_ERR_UNSUPPORTED: shape or alignment outside the supported set";
+    case SQ_ERR_WORKSPACE: return "SQ_ERR_WORKSPACE: workspace missing or too small";
+    case SQ_ERR_HIP: return "SQ_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "unknown sq_status";
+}
+
+sq_status sq_calibrate(const void* x_cal, sq_dtype x_dt, int64_t t_cal, int64_t k, int64_t ldx,
+                       sq_norm norm, const float* gamma, float eps, const void* w, sq_dtype w_dt,
+                       int64_t n, int64_t ldw, float alpha, unsigned flags, float* a, float* wmax,
+                       float* s, hipStream_t stream) {
+  SQ_TRY(check_k(k));
+  if (a == nullptr) return SQ_ERR_NULL;
+  if ((flags & ~SQ_CALIB_ACCUMULATE) != 0u) return SQ_ERR_UNSUPPORTED;
+  if (x_cal != nullptr) {
+    SQ_TRY(check_act(x_cal, x_dt, t_cal, k, ldx, norm, eps));
+    if (norm == SQ_NORM_RMS && k > kMaxNormCalibK) return SQ_ERR_UNSUPPORTED;
+  }
+  if (w != nullptr) {
+    SQ_TRY(check_mat(w, w_dt, k, n, ldw));
+    if (n % 8 != 0) return SQ_ERR_UNSUPPORTED;
+    if (wmax == nullptr || s == nullptr) return SQ_ERR_NULL;
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ALPHA;
+  }
+  if (x_cal == nullptr && w == nullptr) return SQ_OK;
+  if (x_cal != nullptr) {
+    if ((flags & SQ_CALIB_ACCUMULATE) == 0u) sqk::launch_fill_f32(a, k, 0.0f, stream);
+    if (norm == SQ_NORM_RMS)
+      sqk::launch_rms_act_absmax(x_cal, x_dt == SQ_BF16, t_cal, k, ldx, gamma, eps, a, stream);
+    else
+      sqk::launch_col_absmax(x_cal, x_dt == SQ_BF16, t_cal, k, ldx, nullptr, a, stream);
+  }
+  if (w != nullptr)
+    sqk::launch_wrow_absmax_s(w, w_dt == SQ_BF16, k, n, ldw, a, alpha, wmax, s, stream);
+  return hip_status();
+}
+
+sq_status sq_smooth_fold(const float* s, int64_t k, const float* gamma, float* gamma_out,
+                         const void* w, sq_dtype w_dt, int64_t n, int64_t ldw, float* w_out,
+                         hipStream_t stream) {
+  SQ_TRY(check_k(k));
+  if (s == nullptr) return SQ_ERR_NULL;
+  const bool do_w = (w != nullptr && w_out != nullptr);
+  if (do_w) {
+    SQ_TRY(check_mat(w, w_dt, k, n, ldw));
+    if (n % 8 != 0 || !aligned16(w_out)) return SQ_ERR_UNSUPPORTED;
+  }
+  if (gamma_out == nullptr && !do_w) return SQ_OK;
+  if (gamma_out != nullptr) sqk::launch_fold_gamma(s, gamma, gamma_out, k, stream);
+  if (do_w) sqk::launch_fold_w(w, w_dt == SQ_BF16, k, n, ldw, s, w_out, stream);
+  return hip_status();
+}
+
+sq_status sq_quant_weight(const void* w, sq_dtype w_dt, int64_t k, int64_t n, int64_t ldw,
+                          const float* s, int8_t* wq, float* w_scale, hipStream_t stream) {
+  SQ_TRY(check_k(k));
+  SQ_TRY(check_mat(w, w_dt, k, n, ldw));
+  if (wq == nullptr || w_scale == nullptr) return SQ_ERR_NULL;
+  if (n % 8 != 0 || !aligned16(wq)) return SQ_ERR_UNSUPPORTED;
+  if (n == 0) return SQ_OK;
+  sqk::launch_fill_f32(w_scale, n, 0.0f, stream);
+  sqk::launch_col_absmax(w, w_dt == SQ_BF16, k, n, ldw, s, w_scale, stream);
+  sqk::launch_div127(w_scale, n, stream);
+  sqk::launch_quant_weight_t(w, w_dt == SQ_BF16, k, n, ldw, s, w_scale, wq, stream);
+  return hip_status();
+}
+
+sq_status sq_quant_act(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                       sq_norm norm, const float* gamma_f, float eps, int8_t* xq, float* x_scale,
+                       float* row_rscale, hipStream_t stream) {
+  SQ_TRY(check_act(x, x_dt, t, k, ldx, norm, eps));
+  if (xq == nullptr || x_scale == nullptr) return SQ_ERR_NULL;
+  if (!aligned16(xq)) return SQ_ERR_UNSUPPORTED;
+  if (t == 0) return SQ_OK;
+  sqk::launch_quant_act(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps, xq,
+                        x_scale, norm == SQ_NORM_RMS ? row_rscale : nullptr, stream);
+  return hip_status();
+}
+
+sq_status sq_gemm_w8a8(const int8_t* xq, const float* x_scale, int64_t t, int64_t k,
+                       const int8_t* wq, const float* w_scale, int64_t n, const float* bias,
+                       void* y, sq_dtype y_dt, int64_t ldy, int32_t* acc_out,
+                       hipStream_t stream) {
+  SQ_TRY(check_gemm(xq, x_scale, t, k, wq, w_scale, n, y, y_dt, ldy, acc_out));
+  if (t == 0 || n == 0) return SQ_OK;
+  void* out = acc_out != nullptr ? (void*)acc_out : y;
+  sqk::launch_gemm(xq, x_scale, t, k, wq, w_scale, n, bias, out, acc_out ? n : ldy,
+                   gemm_out(y_dt, acc_out), stream);
+  return hip_status();
+}
+
+size_t sq_linear_workspace_bytes(int64_t t, int64_t k) {
+  if (t <= 0 || k <= 0) return 0;
+  return (size_t)(round256(t * k) + round256(t * 4));
+}
+
+sq_status sq_w8a8_linear(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                         sq_norm norm, const float* gamma_f, float eps, const int8_t* wq,
+                         const float* w_scale, int64_t n, const float* bias, void* y,
+                         sq_dtype y_dt, int64_t ldy, void* workspace, size_t ws_bytes,
+                         const sq_debug_out* dbg, hipStream_t stream) {
+  SQ_TRY(check_act(x, x_dt, t, k, ldx, norm, eps));
+  if (t == 0) return wq == nullptr ? SQ_ERR_NULL : SQ_OK;   // nothing to compute
+  int8_t* xq = dbg ? dbg->xq : nullptr;
+  float* xs = dbg ? dbg->x_scale : nullptr;
+  int32_t* acc = dbg ? dbg->acc : nullptr;
+  float* rrow = dbg ? dbg->row_rscale : nullptr;
+  if (xq == nullptr || xs == nullptr) {
+    if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0 ||
+        ws_bytes < sq_linear_workspace_bytes(t, k))
+      return SQ_ERR_WORKSPACE;
+    int8_t* wsb = static_cast<int8_t*>(workspace);
+    if (xq == nullptr) xq = wsb;
+    if (xs == nullptr) xs = reinterpret_cast<float*>(wsb + round256(t * k));
+  }
+  // the GEMM's own checks, with the codes and scales that will exist by then
+  if (w_scale == nullptr && acc == nullptr) return SQ_ERR_NULL;
+  SQ_TRY(check_gemm(xq, xs, t, k, wq, w_scale, n, y, y_dt, ldy, acc));
+  sqk::launch_quant_act(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps, xq, xs,
+                        norm == SQ_NORM_RMS ? rrow : nullptr, stream);
+  SQ_TRY(hip_status());
+  if (n == 0) return SQ_OK;
+  void* out = acc != nullptr ? (void*)acc : y;
+  sqk::launch_gemm(xq, xs, t, k, wq, w_scale, n, bias, out, acc ? n : ldy, gemm_out(y_dt, acc),
+                   stream);
+  return hip_status();
+}
+
+}  // extern "C"
