@@ -46,6 +46,10 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed steps, run one plain elementwise copy kernel over "
+                         "this many MiB (reads and writes that many bytes): the reference "
+                         "that scales the HBM byte counters of a profiling run")
     return ap.parse_args()
 
 
@@ -171,6 +175,13 @@ def main():
     kern_ms = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
                for j, n in enumerate(names)}
     print(f"timed {args.steps} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     ops = 2.0 * T * K * N
     value = ops / (ms_step * 1e-3) / 1e12

@@ -48,6 +48,7 @@ sq_status check_act(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t 
                     float eps) {
   SQ_TRY(check_k(k));
   SQ_TRY(check_mat(x, x_dt, t, k, ldx));
+  if (t > INT32_MAX) return SQ_ERR_UNSUPPORTED;
   if (norm != SQ_NORM_NONE && norm != SQ_NORM_RMS) return SQ_ERR_UNSUPPORTED;
   if (norm == SQ_NORM_RMS && !(eps >= 0.0f && isfinite(eps))) return SQ_ERR_SHAPE;
   return SQ_OK;
