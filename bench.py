@@ -46,6 +46,13 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--rocpd-summary", metavar="DB", default=None,
+                    help="print a text summary of a rocprofv3 result database (kernel "
+                         "durations, or counters per kernel) instead of benchmarking")
+    ap.add_argument("--counters-json", metavar="PATH", default=None,
+                    help="with --rocpd-summary of FETCH_SIZE and WRITE_SIZE databases "
+                         "(comma-separated), write the GEMM's HBM bytes per launch, scaled "
+                         "by the copy probe, to PATH")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run one plain elementwise copy kernel over "
                          "this many MiB (reads and writes that many bytes): the reference "
@@ -72,6 +79,58 @@ def _traffic(gemm_launch_bytes_alg: float):
     if c.get("kernel_source_sha256_16") != _kernel_hash():
         return None
     return c.get("hbm_bytes_per_launch")
+
+
+def _rocpd_rows(db):
+    import sqlite3
+    con = sqlite3.connect(db)
+    names = {r[0] for r in con.execute("select name from sqlite_master where type='view'")}
+    out = {"trace": [], "pmc": []}
+    if "kernels" in names:
+        out["trace"] = list(con.execute(
+            "select name, count(*), avg(duration), min(duration), max(duration) from kernels "
+            "group by name order by sum(duration) desc"))
+    if "counters_collection" in names:
+        out["pmc"] = list(con.execute(
+            "select kernel_name, counter_name, avg(value), count(*), avg(duration) "
+            "from counters_collection group by kernel_name, counter_name order by kernel_name"))
+    return out
+
+
+def _short(name: str) -> str:
+    return name.split("(")[0].replace("void ", "")[:70]
+
+
+def rocpd_summary(dbs: str, counters_json=None) -> None:
+    """Text summary of rocprofv3 result databases (durations in microseconds)."""
+    fetch = write = copy_fetch = copy_write = None
+    for db in dbs.split(","):
+        rows = _rocpd_rows(db)
+        print(f"# {db}")
+        if rows["trace"] and not rows["pmc"]:
+            print(f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+            for n, c, a, lo, hi in rows["trace"]:
+                print(f"{_short(n):70s} {c:6d} {a / 1e3:10.2f} {lo / 1e3:10.2f} {hi / 1e3:10.2f}")
+        for kn, cn, v, c, d in rows["pmc"]:
+            print(f"{_short(kn):70s} {cn:28s} {v:18.1f}  n={c:<4d} avg_us={d / 1e3:.2f}")
+            if "k_gemm_w8a8" in kn and cn == "FETCH_SIZE":
+                fetch = v * 1024.0
+            if "k_gemm_w8a8" in kn and cn == "WRITE_SIZE":
+                write = v * 1024.0
+            if "neg_kernel" in kn and cn == "FETCH_SIZE":
+                copy_fetch = v * 1024.0
+            if "neg_kernel" in kn and cn == "WRITE_SIZE":
+                copy_write = v * 1024.0
+    if counters_json and fetch is not None and write is not None and copy_fetch and copy_write:
+        probe = float(os.environ.get("COPY_PROBE_BYTES", 256 << 20))
+        ff, wf = probe / copy_fetch, probe / copy_write
+        rec = {"kernel_source_sha256_16": _kernel_hash(), "fetch_factor": ff, "write_factor": wf,
+               "fetch_bytes_per_launch": fetch * ff, "write_bytes_per_launch": write * wf,
+               "hbm_bytes_per_launch": fetch * ff + write * wf}
+        with open(counters_json, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(f"# scale factors: fetch {ff:.3f} write {wf:.3f}; GEMM HBM bytes per launch "
+              f"{rec['hbm_bytes_per_launch'] / 2**20:.1f} MiB -> {counters_json}")
 
 
 def cpu_baseline(inp, wl, target_s: float):
@@ -106,6 +165,9 @@ def cpu_baseline(inp, wl, target_s: float):
 
 def main():
     args = _parse()
+    if args.rocpd_summary:
+        rocpd_summary(args.rocpd_summary, args.counters_json)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build measures one GPU only: the layer's multi-GPU "
