@@ -23,9 +23,10 @@
  *   - Argument checks run on the host before any launch and return a status;
  *     nothing is launched when a check fails.  A launch failure reported by
  *     the HIP runtime returns SQ_ERR_HIP.  No call throws across the ABI.
- *   - Supported shapes: K % 64 == 0 and 64 <= K <= 65536; T, N >= 0 (0 launches
- *     nothing); every matrix pointer 16-byte aligned and every leading
- *     dimension a multiple of 16 bytes.  Anything else is SQ_ERR_UNSUPPORTED.
+ *   - Supported shapes: K % 64 == 0 and 64 <= K <= 65536; 0 <= T, N <= 2^24
+ *     (0 launches nothing); every matrix pointer 16-byte aligned and every
+ *     leading dimension a multiple of 16 bytes.  Anything else is
+ *     SQ_ERR_UNSUPPORTED.
  *   - Scales are fp32.  Rounding is IEEE round-to-nearest-even throughout and
  *     no multiply-add is fused, so results are reproducible bit for bit.
  */

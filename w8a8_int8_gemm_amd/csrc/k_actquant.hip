@@ -56,149 +56,126 @@ __device__ __forceinline__ u32x2 quant8_div(const float (&xh)[8], float d) {
 }
 
 // ---------------------------------------------------------------------------
-// K <= 8192: one token per WPR waves (WPR = 1, 2 or 4 of the workgroup's 4
-// waves, so 4/WPR tokens per workgroup pass).  Thread i of a token's 64*WPR
-// threads owns the 8-element chunks i, i + 64*WPR, ... (NV of them), so every
-// load and store of a wave is 1 KiB / 512 B contiguous.  The token's values
-// stay in VGPRs between the max and the quantize pass (HBM is read once and
-// written once); the per-token maximum (and the RMSNorm sum of squares) is
-// combined across the token's waves through LDS.  gamma_f stays in VGPRs for
-// all the tokens a workgroup visits.
+// K <= 8192: one token per wave, WPB tokens per workgroup.  Lane l owns the
+// 8-element chunks l, l + 64, ... (NV of them), so every load of a wave is
+// 1 KiB contiguous and every store 512 B.  The token's raw values stay in
+// VGPRs from the load to the store (HBM is read once and written once) and
+// every reduction stays inside the wave: no workgroup barrier between load
+// and store, so each wave streams on its own.  gamma_f is staged once per
+// workgroup in LDS and read there by both passes (the max pass and the
+// quantize pass recompute x^ with the same fp32 operations).
 // ---------------------------------------------------------------------------
-template <class In, int NV, int WPR, bool NORM>
-__global__ __launch_bounds__(256) void k_quant_act(const typename In::elem* __restrict__ x,
-                                                   int64_t T, int64_t K, int64_t ld,
-                                                   const float* __restrict__ gamma_f, float eps,
-                                                   int8_t* __restrict__ xq,
-                                                   float* __restrict__ xscale,
-                                                   float* __restrict__ rrow) {
-  constexpr int RPB = 4 / WPR;   // tokens per workgroup pass
-  __shared__ float red_m[2][4];
-  __shared__ double red_s[4];
+constexpr int kWavesPerBlock = 8;
+// Up to 16 raw bytes per lane-chunk-slot (bf16 with K <= 4096, fp32 with
+// K <= 2048) the kernel fits 64 VGPRs: ask for 8 waves per SIMD there.
+template <class In, int NV>
+constexpr int quant_act_min_waves() { return In::kBytes * NV <= 16 ? 8 : 1; }
+
+template <class In, int NV, bool NORM>
+__global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV>())) void k_quant_act(
+    const typename In::elem* __restrict__ x, int64_t T, int64_t K, int64_t ld,
+    const float* __restrict__ gamma_f, float eps, int8_t* __restrict__ xq,
+    float* __restrict__ xscale, float* __restrict__ rrow) {
+  // gamma_f of chunk c: elements 0-3 at gs[c], 4-7 at gs[NV * 64 + c] (1
+  // without gamma, 0 past K)
+  __shared__ f32x4 gs[NV * 64 * 2];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int rloc = wave / WPR;
-  const int tl = (wave % WPR) * 64 + lane;
-  const int nchunk = (int)(K >> 3);   // <= 1024 on this path
-  float g[NV][8];
+  const int nchunk = (int)(K >> 3);   // <= 64 * NV
+  for (int i = threadIdx.x; i < NV * 64 * 2; i += 64 * kWavesPerBlock) {
+    const int ch = i % (NV * 64), half = i / (NV * 64);
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (ch < nchunk) {
+      if (gamma_f) v = *reinterpret_cast<const f32x4*>(gamma_f + ch * 8 + half * 4);
+      else v = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+    }
+    gs[i] = v;
+  }
+  __syncthreads();
+  const uint32_t gaddr = lds_addr(&gs[lane]);
+  const int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  if (r >= T) return;
+  const typename In::elem* row = x + r * ld;
+  typename In::Raw raw[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int ch = j * 64 * WPR + tl;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      g[j][i] = (ch < nchunk) ? (gamma_f ? gamma_f[ch * 8 + i] : 1.0f) : 0.0f;
+    const int ch = j * 64 + lane;
+    raw[j] = In::raw8(row + (ch < nchunk ? ch : 0) * 8);
   }
-  const double deps = (double)eps;
-  const double dK = (double)K;
-  const int Ti = (int)T;   // T < 2^31 (checked by the caller)
-  const int step = gridDim.x * RPB;
-  auto load = [&](int rb, typename In::Raw (&raw)[NV]) {
-    const int r = rb + rloc;
-    const typename In::elem* row = x + (int64_t)(r < Ti ? r : 0) * ld;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int ch = j * 64 * WPR + tl;
-      raw[j] = In::raw8(row + (ch < nchunk ? ch : 0) * 8);
-    }
-  };
-  int par = 0;
-  auto process = [&](int rb, const typename In::Raw (&raw)[NV]) {
-    const int r = rb + rloc;
-    const bool ok = r < Ti;
-    float rt = 1.0f;
-    if (NORM) {
-      double ss = 0.0;
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int ch = j * 64 * WPR + tl;
-        float v[8];
-        In::widen(raw[j], v);
-        if (ch < nchunk) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const double dv = (double)v[i];
-            ss = fma(dv, dv, ss);   // exact square, so the same as mul + add
-          }
-        }
-      }
-      ss = wave_sum(ss);
-      if (WPR > 1) {
-        if (lane == 0) red_s[wave] = ss;
-        __syncthreads();
-        ss = red_s[rloc * WPR];
-#pragma unroll
-        for (int w = 1; w < WPR; ++w) ss += red_s[rloc * WPR + w];
-      }
-      rt = (float)(1.0 / sqrt(ss / dK + deps));
-      if (rrow != nullptr && ok && tl == 0) rrow[r] = rt;
-    }
-    float xh[NV][8];
-    float am = 0.0f;
+  float rt = 1.0f;
+  if (NORM) {
+    double ss = 0.0;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       float v[8];
       In::widen(raw[j], v);
+      if (j * 64 + lane < nchunk) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float t = NORM ? v[i] * rt : v[i];
-        xh[j][i] = t * g[j][i];   // g is 0 on chunks past K
-        am = fmaxf(am, fabsf(xh[j][i]));
-      }
-    }
-    am = wave_max(am);
-    if (WPR > 1) {
-      // two buffers, so the next token's writes cannot race this token's reads
-      if (lane == 0) red_m[par][wave] = am;
-      __syncthreads();
-      float m = red_m[par][rloc * WPR];
-#pragma unroll
-      for (int w = 1; w < WPR; ++w) m = fmaxf(m, red_m[par][rloc * WPR + w]);
-      am = m;
-      par ^= 1;
-    }
-    const float d = am / 127.0f;
-    const float rc = 1.0f / d;
-    // d == 0: every x^ is 0 and rc = 0 gives code 0.  1/d overflowing (d tiny):
-    // every chunk is redone by IEEE division below.
-    const bool fast = rc <= 3.0e38f;
-    const float rcu = fast ? rc : 0.0f;
-    if (ok) {
-      if (tl == 0) xscale[r] = d;
-      int8_t* qrow = xq + (int64_t)r * K;
-      uint32_t redo = (!fast && d > 0.0f) ? ~0u : 0u;
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int ch = j * 64 * WPR + tl;
-        bool tie;
-        const u32x2 c = quant8(xh[j], rcu, tie);
-        redo |= (tie ? 1u : 0u) << j;
-        if (ch < nchunk) *reinterpret_cast<u32x2*>(qrow + ch * 8) = c;
-      }
-      // rare: chunks with a quotient near a rounding tie, by IEEE division
-      if (redo != 0u) {
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          const int ch = j * 64 * WPR + tl;
-          if (((redo >> j) & 1u) && ch < nchunk)
-            *reinterpret_cast<u32x2*>(qrow + ch * 8) = quant8_div(xh[j], d);
+        for (int i = 0; i < 8; ++i) {
+          const double dv = (double)v[i];
+          ss = fma(dv, dv, ss);   // exact square, so the same as mul + add
         }
       }
     }
-  };
-  // one token ahead: the next pass's loads are in flight while this one is
-  // reduced, quantized and stored
-  typename In::Raw ra[NV], rb2[NV];
-  int rb = blockIdx.x * RPB;
-  if (rb < Ti) load(rb, ra);
-  while (rb < Ti) {
-    if (rb + step < Ti) load(rb + step, rb2);
-    process(rb, ra);
-    rb += step;
-    if (rb >= Ti) break;
-    if (rb + step < Ti) load(rb + step, ra);
-    process(rb, rb2);
-    rb += step;
+    ss = wave_sum(ss);
+    rt = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+    if (rrow != nullptr && lane == 0) rrow[r] = rt;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) In::opaque(raw[j]);
   }
+  // x^ of chunk j, the same fp32 operations in both passes.  gamma is read
+  // from LDS chunk by chunk, with the wait in the same asm block: the
+  // compiler cannot then hoist every chunk's gamma into VGPRs at once.
+  auto smooth = [&](auto jc, float (&xh)[8]) {
+    constexpr int j = decltype(jc)::value;
+    float v[8];
+    In::widen(raw[j], v);
+    f32x4 g0, g1;
+    asm volatile("ds_read_b128 %0, %2 offset:%3\n\tds_read_b128 %1, %2 offset:%4\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(g0), "=v"(g1)
+                 : "v"(gaddr), "n"(j * 1024), "n"(NV * 1024 + j * 1024)
+                 : "memory");
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float t = NORM ? v[i] * rt : v[i];
+      xh[i] = t * (i < 4 ? g0[i] : g1[i - 4]);   // gamma is 0 past K
+    }
+  };
+  float am = 0.0f;
+  static_for<NV>([&](auto jc) {
+    float xh[8];
+    smooth(jc, xh);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(xh[i]));
+  });
+  am = wave_max(am);
+  // Keep only the raw values alive between the passes: the quantize pass
+  // widens them again and re-reads gamma from LDS (the compiler would otherwise
+  // keep every chunk's x^ in VGPRs and quarter the occupancy).
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < NV; ++j) In::opaque(raw[j]);
+  const float d = am / 127.0f;
+  const float rc = 1.0f / d;
+  // d == 0: every x^ is 0 and rc = 0 gives code 0.  1/d overflowing (d tiny):
+  // every chunk takes the IEEE division below.
+  const bool fast = rc <= 3.0e38f;
+  const float rcu = fast ? rc : 0.0f;
+  if (lane == 0) xscale[r] = d;
+  int8_t* qrow = xq + r * K;
+  // exact path for the whole row when 1/d overflows
+  const bool all_div = !fast && d > 0.0f;
+  static_for<NV>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const int ch = j * 64 + lane;
+    float xh[8];
+    smooth(jc, xh);
+    bool tie;
+    u32x2 c = quant8(xh, rcu, tie);
+    // rare: a quotient near a rounding tie; redo the chunk by IEEE division
+    if (tie || all_div) c = quant8_div(xh, d);
+    if (ch < nchunk) *reinterpret_cast<u32x2*>(qrow + ch * 8) = c;
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -278,26 +255,23 @@ __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem*
 // host launcher
 // ---------------------------------------------------------------------------
 
-template <class In, int NV, int WPR, bool NORM>
+template <class In, int NV, bool NORM>
 static void quant_act_nv(const void* x, int64_t T, int64_t K, int64_t ld, const float* gamma_f,
                          float eps, int8_t* xq, float* xscale, float* rrow, hipStream_t st) {
-  constexpr int RPB = 4 / WPR;
-  // up to 2048 workgroups; each visits the tokens blockIdx*RPB + i*gridDim*RPB
-  int64_t blocks = (T + RPB - 1) / RPB;
-  if (blocks > 2048) blocks = 2048;
-  hipLaunchKernelGGL((k_quant_act<In, NV, WPR, NORM>), dim3((unsigned)blocks), dim3(256), 0, st,
-                     (const typename In::elem*)x, T, K, ld, gamma_f, eps, xq, xscale, rrow);
+  const int64_t blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL((k_quant_act<In, NV, NORM>), dim3((unsigned)blocks), dim3(64 * kWavesPerBlock),
+                     0, st, (const typename In::elem*)x, T, K, ld, gamma_f, eps, xq, xscale, rrow);
 }
 
 template <class In, bool NORM>
 static void quant_act_t(const void* x, int64_t T, int64_t K, int64_t ld, const float* gamma_f,
                         float eps, int8_t* xq, float* xscale, float* rrow, hipStream_t st) {
   const int64_t nchunk = K / 8;
-  if (nchunk <= 64) quant_act_nv<In, 1, 1, NORM>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
-  else if (nchunk <= 128) quant_act_nv<In, 1, 2, NORM>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
-  else if (nchunk <= 256) quant_act_nv<In, 1, 4, NORM>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
-  else if (nchunk <= 512) quant_act_nv<In, 2, 4, NORM>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
-  else if (nchunk <= 1024) quant_act_nv<In, 4, 4, NORM>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
+  if (nchunk <= 64) quant_act_nv<In, 1, NORM>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
+  else if (nchunk <= 128) quant_act_nv<In, 2, NORM>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
+  else if (nchunk <= 256) quant_act_nv<In, 4, NORM>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
+  else if (nchunk <= 512) quant_act_nv<In, 8, NORM>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
+  else if (nchunk <= 1024) quant_act_nv<In, 16, NORM>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
   else
     hipLaunchKernelGGL((k_quant_act_wide<In, NORM>), dim3((unsigned)T), dim3(256), 0, st,
                        (const typename In::elem*)x, T, K, ld, gamma_f, eps, xq, xscale, rrow);

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void k_col_absmax(const typename In::elem* __r
                                                     float* __restrict__ out) {
   __shared__ float red[4][512];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t c0 = (int64_t)blockIdx.x * 512 + lane * 8;
   const bool active = c0 < cols;   // cols % 8 == 0, so a lane is all-in or all-out
   float mx[8];
@@ -48,16 +48,20 @@ __global__ __launch_bounds__(256) void k_col_absmax(const typename In::elem* __r
   if (active) {
     const typename In::elem* base = m + c0;
     for (; r + (U - 1) * step < rows; r += U * step) {
+      // the U rows' loads (and their row scales) all in flight before any use
       typename In::Raw raw[U];
+      float sc[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) raw[u] = In::raw8(base + (r + u * step) * ld);
+      for (int u = 0; u < U; ++u) {
+        raw[u] = In::raw8(base + (r + u * step) * ld);
+        sc[u] = kRowScale ? rs[r + u * step] : 1.0f;
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float v[8];
         In::widen(raw[u], v);
-        const float sc = kRowScale ? rs[r + u * step] : 1.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(kRowScale ? v[i] * sc : v[i]));
+        for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(kRowScale ? v[i] * sc[u] : v[i]));
       }
     }
     for (; r < rows; r += step) {
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(256) void k_wrow_absmax_s(const typename In::elem* 
                                                        float* __restrict__ wmax,
                                                        float* __restrict__ s) {
   const int lane = threadIdx.x & 63;
-  const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t j = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (j >= K) return;
   const typename In::elem* row = w + j * ld;
   float mx = 0.0f;
@@ -282,10 +286,10 @@ void launch_wrow_absmax_s(const void* w, bool bf16, int64_t K, int64_t N, int64_
   if (K <= 0) return;
   const dim3 grid((unsigned)((K + 3) / 4));
   if (bf16)
-    hipLaunchKernelGGL((k_wrow_absmax_s<Bf16In, 4>), grid, dim3(256), 0, st, (const uint16_t*)w,
+    hipLaunchKernelGGL((k_wrow_absmax_s<Bf16In, 8>), grid, dim3(256), 0, st, (const uint16_t*)w,
                        K, N, ld, a, alpha, wmax, s);
   else
-    hipLaunchKernelGGL((k_wrow_absmax_s<F32In, 2>), grid, dim3(256), 0, st, (const float*)w, K, N,
+    hipLaunchKernelGGL((k_wrow_absmax_s<F32In, 4>), grid, dim3(256), 0, st, (const float*)w, K, N,
                        ld, a, alpha, wmax, s);
 }
 

@@ -72,29 +72,44 @@ __global__ __launch_bounds__(256) void k_quant_weight_t(const typename In::elem*
   const bool ncol = nb < N;   // N % 8 == 0: a thread's 8 columns are all valid or none
 
   float d[8];
+  {
+    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4 d0 = ncol ? *reinterpret_cast<const f32x4*>(wscale + nb) : z;
+    const f32x4 d1 = ncol ? *reinterpret_cast<const f32x4*>(wscale + nb + 4) : z;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) d[i] = ncol ? wscale[nb + i] : 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      d[i] = d0[i];
+      d[4 + i] = d1[i];
+    }
+  }
 
+  // all four rows' loads in flight at once (rows past K read row K-1 and
+  // are dropped; columns past N read column 0 and are dropped)
+  typename In::Raw raw[4];
+  float sk[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t k = min(k0 + ty * 4 + r, K - 1);
+    raw[r] = In::raw8(w + k * ld + (ncol ? nb : 0));
+    sk[r] = kRowScale ? s[k] : 1.0f;
+  }
   uint32_t packed[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) packed[i] = 0u;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t k = k0 + ty * 4 + r;
-    if (ncol && k < K) {
-      float v[8];
-      In::load8(w + k * ld + nb, v);
-      const float sk = kRowScale ? s[k] : 1.0f;
+    float v[8];
+    In::widen(raw[r], v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float wh = kRowScale ? v[i] * sk : v[i];
-        float q = 0.0f;
-        if (d[i] != 0.0f) {
-          q = rintf(wh / d[i]);
-          q = fminf(fmaxf(q, -127.0f), 127.0f);
-        }
-        packed[i] |= code_byte(q) << (8 * r);
+    for (int i = 0; i < 8; ++i) {
+      const float wh = kRowScale ? v[i] * sk[r] : v[i];
+      float q = 0.0f;
+      if (d[i] != 0.0f) {
+        q = rintf(wh / d[i]);
+        q = fminf(fmaxf(q, -127.0f), 127.0f);
       }
+      if (ncol && k < K) packed[i] |= code_byte(q) << (8 * r);
     }
   }
 #pragma unroll

@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace sqk {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -14,6 +17,21 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// byte address of a __shared__ object, as LDS instructions take it
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
 
 // bf16 halves of a packed 32-bit word, widened exactly to fp32
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -36,7 +54,7 @@ struct Bf16In {
   struct Raw { u32x4 v; };
   __device__ __forceinline__ static Raw raw8(const uint16_t* p) {
     Raw r;
-    r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    r.v = *reinterpret_cast<const u32x4*>(p);
     return r;
   }
   __device__ __forceinline__ static Raw raw8_cached(const uint16_t* p) {
@@ -44,6 +62,9 @@ struct Bf16In {
     r.v = *reinterpret_cast<const u32x4*>(p);
     return r;
   }
+  // hide the value from the optimizer, so that values derived from it are
+  // recomputed rather than kept alive
+  __device__ __forceinline__ static void opaque(Raw& r) { asm volatile("" : "+v"(r.v)); }
   __device__ __forceinline__ static void widen(const Raw& r, float (&o)[8]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -68,8 +89,8 @@ struct F32In {
   struct Raw { f32x4 a, b; };
   __device__ __forceinline__ static Raw raw8(const float* p) {
     Raw r;
-    r.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-    r.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+    r.a = *reinterpret_cast<const f32x4*>(p);
+    r.b = *reinterpret_cast<const f32x4*>(p + 4);
     return r;
   }
   __device__ __forceinline__ static Raw raw8_cached(const float* p) {
@@ -77,6 +98,10 @@ struct F32In {
     r.a = *reinterpret_cast<const f32x4*>(p);
     r.b = *reinterpret_cast<const f32x4*>(p + 4);
     return r;
+  }
+  __device__ __forceinline__ static void opaque(Raw& r) {
+    asm volatile("" : "+v"(r.a));
+    asm volatile("" : "+v"(r.b));
   }
   __device__ __forceinline__ static void widen(const Raw& r, float (&o)[8]) {
 #pragma unroll

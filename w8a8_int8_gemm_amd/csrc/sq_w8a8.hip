@@ -11,6 +11,7 @@
 namespace {
 
 constexpr int64_t kMaxK = 65536;
+constexpr int64_t kMaxRows = int64_t(1) << 24;   // tokens (T) and output channels (N) per call
 constexpr int64_t kMaxNormCalibK = 8192;
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -48,7 +49,7 @@ sq_status check_act(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t 
                     float eps) {
   SQ_TRY(check_k(k));
   SQ_TRY(check_mat(x, x_dt, t, k, ldx));
-  if (t > INT32_MAX) return SQ_ERR_UNSUPPORTED;
+  if (t > kMaxRows) return SQ_ERR_UNSUPPORTED;
   if (norm != SQ_NORM_NONE && norm != SQ_NORM_RMS) return SQ_ERR_UNSUPPORTED;
   if (norm == SQ_NORM_RMS && !(eps >= 0.0f && isfinite(eps))) return SQ_ERR_SHAPE;
   return SQ_OK;
@@ -60,7 +61,9 @@ sq_status check_gemm(const int8_t* xq, const float* xs, int64_t t, int64_t k, co
   SQ_TRY(check_k(k));
   if (xq == nullptr || wq == nullptr) return SQ_ERR_NULL;
   if (t < 0 || n < 0) return SQ_ERR_SHAPE;
-  if (t > INT32_MAX || n > INT32_MAX) return SQ_ERR_UNSUPPORTED;
+  if (t > kMaxRows || n > kMaxRows) return SQ_ERR_UNSUPPORTED;
+  // launch grids stay far below 2^32 work-items
+  if (((t + 127) / 128) * ((n + 127) / 128) > (int64_t(1) << 22)) return SQ_ERR_UNSUPPORTED;
   if (!aligned16(xq) || !aligned16(wq)) return SQ_ERR_UNSUPPORTED;
   if (acc_out != nullptr) {
     if (!aligned16(acc_out)) return SQ_ERR_UNSUPPORTED;
