@@ -13,10 +13,16 @@ calibration tokens, alpha 0.5, bf16 in and out), inputs resident in HBM:
 
 `value` is 2*T*K*N integer ops per step / step time (TOPS).  Every kernel is
 also timed on its own with HIP events on the stream it runs on; the roofline
-object is for the GEMM (MFMA bound, against the INT8 dense peak).  The CPU
-oracle is timed on the host on the same inputs (a bounded sample of tokens).
+object is for the GEMM (MFMA bound, against the INT8 dense peak).  The steps
+take their inputs in turn from --sets copies in HBM, so the 256 MB Infinity
+Cache does not hold a step's inputs from the step before.  The CPU oracle is
+timed on the host on the same inputs (a bounded sample of tokens).
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+Untimed extras on the same line: the layer's output error against the fp64
+product per migration strength alpha (and without smoothing), and the
+decode-shaped GEMM (16 x 8192 x 8192, HBM bound) in GB/s.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-extras]
 """
 from __future__ import annotations
 
@@ -53,6 +59,11 @@ def _parse():
                     help="with --rocpd-summary of FETCH_SIZE and WRITE_SIZE databases "
                          "(comma-separated), write the GEMM's HBM bytes per launch, scaled "
                          "by the copy probe, to PATH")
+    ap.add_argument("--sets", type=int, default=3,
+                    help="copies of the input set (X_cal, X, W) in HBM, used in turn by the "
+                         "steps, so that no step finds its inputs in the 256 MB Infinity Cache")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the untimed extras: the error per alpha and the decode GEMM")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run one plain elementwise copy kernel over "
                          "this many MiB (reads and writes that many bytes): the reference "
@@ -133,6 +144,78 @@ def rocpd_summary(dbs: str, counters_json=None) -> None:
               f"{rec['hbm_bytes_per_launch'] / 2**20:.1f} MiB -> {counters_json}")
 
 
+def alpha_sweep(sq, torch, inp, wl, x_cal, x, w, bias, dev, sample=256):
+    """Relative Frobenius error of the W8A8 layer output against X W + b in
+    fp64, per migration strength alpha and without smoothing (s = 1), over a
+    sample of tokens.  Untimed; the GPU computes every layer output, numpy
+    computes the fp64 reference of the sampled rows."""
+    import numpy as np
+
+    T, K, N = wl.T, wl.K, wl.N
+    rows = np.linspace(0, T - 1, sample).astype(np.int64)
+
+    def f64(bits):
+        return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+    ref = f64(inp.x[rows]) @ f64(inp.w) + inp.bias.astype(np.float64)[None, :]
+    ref_norm = float(np.linalg.norm(ref))
+    e = lambda n: torch.empty(n, dtype=torch.float32, device=dev)  # noqa: E731
+    a, wm, s, gp, wsc, xs = e(K), e(K), e(K), e(K), e(N), e(T)
+    wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    xq = torch.empty((T, K), dtype=torch.int8, device=dev)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    sq.sq_calibrate(x_cal, None, 0.5, a)           # activation absmax once
+    res = {}
+    for alpha in (None, 0.1, 0.25, 0.5, 0.75, 1.0):
+        if alpha is None:                          # unsmoothed: s = 1, gamma_f = 1
+            sq.sq_quant_weight(w, None, wq, wsc)
+            sq.sq_quant_act(x, None, xq, xs)
+        else:
+            sq.sq_calibrate(None, w, alpha, a, wm, s)   # s from the stored absmax
+            sq.sq_smooth_fold(s, None, gp)
+            sq.sq_quant_weight(w, s, wq, wsc)
+            sq.sq_quant_act(x, gp, xq, xs)
+        sq.sq_gemm_w8a8(xq, xs, wq, wsc, y, bias=bias)
+        torch.cuda.synchronize()
+        yb = y[torch.from_numpy(rows).to(dev)].view(torch.int16).cpu().numpy().view(np.uint16)
+        err = float(np.linalg.norm(f64(yb) - ref)) / ref_norm
+        res["unsmoothed" if alpha is None else f"{alpha:g}"] = err
+    res["tokens"] = int(sample)
+    res["reference"] = "X W + b in fp64 over evenly spaced tokens; relative Frobenius norm"
+    return res
+
+
+def decode_gemm(sq, torch, dev, T=16, K=8192, N=8192, copies=5, iters=50):
+    """Decode-shaped INT8 GEMM (16 tokens, K = N = 8192): HBM-bound on the
+    64 MiB weight.  Five weight copies (320 MiB) are used in turn so that the
+    weight never sits in the Infinity Cache.  Returns the event time per call
+    and the algorithmic bytes moved per second."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(105)
+    wqs = [torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev, generator=g)
+           for _ in range(copies)]
+    xq = torch.randint(-127, 128, (T, K), dtype=torch.int8, device=dev, generator=g)
+    xs = torch.rand(T, device=dev, generator=g) * 1e-2
+    ws = torch.rand(N, device=dev, generator=g) * 1e-3
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(copies):
+        sq.sq_gemm_w8a8(xq, xs, wqs[i], ws, y, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(iters):
+        sq.sq_gemm_w8a8(xq, xs, wqs[i % copies], ws, y, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    byts = K * N + T * K + 4.0 * (T + N) + 2.0 * T * N
+    gbs = byts / (us * 1e-6) / 1e9
+    return {"workload": f"decode T={T} K={K} N={N}", "us": us, "achieved": gbs, "unit": "GB/s",
+            "frac_of_peak": gbs / PEAK_HBM_GBS,
+            "algorithmic": "K*N weight bytes + T*K + scales + 2*T*N output bytes per call"}
+
+
 def cpu_baseline(inp, wl, target_s: float):
     import numpy as np  # noqa: F401
 
@@ -195,7 +278,9 @@ def main():
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    x_cal, x, w, bias = d(inp.x_cal), d(inp.x), d(inp.w), d(inp.bias)
+    nsets = max(1, args.sets)
+    sets = [(d(inp.x_cal), d(inp.x), d(inp.w)) for _ in range(nsets)]
+    bias = d(inp.bias)
     f = lambda n: torch.empty(n, dtype=torch.float32, device=dev)  # noqa: E731
     a, wm, s, gp, wsc, xs = f(K), f(K), f(K), f(K), f(N), f(T)
     wq = torch.empty((N, K), dtype=torch.int8, device=dev)
@@ -204,7 +289,8 @@ def main():
     stream = torch.cuda.current_stream()
     names = ["calibrate", "smooth_fold", "quant_weight", "quant_act", "gemm"]
 
-    def step(ev=None):
+    def step(ev=None, i=0):
+        x_cal, x, w = sets[i % nsets]
         if ev is not None:
             ev[0].record(stream)
         sq.sq_calibrate(x_cal, w, wl.alpha, a, wm, s, stream=stream)
@@ -223,14 +309,14 @@ def main():
         if ev is not None:
             ev[5].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i=i)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(evs[i], i=args.warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -286,6 +372,10 @@ def main():
         "kernels": kernels,
         "device": torch.cuda.get_device_properties(0).name,
     }
+    if not args.no_extras:
+        x_cal, x, w = sets[0]
+        out["alpha_sweep"] = alpha_sweep(sq, torch, inp, wl, x_cal, x, w, bias, dev)
+        out["decode_gemm"] = decode_gemm(sq, torch, dev)
     if not args.no_cpu_baseline:
         print("timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_seconds)
