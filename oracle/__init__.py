@@ -58,6 +58,9 @@ def _load():
         _lib.oracle_fold.argtypes = [P, I64, P, P, P, I, I64, I64, P]
         _lib.oracle_quant_weight.argtypes = [P, I64, I64, I64, P, P]
         _lib.oracle_quant_act.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, P, P]
+        _lib.oracle_static_scale.argtypes = [P, I, I64, I64, I64, I, F, P]
+        _lib.oracle_static_scale.restype = F
+        _lib.oracle_quant_act_static.argtypes = [P, I, I64, I64, I64, I, P, F, P, F, P, P, P]
         _lib.oracle_int_gemm.argtypes = [P, P, I64, I64, I64, P]
         _lib.oracle_int_gemm.restype = I64
         _lib.oracle_epilogue.argtypes = [P, P, P, P, I64, I64, P]
@@ -168,6 +171,28 @@ def quant_act(x: np.ndarray, gamma_f=None, *, norm: bool = False, r: Optional[np
     return q, xs, rout
 
 
+def static_scale(x_cal: np.ndarray, gamma_f=None, *, norm: bool = False, eps: float = 1e-6) -> np.float32:
+    """Per-tensor activation step from the calibration tokens' maximum of x^."""
+    x, bf = _mat(x_cal)
+    T, K = x.shape
+    return np.float32(_load().oracle_static_scale(_p(x), bf, T, K, K, int(norm), float(eps),
+                                                  _p(_f32(gamma_f))))
+
+
+def quant_act_static(x: np.ndarray, delta, gamma_f=None, *, norm: bool = False,
+                     r: Optional[np.ndarray] = None, eps: float = 1e-6):
+    """(q [T,K] int8, x_scale [T] fp32 = delta, r [T] fp32 or None) with a fixed step."""
+    x, bf = _mat(x)
+    T, K = x.shape
+    q = np.empty((T, K), np.int8)
+    xs = np.empty(T, np.float32)
+    rout = np.empty(T, np.float32) if norm else None
+    _load().oracle_quant_act_static(_p(x), bf, T, K, K, int(norm), _p(_f32(r)), float(eps),
+                                    _p(_f32(gamma_f)), float(np.float32(delta)), _p(q), _p(xs),
+                                    _p(rout))
+    return q, xs, rout
+
+
 def int_gemm(q: np.ndarray, qw: np.ndarray) -> np.ndarray:
     q = np.ascontiguousarray(q, dtype=np.int8)
     qw = np.ascontiguousarray(qw, dtype=np.int8)
@@ -217,6 +242,15 @@ def prepare_weight(w, s, gamma=None):
 def linear(x, gamma_f, qw, w_scale, bias=None, *, norm=False, r=None, eps=1e-6, out_bf16=True):
     """The online forward: quantize activations, integer GEMM, epilogue."""
     q, xs, rr = quant_act(x, gamma_f, norm=norm, r=r, eps=eps)
+    acc = int_gemm(q, qw)
+    y = epilogue(acc, xs, w_scale, bias)
+    return dict(q=q, x_scale=xs, r=rr, acc=acc, y32=y, y=to_bf16(y) if out_bf16 else y)
+
+
+def linear_static(x, delta, gamma_f, qw, w_scale, bias=None, *, norm=False, r=None, eps=1e-6,
+                  out_bf16=True):
+    """The online forward with one static activation step for every token."""
+    q, xs, rr = quant_act_static(x, delta, gamma_f, norm=norm, r=r, eps=eps)
     acc = int_gemm(q, qw)
     y = epilogue(acc, xs, w_scale, bias)
     return dict(q=q, x_scale=xs, r=rr, acc=acc, y32=y, y=to_bf16(y) if out_bf16 else y)

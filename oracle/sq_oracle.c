@@ -28,6 +28,13 @@
  *                  section 7; "Taming the Outliers", the quantization equation).
  *   quant_act      one dynamic symmetric scale per token, same quantizer
  *                  ("06 -- SmoothQuant", section 7).
+ *   static_scale   one activation step for the whole tensor, from the
+ *                  calibration tokens' maximum ("SmoothQuant and W8A8", One
+ *                  layer, measured; "06 -- SmoothQuant", section 7: per-token
+ *                  or per-tensor activation scales).
+ *   quant_act_static  the same quantizer with that fixed step: values past the
+ *                  calibrated maximum clip to +-127 ("SmoothQuant and W8A8",
+ *                  Gotchas: a static scale clips what calibration never saw).
  *   int_gemm       acc = sum_k q[t,k] * qw[n,k] in int64 ("06 -- SmoothQuant",
  *                  section 7: INT8 x INT8 -> INT32).
  *   epilogue       y = (Delta_t * Delta_n) * acc + bias ("06 -- SmoothQuant",
@@ -206,6 +213,60 @@ void oracle_quant_act(const void *x, int is_bf16, int64_t T, int64_t K, int64_t 
         q[t * K + k] = (d == 0.0f) ? (int8_t)0 : code_of(xh[k] / d);
     }
     free(xh);
+  }
+  free(r);
+}
+
+/* x^[t,k] of one element, as the activation quantizer forms it */
+static float smoothed(const void *x, int is_bf16, int64_t i, int norm, float r, const float *gamma_f,
+                      int64_t k) {
+  float v = elem(x, is_bf16, i);
+  if (norm) v = v * r;
+  return v * (gamma_f ? gamma_f[k] : 1.0f);
+}
+
+/* Static per-tensor step: Delta = fp32( max over every calibration token t and
+   channel k of |x^[t,k]| / 127 ), with x^ formed exactly as in oracle_quant_act. */
+float oracle_static_scale(const void *x, int is_bf16, int64_t T, int64_t K, int64_t ld, int norm,
+                          float eps, const float *gamma_f) {
+  float *r = NULL;
+  if (norm) {
+    r = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1));
+    oracle_rms_rscale(x, is_bf16, T, K, ld, eps, r);
+  }
+  float amax = 0.0f;
+#pragma omp parallel for schedule(static) reduction(max : amax)
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t k = 0; k < K; ++k)
+      amax = fmaxf(amax, fabsf(smoothed(x, is_bf16, t * ld + k, norm, norm ? r[t] : 1.0f,
+                                        gamma_f, k)));
+  free(r);
+  return amax / 127.0f;
+}
+
+/* Static quantization with a fixed step `delta` for every token:
+   q = code(x^ / delta), clamped to [-127, 127] (code_of), so values past the
+   calibrated maximum clip; x_scale[t] = delta.  delta == 0 gives codes 0.
+   r_in / r_out as in oracle_quant_act. */
+void oracle_quant_act_static(const void *x, int is_bf16, int64_t T, int64_t K, int64_t ld,
+                             int norm, const float *r_in, float eps, const float *gamma_f,
+                             float delta, int8_t *q, float *x_scale, float *r_out) {
+  float *r = NULL;
+  if (norm) {
+    r = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1));
+    if (r_in)
+      memcpy(r, r_in, sizeof(float) * (size_t)T);
+    else
+      oracle_rms_rscale(x, is_bf16, T, K, ld, eps, r);
+    if (r_out) memcpy(r_out, r, sizeof(float) * (size_t)T);
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    x_scale[t] = delta;
+    for (int64_t k = 0; k < K; ++k) {
+      float v = smoothed(x, is_bf16, t * ld + k, norm, norm ? r[t] : 1.0f, gamma_f, k);
+      q[t * K + k] = (delta == 0.0f) ? (int8_t)0 : code_of(v / delta);
+    }
   }
   free(r);
 }

@@ -428,3 +428,78 @@ def test_evaluation_script_shape():
         gp, qw, ws = oracle.prepare_weight(W, s)
         errs.append(oracle.rel_error(ref, oracle.linear(xt, gp, qw, ws, out_bf16=False)["y32"]))
     assert errs[1] < errs[0], errs
+
+
+# ---------------------------------------------------------------------------
+# static per-tensor activation step ("SmoothQuant and W8A8", One layer,
+# measured: one scale per tensor from the calibration tokens' maximum; Gotchas:
+# what the calibration never saw is clipped)
+# ---------------------------------------------------------------------------
+
+def test_static_scale_worked_values():
+    # a calibration set whose largest |x| is amax gives the pages' step, and
+    # the worked value maps to the printed code through the static path
+    for r in _golden_rows("quantizer_worked.txt"):
+        amax, value, delta_printed, tol, code = r.split()
+        cal = np.array([[float(amax), 0.1], [-0.5 * float(amax), 0.0]], np.float32)
+        d = oracle.static_scale(cal)
+        assert abs(float(d) - float(delta_printed)) <= float(tol), r
+        q, xs, _ = oracle.quant_act_static(np.array([[float(value), 0.0]], np.float32), d)
+        assert int(q[0, 0]) == int(code), r
+        assert xs[0] == d
+
+
+def test_static_equals_dynamic_on_the_calibration_maximum():
+    # a token that holds the calibration maximum has the same step, hence the
+    # same codes, under the static and the per-token quantizer
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((64, 256)).astype(np.float32)
+    x[:, 9] *= 40
+    g = rng.uniform(0.5, 1.5, 256).astype(np.float32)
+    d = oracle.static_scale(x, g)
+    t = int(np.argmax(np.abs(x * g).max(axis=1)))
+    qs, _, _ = oracle.quant_act_static(x[t:t + 1], d, g)
+    qd, xd, _ = oracle.quant_act(x[t:t + 1], g)
+    assert xd[0] == d
+    np.testing.assert_array_equal(qs, qd)
+
+
+def test_static_quant_clips_past_the_calibrated_maximum():
+    rng = np.random.default_rng(22)
+    cal = rng.standard_normal((32, 16)).astype(np.float32)
+    d = oracle.static_scale(cal)
+    x = (rng.standard_normal((8, 16)) * 3).astype(np.float32)   # well past the calibration range
+    q, _, _ = oracle.quant_act_static(x, d)
+    assert np.abs(q).max() == 127
+    for t in range(8):
+        for k in range(16):
+            qq = float(x[t, k]) / float(d)
+            assert abs(abs(qq - math.floor(qq)) - 0.5) > 1e-4
+            c, _ = _nearest_code_bruteforce(x[t, k], d)   # searches -127..127 only
+            assert q[t, k] == c, (t, k, qq)
+
+
+def test_static_scale_norm_mode_by_channel_maxima():
+    # max over tokens and channels of |fp32(fp32(h r_t) g_k)| equals
+    # max_k fp32(max_t |fp32(h r_t)| * |g_k|): rounding is monotone and sign
+    # symmetric, the route the GPU takes from the channel maxima
+    rng = np.random.default_rng(23)
+    h = rng.standard_normal((96, 320)).astype(np.float32)
+    h[:, 5] *= 30
+    g = rng.uniform(-1.5, 1.5, 320).astype(np.float32)
+    d = oracle.static_scale(h, g, norm=True)
+    m = oracle.act_absmax(h, norm=True, gamma=None)
+    via = F32(np.max((m * np.abs(g)).astype(np.float32)) / F32(127.0))
+    assert d == via
+    # and with no norm the same identity on the raw absmax
+    d0 = oracle.static_scale(h, g)
+    a0 = oracle.act_absmax(h)
+    assert d0 == F32(np.max((a0 * np.abs(g)).astype(np.float32)) / F32(127.0))
+
+
+def test_static_zero_step_gives_zero_codes():
+    x = np.zeros((3, 64), np.float32)
+    d = oracle.static_scale(x)
+    assert d == 0.0
+    q, xs, _ = oracle.quant_act_static(np.ones((2, 64), np.float32), d)
+    assert not q.any() and not xs.any()
