@@ -19,8 +19,10 @@ Cache does not hold a step's inputs from the step before.  The CPU oracle is
 timed on the host on the same inputs (a bounded sample of tokens).
 
 Untimed extras on the same line: the layer's output error against the fp64
-product per migration strength alpha (and without smoothing), and the
-decode-shaped GEMM (16 x 8192 x 8192, HBM bound) in GB/s.
+product per migration strength alpha (and without smoothing), with per-token
+and with static per-tensor activation steps; the static-step activation
+quantizer's time next to the per-token one; and the decode-shaped GEMM
+(16 x 8192 x 8192, HBM bound) in GB/s.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-extras]
 """
@@ -164,25 +166,57 @@ def alpha_sweep(sq, torch, inp, wl, x_cal, x, w, bias, dev, sample=256):
     wq = torch.empty((N, K), dtype=torch.int8, device=dev)
     xq = torch.empty((T, K), dtype=torch.int8, device=dev)
     y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    d = e(1)
     sq.sq_calibrate(x_cal, None, 0.5, a)           # activation absmax once
-    res = {}
+    res, res_static = {}, {}
     for alpha in (None, 0.1, 0.25, 0.5, 0.75, 1.0):
+        key = "unsmoothed" if alpha is None else f"{alpha:g}"
+        gamma_f = None
         if alpha is None:                          # unsmoothed: s = 1, gamma_f = 1
             sq.sq_quant_weight(w, None, wq, wsc)
-            sq.sq_quant_act(x, None, xq, xs)
         else:
             sq.sq_calibrate(None, w, alpha, a, wm, s)   # s from the stored absmax
             sq.sq_smooth_fold(s, None, gp)
             sq.sq_quant_weight(w, s, wq, wsc)
-            sq.sq_quant_act(x, gp, xq, xs)
-        sq.sq_gemm_w8a8(xq, xs, wq, wsc, y, bias=bias)
-        torch.cuda.synchronize()
-        yb = y[torch.from_numpy(rows).to(dev)].view(torch.int16).cpu().numpy().view(np.uint16)
-        err = float(np.linalg.norm(f64(yb) - ref)) / ref_norm
-        res["unsmoothed" if alpha is None else f"{alpha:g}"] = err
+            gamma_f = gp
+        for static, out in ((False, res), (True, res_static)):
+            if static:                             # one step from the calibration maximum
+                sq.sq_act_static_scale(a, gamma_f, d)
+                sq.sq_quant_act_static(x, gamma_f, d, xq, xs)
+            else:
+                sq.sq_quant_act(x, gamma_f, xq, xs)
+            sq.sq_gemm_w8a8(xq, xs, wq, wsc, y, bias=bias)
+            torch.cuda.synchronize()
+            yb = y[torch.from_numpy(rows).to(dev)].view(torch.int16).cpu().numpy().view(np.uint16)
+            out[key] = float(np.linalg.norm(f64(yb) - ref)) / ref_norm
+    res["static_per_tensor"] = res_static
     res["tokens"] = int(sample)
-    res["reference"] = "X W + b in fp64 over evenly spaced tokens; relative Frobenius norm"
+    res["reference"] = ("X W + b in fp64 over evenly spaced tokens; relative Frobenius norm; "
+                        "top level: per-token activation steps")
     return res
+
+
+def static_act_timing(sq, torch, sets, gp, a, xq, xs, dev, iters=20):
+    """Event time of the static-step activation quantizer (no per-token
+    maximum) next to the per-token one, on the rotating input sets."""
+    d = torch.empty(1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sq.sq_act_static_scale(a, gp, d, stream=stream)
+    out = {}
+    for name, fn in (("per_token", lambda x: sq.sq_quant_act(x, gp, xq, xs, stream=stream)),
+                     ("static", lambda x: sq.sq_quant_act_static(x, gp, d, xq, xs,
+                                                                 stream=stream))):
+        for i in range(len(sets)):
+            fn(sets[i][1])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(iters):
+            fn(sets[i % len(sets)][1])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name + "_us"] = e0.elapsed_time(e1) * 1e3 / iters
+    return out
 
 
 def decode_gemm(sq, torch, dev, T=16, K=8192, N=8192, copies=5, iters=50):
@@ -375,6 +409,8 @@ def main():
     if not args.no_extras:
         x_cal, x, w = sets[0]
         out["alpha_sweep"] = alpha_sweep(sq, torch, inp, wl, x_cal, x, w, bias, dev)
+        out["quant_act_static_vs_per_token"] = static_act_timing(sq, torch, sets, gp, a, xq, xs,
+                                                                 dev)
         out["decode_gemm"] = decode_gemm(sq, torch, dev)
     if not args.no_cpu_baseline:
         print("timing the CPU oracle", file=sys.stderr, flush=True)

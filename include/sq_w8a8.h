@@ -182,6 +182,50 @@ sq_status sq_w8a8_linear(const void *x, sq_dtype x_dt, int64_t t, int64_t k, int
                          void *workspace, size_t ws_bytes, const sq_debug_out *dbg,
                          hipStream_t stream);
 
+/*
+ * Static per-tensor activation step -- one scale for every token, from the
+ * calibration tokens' maximum ("SmoothQuant and W8A8", One layer, measured;
+ * "06 -- SmoothQuant" section 7: per-token or per-tensor activation scales).
+ * The per-token calls above stay the default; these three are the static
+ * variant.
+ *
+ * sq_act_static_scale:
+ *   x_scale_static[0] = fp32( max_j fp32(a[j] * |gamma_f[j]|) / 127 )
+ *   a        [k] fp32: per-channel calibration absmax of the activation BEFORE
+ *            the smoothing multiply -- sq_calibrate's a[] in plain mode; in
+ *            norm mode sq_calibrate's a[] taken with gamma = NULL, i.e. the
+ *            absmax of fp32(h * r_t)
+ *   gamma_f  [k] fp32, the folded factor the run-time quantizer multiplies by
+ *            (sq_smooth_fold's gamma_out); NULL = ones
+ *   x_scale_static  1 fp32 (device), out
+ * Rounding is monotone and sign symmetric, so this equals the maximum of
+ * |x^| = |fp32(x * gamma_f)| (norm: |fp32(fp32(h * r_t) * gamma_f)|) over every
+ * calibration token and channel.
+ *
+ * sq_quant_act_static: sq_quant_act with the step fixed at x_scale_static[0]
+ * for every token: code = clamp(round-half-even(fp32(x^ / Delta)), -127, 127)
+ * -- values past the calibrated maximum clip ("SmoothQuant and W8A8",
+ * Gotchas) -- and x_scale[t] = Delta for every t (so sq_gemm_w8a8 applies it
+ * unchanged).  Delta == 0 gives codes 0.  Other arguments as sq_quant_act.
+ *
+ * sq_w8a8_linear_static: sq_w8a8_linear with sq_quant_act_static in place of
+ * sq_quant_act; same workspace and debug outputs.
+ * All three: SQ_ERR_NULL if a required pointer is NULL.
+ */
+sq_status sq_act_static_scale(const float *a, const float *gamma_f, int64_t k,
+                              float *x_scale_static, hipStream_t stream);
+sq_status sq_quant_act_static(const void *x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                              sq_norm norm, const float *gamma_f, float eps,
+                              const float *x_scale_static, int8_t *xq, float *x_scale,
+                              float *row_rscale, hipStream_t stream);
+sq_status sq_w8a8_linear_static(const void *x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                                sq_norm norm, const float *gamma_f, float eps,
+                                const float *x_scale_static,
+                                const int8_t *wq, const float *w_scale, int64_t n,
+                                const float *bias, void *y, sq_dtype y_dt, int64_t ldy,
+                                void *workspace, size_t ws_bytes, const sq_debug_out *dbg,
+                                hipStream_t stream);
+
 /* Static description of a status code (host memory, never NULL). */
 const char *sq_status_string(sq_status status);
 

@@ -129,6 +129,34 @@ def test_act_gemm_linear_validation(L):
                None, 0, None, None) == sq.SQ_OK
 
 
+def test_static_step_validation(L):
+    st = L.sq_act_static_scale
+    assert st(None, None, 64, A16, None) == sq.SQ_ERR_NULL
+    assert st(A16, None, 64, None, None) == sq.SQ_ERR_NULL
+    assert st(A16, None, 0, A16, None) == sq.SQ_ERR_SHAPE
+    assert st(A16, None, 96, A16, None) == sq.SQ_ERR_UNSUPPORTED
+    qs = L.sq_quant_act_static
+    assert qs(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, None, A16, A16, None, None) == sq.SQ_ERR_NULL
+    assert qs(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, A16, None, A16, None, None) == sq.SQ_ERR_NULL
+    assert qs(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, A16, MIS, A16, None, None) == sq.SQ_ERR_UNSUPPORTED
+    assert qs(A16, sq.SQ_BF16, 0, 64, 64, 0, None, 1e-6, A16, A16, A16, None, None) == sq.SQ_OK
+    ls = L.sq_w8a8_linear_static
+    assert ls(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, None, A16, A16, 8, None, A16,
+              sq.SQ_BF16, 8, A16, 1 << 20, None, None) == sq.SQ_ERR_NULL
+    assert ls(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, A16, A16, A16, 8, None, A16,
+              sq.SQ_BF16, 8, None, 0, None, None) == sq.SQ_ERR_WORKSPACE
+
+
+def test_row_limits(L):
+    big = (1 << 24) + 1
+    assert L.sq_quant_act(A16, sq.SQ_BF16, big, 64, 64, 0, None, 1e-6, A16, A16, None,
+                          None) == sq.SQ_ERR_UNSUPPORTED
+    assert L.sq_gemm_w8a8(A16, A16, big, 64, A16, A16, 8, None, A16, sq.SQ_BF16, 8, None,
+                          None) == sq.SQ_ERR_UNSUPPORTED
+    assert L.sq_gemm_w8a8(A16, A16, 8, 64, A16, A16, big, None, A16, sq.SQ_BF16, big + 7, None,
+                          None) == sq.SQ_ERR_UNSUPPORTED
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(sq, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(sq, "_lib", None)

@@ -19,6 +19,13 @@
 // No clamp to [-127, 127] is needed: |x^| <= max|x^| = 127 * Delta * (1 + e)
 // with |e| <= 2^-24, so |x^ / Delta| and its rounded forms stay below 127.5 and
 // round to at most 127 in magnitude.
+//
+// Static per-tensor step ("SmoothQuant and W8A8", One layer, measured: one
+// scale per tensor from the calibration tokens' maximum): Delta is given, the
+// same for every token, and the codes are clamped to [-127, 127] -- values past
+// the calibrated maximum clip (same page, Gotchas).  The tie argument above
+// holds for every quotient below 128 in magnitude; at and above 128 the
+// rounded value clamps to +-127 whichever way it rounds.
 #include "sq_common.h"
 #include "sq_internal.h"
 
@@ -29,6 +36,13 @@ constexpr float kTieBand = 0.5f - 0x1p-15f;
 // codes of 8 values of one token by the reciprocal; `d` > 0, `rc` = fp32(1/d)
 // finite.  `near_tie` is set when some quotient is within 2^-15 of a
 // half-integer: those 8 codes must then be recomputed with quant8_div.
+// CLAMP: clamp the rounded quotient to [-127, 127] (static step only).
+template <bool CLAMP>
+__device__ __forceinline__ float clamp127(float r) {
+  return CLAMP ? fminf(fmaxf(r, -127.0f), 127.0f) : r;
+}
+
+template <bool CLAMP = false>
 __device__ __forceinline__ u32x2 quant8(const float (&xh)[8], float rc, bool& near_tie) {
   u32x2 out;
   out[0] = 0u;
@@ -39,19 +53,21 @@ __device__ __forceinline__ u32x2 quant8(const float (&xh)[8], float rc, bool& ne
     const float y = xh[i] * rc;
     const float r = rintf(y);
     dm = fmaxf(dm, fabsf(y - r));
-    out[i >> 2] |= code_byte(r) << (8 * (i & 3));
+    out[i >> 2] |= code_byte(clamp127<CLAMP>(r)) << (8 * (i & 3));
   }
   near_tie = dm > kTieBand;
   return out;
 }
 
 // exact path for every element (Delta so small that 1/Delta overflows)
+template <bool CLAMP = false>
 __device__ __forceinline__ u32x2 quant8_div(const float (&xh)[8], float d) {
   u32x2 out;
   out[0] = 0u;
   out[1] = 0u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) out[i >> 2] |= code_byte(rintf(xh[i] / d)) << (8 * (i & 3));
+  for (int i = 0; i < 8; ++i)
+    out[i >> 2] |= code_byte(clamp127<CLAMP>(rintf(xh[i] / d))) << (8 * (i & 3));
   return out;
 }
 
@@ -71,11 +87,11 @@ constexpr int kWavesPerBlock = 8;
 template <class In, int NV>
 constexpr int quant_act_min_waves() { return In::kBytes * NV <= 16 ? 8 : 1; }
 
-template <class In, int NV, bool NORM>
+template <class In, int NV, bool NORM, bool STATIC>
 __global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV>())) void k_quant_act(
     const typename In::elem* __restrict__ x, int64_t T, int64_t K, int64_t ld,
-    const float* __restrict__ gamma_f, float eps, int8_t* __restrict__ xq,
-    float* __restrict__ xscale, float* __restrict__ rrow) {
+    const float* __restrict__ gamma_f, float eps, const float* __restrict__ static_scale,
+    int8_t* __restrict__ xq, float* __restrict__ xscale, float* __restrict__ rrow) {
   // gamma_f of chunk c: elements 0-3 at gs[c], 4-7 at gs[NV * 64 + c] (1
   // without gamma, 0 past K)
   __shared__ f32x4 gs[NV * 64 * 2];
@@ -142,23 +158,26 @@ __global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV>()
     }
   };
   float am = 0.0f;
-  static_for<NV>([&](auto jc) {
-    float xh[8];
-    smooth(jc, xh);
+  if (!STATIC) {
+    static_for<NV>([&](auto jc) {
+      float xh[8];
+      smooth(jc, xh);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(xh[i]));
-  });
-  am = wave_max(am);
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(xh[i]));
+    });
+    am = wave_max(am);
+  }
   // Keep only the raw values alive between the passes: the quantize pass
   // widens them again and re-reads gamma from LDS (the compiler would otherwise
   // keep every chunk's x^ in VGPRs and quarter the occupancy).
   asm volatile("" ::: "memory");
 #pragma unroll
   for (int j = 0; j < NV; ++j) In::opaque(raw[j]);
-  const float d = am / 127.0f;
+  const float d = STATIC ? static_scale[0] : am / 127.0f;
   const float rc = 1.0f / d;
-  // d == 0: every x^ is 0 and rc = 0 gives code 0.  1/d overflowing (d tiny):
-  // every chunk takes the IEEE division below.
+  // d == 0: every x^ is 0 (or, for a static step, every code is 0) and rc = 0
+  // gives code 0.  1/d overflowing (d tiny): every chunk takes the IEEE
+  // division below.
   const bool fast = rc <= 3.0e38f;
   const float rcu = fast ? rc : 0.0f;
   if (lane == 0) xscale[r] = d;
@@ -171,9 +190,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV>()
     float xh[8];
     smooth(jc, xh);
     bool tie;
-    u32x2 c = quant8(xh, rcu, tie);
+    u32x2 c = quant8<STATIC>(xh, rcu, tie);
     // rare: a quotient near a rounding tie; redo the chunk by IEEE division
-    if (tie || all_div) c = quant8_div(xh, d);
+    if (tie || all_div) c = quant8_div<STATIC>(xh, d);
     if (ch < nchunk) *reinterpret_cast<u32x2*>(qrow + ch * 8) = c;
   });
 }
@@ -182,11 +201,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV>()
 // K > 8192: one workgroup per token, three passes over the row (sum of
 // squares, max, quantize); the re-reads hit L2.
 // ---------------------------------------------------------------------------
-template <class In, bool NORM>
+template <class In, bool NORM, bool STATIC>
 __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem* __restrict__ x,
                                                         int64_t T, int64_t K, int64_t ld,
                                                         const float* __restrict__ gamma_f,
-                                                        float eps, int8_t* __restrict__ xq,
+                                                        float eps,
+                                                        const float* __restrict__ static_scale,
+                                                        int8_t* __restrict__ xq,
                                                         float* __restrict__ xscale,
                                                         float* __restrict__ rrow) {
   __shared__ double red_d[4];
@@ -216,20 +237,22 @@ __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem*
     if (rrow != nullptr && threadIdx.x == 0) rrow[r] = rt;
   }
   float am = 0.0f;
-  for (int64_t ch = threadIdx.x; ch < nchunk; ch += 256) {
-    float v[8];
-    In::load8(row + ch * 8, v);
+  if (!STATIC) {
+    for (int64_t ch = threadIdx.x; ch < nchunk; ch += 256) {
+      float v[8];
+      In::load8(row + ch * 8, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float t = NORM ? v[i] * rt : v[i];
-      am = fmaxf(am, fabsf(t * (gamma_f ? gamma_f[ch * 8 + i] : 1.0f)));
+      for (int i = 0; i < 8; ++i) {
+        const float t = NORM ? v[i] * rt : v[i];
+        am = fmaxf(am, fabsf(t * (gamma_f ? gamma_f[ch * 8 + i] : 1.0f)));
+      }
     }
+    am = wave_max(am);
+    if (lane == 0) red_f[wave] = am;
+    __syncthreads();
+    am = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
   }
-  am = wave_max(am);
-  if (lane == 0) red_f[wave] = am;
-  __syncthreads();
-  am = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
-  const float d = am / 127.0f;
+  const float d = STATIC ? static_scale[0] : am / 127.0f;
   if (threadIdx.x == 0) xscale[r] = d;
   const float rc = 1.0f / d;
   const bool fast = d > 0.0f && rc <= 3.0e38f;
@@ -245,8 +268,8 @@ __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem*
     c[0] = 0u;
     c[1] = 0u;
     bool tie = true;
-    if (fast) c = quant8(xh, rc, tie);
-    if (d > 0.0f && tie) c = quant8_div(xh, d);
+    if (fast) c = quant8<STATIC>(xh, rc, tie);
+    if (d > 0.0f && tie) c = quant8_div<STATIC>(xh, d);
     *reinterpret_cast<u32x2*>(xq + r * K + ch * 8) = c;
   }
 }
@@ -255,39 +278,77 @@ __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem*
 // host launcher
 // ---------------------------------------------------------------------------
 
-template <class In, int NV, bool NORM>
+template <class In, int NV, bool NORM, bool STATIC>
 static void quant_act_nv(const void* x, int64_t T, int64_t K, int64_t ld, const float* gamma_f,
-                         float eps, int8_t* xq, float* xscale, float* rrow, hipStream_t st) {
+                         float eps, const float* sscale, int8_t* xq, float* xscale, float* rrow,
+                         hipStream_t st) {
   const int64_t blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL((k_quant_act<In, NV, NORM>), dim3((unsigned)blocks), dim3(64 * kWavesPerBlock),
-                     0, st, (const typename In::elem*)x, T, K, ld, gamma_f, eps, xq, xscale, rrow);
+  hipLaunchKernelGGL((k_quant_act<In, NV, NORM, STATIC>), dim3((unsigned)blocks),
+                     dim3(64 * kWavesPerBlock), 0, st, (const typename In::elem*)x, T, K, ld,
+                     gamma_f, eps, sscale, xq, xscale, rrow);
+}
+
+template <class In, bool NORM, bool STATIC>
+static void quant_act_t(const void* x, int64_t T, int64_t K, int64_t ld, const float* gamma_f,
+                        float eps, const float* sscale, int8_t* xq, float* xscale, float* rrow,
+                        hipStream_t st) {
+  const int64_t nchunk = K / 8;
+#define SQ_QA(NV) \
+  quant_act_nv<In, NV, NORM, STATIC>(x, T, K, ld, gamma_f, eps, sscale, xq, xscale, rrow, st)
+  if (nchunk <= 64) SQ_QA(1);
+  else if (nchunk <= 128) SQ_QA(2);
+  else if (nchunk <= 256) SQ_QA(4);
+  else if (nchunk <= 512) SQ_QA(8);
+  else if (nchunk <= 1024) SQ_QA(16);
+  else
+    hipLaunchKernelGGL((k_quant_act_wide<In, NORM, STATIC>), dim3((unsigned)T), dim3(256), 0, st,
+                       (const typename In::elem*)x, T, K, ld, gamma_f, eps, sscale, xq, xscale,
+                       rrow);
+#undef SQ_QA
 }
 
 template <class In, bool NORM>
-static void quant_act_t(const void* x, int64_t T, int64_t K, int64_t ld, const float* gamma_f,
-                        float eps, int8_t* xq, float* xscale, float* rrow, hipStream_t st) {
-  const int64_t nchunk = K / 8;
-  if (nchunk <= 64) quant_act_nv<In, 1, NORM>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
-  else if (nchunk <= 128) quant_act_nv<In, 2, NORM>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
-  else if (nchunk <= 256) quant_act_nv<In, 4, NORM>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
-  else if (nchunk <= 512) quant_act_nv<In, 8, NORM>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
-  else if (nchunk <= 1024) quant_act_nv<In, 16, NORM>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
-  else
-    hipLaunchKernelGGL((k_quant_act_wide<In, NORM>), dim3((unsigned)T), dim3(256), 0, st,
-                       (const typename In::elem*)x, T, K, ld, gamma_f, eps, xq, xscale, rrow);
+static void quant_act_s(const void* x, int64_t T, int64_t K, int64_t ld, const float* gamma_f,
+                        float eps, const float* sscale, int8_t* xq, float* xscale, float* rrow,
+                        hipStream_t st) {
+  if (sscale) quant_act_t<In, NORM, true>(x, T, K, ld, gamma_f, eps, sscale, xq, xscale, rrow, st);
+  else quant_act_t<In, NORM, false>(x, T, K, ld, gamma_f, eps, sscale, xq, xscale, rrow, st);
 }
 
 void launch_quant_act(const void* x, bool bf16, int64_t T, int64_t K, int64_t ld, bool norm,
-                      const float* gamma_f, float eps, int8_t* xq, float* xscale, float* rrow,
-                      hipStream_t st) {
+                      const float* gamma_f, float eps, const float* static_scale, int8_t* xq,
+                      float* xscale, float* rrow, hipStream_t st) {
   if (T <= 0) return;
   if (bf16) {
-    if (norm) quant_act_t<Bf16In, true>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
-    else quant_act_t<Bf16In, false>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
+    if (norm) quant_act_s<Bf16In, true>(x, T, K, ld, gamma_f, eps, static_scale, xq, xscale, rrow, st);
+    else quant_act_s<Bf16In, false>(x, T, K, ld, gamma_f, eps, static_scale, xq, xscale, rrow, st);
   } else {
-    if (norm) quant_act_t<F32In, true>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
-    else quant_act_t<F32In, false>(x, T, K, ld, gamma_f, eps, xq, xscale, rrow, st);
+    if (norm) quant_act_s<F32In, true>(x, T, K, ld, gamma_f, eps, static_scale, xq, xscale, rrow, st);
+    else quant_act_s<F32In, false>(x, T, K, ld, gamma_f, eps, static_scale, xq, xscale, rrow, st);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Static step from channel maxima: out[0] = fp32( max_j fp32(a[j] * |g[j]|) /
+// 127 ), g NULL = 1.  Rounding is monotone and sign symmetric, so with a[j] the
+// channel maximum of |x| (of |fp32(h * r_t)| in norm mode) this is the maximum
+// of |x^| over every calibration token and channel.  One workgroup.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_static_scale(const float* __restrict__ a,
+                                                      const float* __restrict__ g, int64_t K,
+                                                      float* __restrict__ out) {
+  __shared__ float red[4];
+  float m = 0.0f;
+  for (int64_t j = threadIdx.x; j < K; j += 256) m = fmaxf(m, a[j] * (g ? fabsf(g[j]) : 1.0f));
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) out[0] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) / 127.0f;
+}
+
+void launch_static_scale(const float* a, const float* gamma_f, int64_t K, float* out,
+                         hipStream_t st) {
+  hipLaunchKernelGGL(k_static_scale, dim3(1), dim3(256), 0, st, a, gamma_f, K, out);
 }
 
 }  // namespace sqk

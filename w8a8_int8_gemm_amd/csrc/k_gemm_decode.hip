@@ -58,7 +58,7 @@ __global__ __launch_bounds__(512) void k_gemm_decode(const int8_t* __restrict__ 
       const int64_t off = (int64_t)(s + u) * 64;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
-        a[u][b] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrow[b] + off));
+        a[u][b] = *reinterpret_cast<const v4i*>(wrow[b] + off);
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) x[u][tb] = *reinterpret_cast<const v4i*>(xrow[tb] + off);
     }
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(512) void k_gemm_decode(const int8_t* __restrict__ 
     const int64_t off = (int64_t)s * 64;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const v4i a = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrow[b] + off));
+      const v4i a = *reinterpret_cast<const v4i*>(wrow[b] + off);
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const v4i x = *reinterpret_cast<const v4i*>(xrow[tb] + off);

@@ -25,9 +25,12 @@ void launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, int64
                            const float* s, const float* wscale, int8_t* wq, hipStream_t st);
 
 // k_actquant.hip
+// static_scale NULL: per-token step; else the device scalar per-tensor step
 void launch_quant_act(const void* x, bool bf16, int64_t T, int64_t K, int64_t ld, bool norm,
-                      const float* gamma_f, float eps, int8_t* xq, float* xscale, float* rrow,
-                      hipStream_t st);
+                      const float* gamma_f, float eps, const float* static_scale, int8_t* xq,
+                      float* xscale, float* rrow, hipStream_t st);
+void launch_static_scale(const float* a, const float* gamma_f, int64_t K, float* out,
+                         hipStream_t st);
 
 // k_gemm.hip / k_gemm_decode.hip; out: 0 = bf16, 1 = fp32, 2 = int32 accumulators
 void launch_gemm(const int8_t* xq, const float* xs, int64_t T, int64_t K, const int8_t* wq,

@@ -169,8 +169,30 @@ sq_status sq_quant_act(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64
   if (xq == nullptr || x_scale == nullptr) return SQ_ERR_NULL;
   if (!aligned16(xq)) return SQ_ERR_UNSUPPORTED;
   if (t == 0) return SQ_OK;
-  sqk::launch_quant_act(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps, xq,
-                        x_scale, norm == SQ_NORM_RMS ? row_rscale : nullptr, stream);
+  sqk::launch_quant_act(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps, nullptr,
+                        xq, x_scale, norm == SQ_NORM_RMS ? row_rscale : nullptr, stream);
+  return hip_status();
+}
+
+sq_status sq_act_static_scale(const float* a, const float* gamma_f, int64_t k,
+                              float* x_scale_static, hipStream_t stream) {
+  SQ_TRY(check_k(k));
+  if (a == nullptr || x_scale_static == nullptr) return SQ_ERR_NULL;
+  sqk::launch_static_scale(a, gamma_f, k, x_scale_static, stream);
+  return hip_status();
+}
+
+sq_status sq_quant_act_static(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                              sq_norm norm, const float* gamma_f, float eps,
+                              const float* x_scale_static, int8_t* xq, float* x_scale,
+                              float* row_rscale, hipStream_t stream) {
+  SQ_TRY(check_act(x, x_dt, t, k, ldx, norm, eps));
+  if (x_scale_static == nullptr || xq == nullptr || x_scale == nullptr) return SQ_ERR_NULL;
+  if (!aligned16(xq)) return SQ_ERR_UNSUPPORTED;
+  if (t == 0) return SQ_OK;
+  sqk::launch_quant_act(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps,
+                        x_scale_static, xq, x_scale, norm == SQ_NORM_RMS ? row_rscale : nullptr,
+                        stream);
   return hip_status();
 }
 
@@ -191,11 +213,16 @@ size_t sq_linear_workspace_bytes(int64_t t, int64_t k) {
   return (size_t)(round256(t * k) + round256(t * 4));
 }
 
-sq_status sq_w8a8_linear(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
-                         sq_norm norm, const float* gamma_f, float eps, const int8_t* wq,
-                         const float* w_scale, int64_t n, const float* bias, void* y,
-                         sq_dtype y_dt, int64_t ldy, void* workspace, size_t ws_bytes,
-                         const sq_debug_out* dbg, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// the forward of sq_w8a8_linear (static_scale NULL) and sq_w8a8_linear_static
+sq_status linear_impl(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                      sq_norm norm, const float* gamma_f, float eps, const float* static_scale,
+                      const int8_t* wq, const float* w_scale, int64_t n, const float* bias,
+                      void* y, sq_dtype y_dt, int64_t ldy, void* workspace, size_t ws_bytes,
+                      const sq_debug_out* dbg, hipStream_t stream) {
   SQ_TRY(check_act(x, x_dt, t, k, ldx, norm, eps));
   if (t == 0) return wq == nullptr ? SQ_ERR_NULL : SQ_OK;   // nothing to compute
   int8_t* xq = dbg ? dbg->xq : nullptr;
@@ -213,14 +240,38 @@ sq_status sq_w8a8_linear(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int
   // the GEMM's own checks, with the codes and scales that will exist by then
   if (w_scale == nullptr && acc == nullptr) return SQ_ERR_NULL;
   SQ_TRY(check_gemm(xq, xs, t, k, wq, w_scale, n, y, y_dt, ldy, acc));
-  sqk::launch_quant_act(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps, xq, xs,
-                        norm == SQ_NORM_RMS ? rrow : nullptr, stream);
+  sqk::launch_quant_act(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps,
+                        static_scale, xq, xs, norm == SQ_NORM_RMS ? rrow : nullptr, stream);
   SQ_TRY(hip_status());
   if (n == 0) return SQ_OK;
   void* out = acc != nullptr ? (void*)acc : y;
   sqk::launch_gemm(xq, xs, t, k, wq, w_scale, n, bias, out, acc ? n : ldy, gemm_out(y_dt, acc),
                    stream);
   return hip_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+sq_status sq_w8a8_linear(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                         sq_norm norm, const float* gamma_f, float eps, const int8_t* wq,
+                         const float* w_scale, int64_t n, const float* bias, void* y,
+                         sq_dtype y_dt, int64_t ldy, void* workspace, size_t ws_bytes,
+                         const sq_debug_out* dbg, hipStream_t stream) {
+  return linear_impl(x, x_dt, t, k, ldx, norm, gamma_f, eps, nullptr, wq, w_scale, n, bias, y,
+                     y_dt, ldy, workspace, ws_bytes, dbg, stream);
+}
+
+sq_status sq_w8a8_linear_static(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                                sq_norm norm, const float* gamma_f, float eps,
+                                const float* x_scale_static, const int8_t* wq,
+                                const float* w_scale, int64_t n, const float* bias, void* y,
+                                sq_dtype y_dt, int64_t ldy, void* workspace, size_t ws_bytes,
+                                const sq_debug_out* dbg, hipStream_t stream) {
+  if (x_scale_static == nullptr) return SQ_ERR_NULL;
+  return linear_impl(x, x_dt, t, k, ldx, norm, gamma_f, eps, x_scale_static, wq, w_scale, n, bias,
+                     y, y_dt, ldy, workspace, ws_bytes, dbg, stream);
 }
 
 }  // extern "C"
