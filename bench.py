@@ -66,6 +66,10 @@ def _parse():
                          "steps, so that no step finds its inputs in the 256 MB Infinity Cache")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the untimed extras: the error per alpha and the decode GEMM")
+    ap.add_argument("--gemm-loop", type=float, default=0.0, metavar="SECONDS",
+                    help="instead of benchmarking, run only the headline GEMM back to back for "
+                         "this long (for sampling power and clocks from outside) and print the "
+                         "time per launch")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run one plain elementwise copy kernel over "
                          "this many MiB (reads and writes that many bytes): the reference "
@@ -219,6 +223,36 @@ def static_act_timing(sq, torch, sets, gp, a, xq, xs, dev, iters=20):
     return out
 
 
+def gemm_loop(sq, torch, inp, wl, d, dev, seconds):
+    """The headline GEMM alone, back to back for `seconds`, on the workload's own
+    quantized operands (calibrate, fold, quantize once, untimed)."""
+    T, K, N = wl.T, wl.K, wl.N
+    x_cal, x, w, bias = d(inp.x_cal), d(inp.x), d(inp.w), d(inp.bias)
+    e = lambda n: torch.empty(n, dtype=torch.float32, device=dev)  # noqa: E731
+    a, wm, s, gp, wsc, xs = e(K), e(K), e(K), e(K), e(N), e(T)
+    wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    xq = torch.empty((T, K), dtype=torch.int8, device=dev)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    sq.sq_calibrate(x_cal, w, wl.alpha, a, wm, s)
+    sq.sq_smooth_fold(s, None, gp)
+    sq.sq_quant_weight(w, s, wq, wsc)
+    sq.sq_quant_act(x, gp, xq, xs)
+    torch.cuda.synchronize()
+    n = 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_end = time.time() + seconds
+    e0.record()
+    while time.time() < t_end:
+        for _ in range(50):
+            sq.sq_gemm_w8a8(xq, xs, wq, wsc, y, bias=bias)
+        torch.cuda.synchronize()
+        n += 50
+    e1.record()
+    torch.cuda.synchronize()
+    print(json.dumps({"gemm_loop_launches": n, "us_per_launch": e0.elapsed_time(e1) * 1e3 / n}),
+          flush=True)
+
+
 def decode_gemm(sq, torch, dev, T=16, K=8192, N=8192, copies=5, iters=50):
     """Decode-shaped INT8 GEMM (16 tokens, K = N = 8192): HBM-bound on the
     64 MiB weight.  Five weight copies (320 MiB) are used in turn so that the
@@ -312,6 +346,9 @@ def main():
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
+    if args.gemm_loop > 0:
+        gemm_loop(sq, torch, inp, wl, d, dev, args.gemm_loop)
+        return
     nsets = max(1, args.sets)
     sets = [(d(inp.x_cal), d(inp.x), d(inp.w)) for _ in range(nsets)]
     bias = d(inp.bias)
