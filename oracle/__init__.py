@@ -61,6 +61,11 @@ def _load():
         _lib.oracle_static_scale.argtypes = [P, I, I64, I64, I64, I, F, P]
         _lib.oracle_static_scale.restype = F
         _lib.oracle_quant_act_static.argtypes = [P, I, I64, I64, I64, I, P, F, P, F, P, P, P]
+        _lib.oracle_e4m3_encode_array.argtypes = [P, I64, P]
+        _lib.oracle_e4m3_decode_array.argtypes = [P, I64, P]
+        _lib.oracle_quant_weight_fp8.argtypes = [P, I64, I64, I64, P, P]
+        _lib.oracle_quant_act_fp8.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, P, P]
+        _lib.oracle_gemm_fp8.argtypes = [P, P, I64, I64, I64, P]
         _lib.oracle_int_gemm.argtypes = [P, P, I64, I64, I64, P]
         _lib.oracle_int_gemm.restype = I64
         _lib.oracle_epilogue.argtypes = [P, P, P, P, I64, I64, P]
@@ -191,6 +196,87 @@ def quant_act_static(x: np.ndarray, delta, gamma_f=None, *, norm: bool = False,
                                     _p(_f32(gamma_f)), float(np.float32(delta)), _p(q), _p(xs),
                                     _p(rout))
     return q, xs, rout
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 variant
+# ---------------------------------------------------------------------------
+
+def e4m3_encode(v) -> np.ndarray:
+    """Nearest E4M3 codes (uint8) of fp32 values, ties to even."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, np.uint8)
+    _load().oracle_e4m3_encode_array(_p(v), v.size, _p(out))
+    return out
+
+
+def e4m3_decode(c) -> np.ndarray:
+    c = np.ascontiguousarray(c, dtype=np.uint8)
+    out = np.empty(c.shape, np.float32)
+    _load().oracle_e4m3_decode_array(_p(c), c.size, _p(out))
+    return out
+
+
+def quant_weight_fp8(w_hat: np.ndarray):
+    """(qw [N,K] E4M3 codes, w_scale [N]) with w_scale = amax / 448."""
+    w_hat = np.ascontiguousarray(w_hat, dtype=np.float32)
+    K, N = w_hat.shape
+    qw = np.empty((N, K), np.uint8)
+    ws = np.empty(N, np.float32)
+    _load().oracle_quant_weight_fp8(_p(w_hat), K, N, N, _p(qw), _p(ws))
+    return qw, ws
+
+
+def quant_act_fp8(x: np.ndarray, gamma_f=None, *, norm: bool = False,
+                  r: Optional[np.ndarray] = None, eps: float = 1e-6):
+    """(q [T,K] E4M3 codes, x_scale [T] = amax_t / 448, r [T] or None)."""
+    x, bf = _mat(x)
+    T, K = x.shape
+    q = np.empty((T, K), np.uint8)
+    xs = np.empty(T, np.float32)
+    rout = np.empty(T, np.float32) if norm else None
+    _load().oracle_quant_act_fp8(_p(x), bf, T, K, K, int(norm), _p(_f32(r)), float(eps),
+                                 _p(_f32(gamma_f)), _p(q), _p(xs), _p(rout))
+    return q, xs, rout
+
+
+def gemm_fp8(q: np.ndarray, qw: np.ndarray) -> np.ndarray:
+    """Exact sums of E4M3 products, fp64 [T,N]."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    qw = np.ascontiguousarray(qw, dtype=np.uint8)
+    T, K = q.shape
+    N = qw.shape[0]
+    assert qw.shape[1] == K
+    acc = np.empty((T, N), np.float64)
+    _load().oracle_gemm_fp8(_p(q), _p(qw), T, K, N, _p(acc))
+    return acc
+
+
+def prepare_weight_fp8(w, s, gamma=None):
+    """(gamma', qw [N,K] E4M3, w_scale [N]) -- fold then per-output-channel E4M3."""
+    gp, what = fold(s, gamma, w)
+    qw, ws = quant_weight_fp8(what)
+    return gp, qw, ws
+
+
+def linear_fp8(x, gamma_f, qw, w_scale, bias=None, *, norm=False, r=None, eps=1e-6,
+               out_bf16=True):
+    """E4M3 forward: quantize activations per token, exact product sums (fp64,
+    rounded once to fp32 for the epilogue), epilogue as for INT8."""
+    q, xs, rr = quant_act_fp8(x, gamma_f, norm=norm, r=r, eps=eps)
+    acc = gemm_fp8(q, qw)
+    y = epilogue_f32acc(acc.astype(np.float32), xs, w_scale, bias)
+    return dict(q=q, x_scale=xs, r=rr, acc=acc, y32=y, y=to_bf16(y) if out_bf16 else y)
+
+
+def epilogue_f32acc(acc: np.ndarray, x_scale, w_scale, bias=None) -> np.ndarray:
+    """y = fp32(fp32(x_scale[t] * w_scale[n]) * acc[t,n]) + bias[n] for fp32 acc."""
+    acc = np.asarray(acc, np.float32)
+    sc = (np.asarray(x_scale, np.float32)[:, None] * np.asarray(w_scale, np.float32)[None, :])
+    y = (sc.astype(np.float32) * acc).astype(np.float32)
+    if bias is not None:
+        y = (y + np.asarray(bias, np.float32)[None, :]).astype(np.float32)
+    return y
 
 
 def int_gemm(q: np.ndarray, qw: np.ndarray) -> np.ndarray:

@@ -35,6 +35,12 @@
  *   quant_act_static  the same quantizer with that fixed step: values past the
  *                  calibrated maximum clip to +-127 ("SmoothQuant and W8A8",
  *                  Gotchas: a static scale clips what calibration never saw).
+ *   e4m3_*, *_fp8  the FP8 E4M3 variant of the same path ("SmoothQuant and
+ *                  W8A8", One layer, measured: weights per output channel,
+ *                  activations per token, in FP8 E4M3): step = amax / 448
+ *                  (448 is E4M3's largest finite value), code = the E4M3
+ *                  value nearest fp32(x / step), ties to even; products summed
+ *                  exactly (fp64) in place of the int64 sum.
  *   int_gemm       acc = sum_k q[t,k] * qw[n,k] in int64 ("06 -- SmoothQuant",
  *                  section 7: INT8 x INT8 -> INT32).
  *   epilogue       y = (Delta_t * Delta_n) * acc + bias ("06 -- SmoothQuant",
@@ -269,6 +275,116 @@ void oracle_quant_act_static(const void *x, int is_bf16, int64_t T, int64_t K, i
     }
   }
   free(r);
+}
+
+/* ---------------------------------------------------------------------------
+ * FP8 E4M3 (the OCP "fn" encoding): sign bit, 4 exponent bits with bias 7,
+ * 3 mantissa bits; no infinities; 0x7F / 0xFF are NaN, so the largest finite
+ * magnitude is 1.75 * 2^8 = 448.  Exponent field 0 holds the subnormals
+ * m * 2^-9, m = 0..7.
+ * ------------------------------------------------------------------------- */
+
+/* value of an E4M3 code (NaN codes decode to NaN) */
+float oracle_e4m3_decode(uint8_t c) {
+  const int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  float v = (e == 0) ? ldexpf((float)m, -9) : ldexpf(1.0f + (float)m / 8.0f, e - 7);
+  return sign ? -v : v;
+}
+
+/* nearest E4M3 value to a finite v, ties to even (even mantissa field);
+   magnitudes past 448 saturate to 448 (the quantizers never produce them:
+   their quotients are at most 448 up to one fp32 rounding) */
+uint8_t oracle_e4m3_encode(float v) {
+  const uint8_t sign = (v < 0.0f || (v == 0.0f && signbit(v))) ? 0x80 : 0x00;
+  const double a = fabs((double)v);
+  if (a == 0.0) return sign;
+  if (a >= 448.0) return sign | 0x7E;
+  int e;
+  frexp(a, &e);            /* a = f * 2^e, f in [0.5, 1): a in [2^(e-1), 2^e) */
+  int ex = e - 1;          /* a in [2^ex, 2^(ex+1)) */
+  if (ex < -6) {           /* subnormal range: multiples of 2^-9 */
+    const double q = nearbyint(a * 512.0);      /* exact scaling, ties to even */
+    return sign | (uint8_t)q;                   /* q = 8 is the smallest normal, 0x08 */
+  }
+  const double f = nearbyint((a / ldexp(1.0, ex) - 1.0) * 8.0);   /* 0..8 */
+  int m = (int)f;
+  if (m == 8) { m = 0; ex += 1; }
+  if (ex > 8 || (ex == 8 && m == 7)) return sign | 0x7E;
+  return sign | (uint8_t)(((ex + 7) << 3) | m);
+}
+
+void oracle_e4m3_encode_array(const float *v, int64_t n, uint8_t *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(v[i]);
+}
+
+void oracle_e4m3_decode_array(const uint8_t *c, int64_t n, float *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_decode(c[i]);
+}
+
+/* Per-output-channel E4M3 of W^ [K,N]: w_scale[n] = max_j |W^[j,n]| / 448,
+   code = e4m3(fp32(W^[j,n] / w_scale[n])), stored transposed [N,K]. */
+void oracle_quant_weight_fp8(const float *w_hat, int64_t K, int64_t N, int64_t ld, uint8_t *qw,
+                             float *w_scale) {
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    float amax = 0.0f;
+    for (int64_t j = 0; j < K; ++j) amax = fmaxf(amax, fabsf(w_hat[j * ld + n]));
+    float d = amax / 448.0f;
+    w_scale[n] = d;
+    for (int64_t j = 0; j < K; ++j)
+      qw[n * K + j] = (d == 0.0f) ? (uint8_t)0 : oracle_e4m3_encode(w_hat[j * ld + n] / d);
+  }
+}
+
+/* Per-token E4M3 of the smoothed activation, x^ formed as in
+   oracle_quant_act: x_scale[t] = max_k |x^| / 448, code = e4m3(fp32(x^ / x_scale[t])). */
+void oracle_quant_act_fp8(const void *x, int is_bf16, int64_t T, int64_t K, int64_t ld, int norm,
+                          const float *r_in, float eps, const float *gamma_f, uint8_t *q,
+                          float *x_scale, float *r_out) {
+  float *r = NULL;
+  if (norm) {
+    r = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1));
+    if (r_in)
+      memcpy(r, r_in, sizeof(float) * (size_t)T);
+    else
+      oracle_rms_rscale(x, is_bf16, T, K, ld, eps, r);
+    if (r_out) memcpy(r_out, r, sizeof(float) * (size_t)T);
+  }
+#pragma omp parallel
+  {
+    float *xh = (float *)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      float amax = 0.0f;
+      for (int64_t k = 0; k < K; ++k) {
+        xh[k] = smoothed(x, is_bf16, t * ld + k, norm, norm ? r[t] : 1.0f, gamma_f, k);
+        amax = fmaxf(amax, fabsf(xh[k]));
+      }
+      float d = amax / 448.0f;
+      x_scale[t] = d;
+      for (int64_t k = 0; k < K; ++k)
+        q[t * K + k] = (d == 0.0f) ? (uint8_t)0 : oracle_e4m3_encode(xh[k] / d);
+    }
+    free(xh);
+  }
+  free(r);
+}
+
+/* acc[t,n] = sum_k e4m3(q[t,k]) * e4m3(qw[n,k]), summed in fp64 (every product
+   and every partial sum of 4-bit-significand values is exact there for
+   K <= 65536), returned in fp64 [T,N]. */
+void oracle_gemm_fp8(const uint8_t *q, const uint8_t *qw, int64_t T, int64_t K, int64_t N,
+                     double *acc) {
+  double lut[256];
+  for (int c = 0; c < 256; ++c) lut[c] = (double)oracle_e4m3_decode((uint8_t)c);
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t n = 0; n < N; ++n) {
+      double s = 0.0;
+      for (int64_t k = 0; k < K; ++k) s += lut[q[t * K + k]] * lut[qw[n * K + k]];
+      acc[t * N + n] = s;
+    }
 }
 
 /* acc[t,n] = sum_k q[t,k] * qw[n,k] in int64; q is [T,K], qw is [N,K].

@@ -503,3 +503,88 @@ def test_static_zero_step_gives_zero_codes():
     assert d == 0.0
     q, xs, _ = oracle.quant_act_static(np.ones((2, 64), np.float32), d)
     assert not q.any() and not xs.any()
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 variant ("SmoothQuant and W8A8", One layer, measured: weights per
+# output channel and activations per token in FP8 E4M3)
+# ---------------------------------------------------------------------------
+
+def _e4m3_table():
+    """Every finite E4M3 value from the format's definition: bias 7, 3 mantissa
+    bits, exponent field 0 subnormal, 0x7F/0xFF NaN."""
+    vals = {}
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            continue
+        v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        vals[c] = -v if s else v
+    return vals
+
+
+def test_e4m3_decode_definition_and_round_trip():
+    tab = _e4m3_table()
+    codes = np.array(sorted(tab), np.uint8)
+    dec = oracle.e4m3_decode(codes)
+    np.testing.assert_array_equal(dec, np.array([tab[c] for c in codes], np.float32))
+    assert np.isnan(oracle.e4m3_decode(np.array([0x7F, 0xFF], np.uint8))).all()
+    assert tab[0x38] == 1.0 and tab[0x7E] == 448.0 and tab[0x01] == 2.0 ** -9 and tab[0x08] == 2.0 ** -6
+    # encoding a finite value reproduces its code (+0 and -0 keep their sign)
+    np.testing.assert_array_equal(oracle.e4m3_encode(dec), codes)
+
+
+def test_e4m3_encode_is_nearest_ties_to_even():
+    tab = _e4m3_table()
+    pos = sorted((v, c) for c, v in tab.items() if c < 0x80)
+    rng = np.random.default_rng(31)
+    v = np.concatenate([rng.uniform(0, 448, 3000), np.exp(rng.uniform(np.log(1e-4), np.log(448), 3000)),
+                        # exact midpoints between neighbours: ties
+                        [(a[0] + b[0]) / 2 for a, b in zip(pos, pos[1:])]]).astype(np.float32)
+    v = np.concatenate([v, -v])
+    got = oracle.e4m3_encode(v)
+    for x, c in zip(v, got):
+        a = abs(float(x))
+        best = min(pos, key=lambda p: (abs(p[0] - a), p[1] & 1))   # nearest, then even mantissa
+        assert (int(c) & 0x7F) == best[1], (x, hex(c), best)
+        assert (int(c) >> 7) == (1 if x < 0 else 0)
+
+
+def test_e4m3_relative_precision_over_the_pages_range():
+    # with a token maximum of 17.5 the step is 17.5/448: every value from 0.68
+    # to 17.5 keeps a relative error of at most half an E4M3 mantissa step
+    # (1/16); INT8 at the same maximum rounds 0.68 to 5 steps of 0.138
+    x = np.linspace(0.68, 17.5, 2001).astype(np.float32)
+    row = np.concatenate([[17.5], x]).astype(np.float32)[None, :]
+    q, xs, _ = oracle.quant_act_fp8(row, np.ones(row.shape[1], np.float32))
+    assert xs[0] == F32(17.5) / F32(448.0)
+    back = oracle.e4m3_decode(q[0, 1:]).astype(np.float64) * float(xs[0])
+    rel = np.abs(back - x) / x
+    assert rel.max() <= 1 / 16 + 1e-6
+    qi, xi, _ = oracle.quant_act(row, np.ones(row.shape[1], np.float32))
+    assert qi[0, 1] == 5 and abs(float(qi[0, 1]) * float(xi[0]) - 0.68) / 0.68 > 0.01
+
+
+def test_fp8_quantizers_map_the_maximum_to_448():
+    rng = np.random.default_rng(32)
+    x = (rng.standard_normal((20, 256)) * rng.uniform(0.1, 30, (20, 1))).astype(np.float32)
+    q, xs, _ = oracle.quant_act_fp8(x)
+    np.testing.assert_array_equal(xs, (np.abs(x).max(axis=1) / F32(448.0)).astype(np.float32))
+    assert (np.abs(oracle.e4m3_decode(q)).max(axis=1) == 448.0).all()
+    w = (rng.standard_normal((300, 24)) * rng.uniform(0.01, 2, (1, 24))).astype(np.float32)
+    qw, ws = oracle.quant_weight_fp8(w)
+    np.testing.assert_array_equal(ws, (np.abs(w).max(axis=0) / F32(448.0)).astype(np.float32))
+    np.testing.assert_array_equal(qw, oracle.e4m3_encode((w / ws[None, :]).astype(np.float32)).T)
+    # codes are the nearest E4M3 of the fp32 quotient, as in the INT8 quantizer
+    np.testing.assert_array_equal(q, oracle.e4m3_encode((x / xs[:, None]).astype(np.float32)))
+
+
+def test_gemm_fp8_matches_numpy_fp64():
+    rng = np.random.default_rng(33)
+    q = rng.integers(0, 256, (12, 320)).astype(np.uint8)
+    qw = rng.integers(0, 256, (9, 320)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x10          # no NaN codes
+    qw[(qw & 0x7F) == 0x7F] = 0x20
+    acc = oracle.gemm_fp8(q, qw)
+    ref = oracle.e4m3_decode(q).astype(np.float64) @ oracle.e4m3_decode(qw).astype(np.float64).T
+    np.testing.assert_array_equal(acc, ref)
