@@ -147,6 +147,23 @@ def test_static_step_validation(L):
               sq.SQ_BF16, 8, None, 0, None, None) == sq.SQ_ERR_WORKSPACE
 
 
+def test_fp8_validation(L):
+    qw = L.sq_quant_weight_fp8
+    assert qw(None, sq.SQ_BF16, 64, 64, 64, None, A16, A16, None) == sq.SQ_ERR_NULL
+    assert qw(A16, sq.SQ_BF16, 64, 12, 16, None, A16, A16, None) == sq.SQ_ERR_UNSUPPORTED
+    qa = L.sq_quant_act_fp8
+    assert qa(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, None, A16, None, None) == sq.SQ_ERR_NULL
+    assert qa(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, MIS, A16, None, None) == sq.SQ_ERR_UNSUPPORTED
+    assert qa(A16, sq.SQ_BF16, 0, 64, 64, 0, None, 1e-6, A16, A16, None, None) == sq.SQ_OK
+    g = L.sq_gemm_fp8
+    assert g(None, A16, 4, 64, A16, A16, 8, None, A16, sq.SQ_BF16, 8, None, None) == sq.SQ_ERR_NULL
+    assert g(A16, A16, 4, 80, A16, A16, 8, None, A16, sq.SQ_BF16, 8, None, None) == sq.SQ_ERR_UNSUPPORTED
+    assert g(A16, A16, 0, 64, A16, A16, 8, None, A16, sq.SQ_BF16, 8, None, None) == sq.SQ_OK
+    lin = L.sq_w8a8_linear_fp8
+    assert lin(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, A16, A16, 8, None, A16, sq.SQ_BF16, 8,
+               None, 0, None, None) == sq.SQ_ERR_WORKSPACE
+
+
 def test_row_limits(L):
     big = (1 << 24) + 1
     assert L.sq_quant_act(A16, sq.SQ_BF16, big, 64, 64, 0, None, 1e-6, A16, A16, None,

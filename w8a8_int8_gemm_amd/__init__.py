@@ -60,6 +60,11 @@ def lib() -> ctypes.CDLL:
         L.sq_quant_act_static.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, P, P, P]
         L.sq_w8a8_linear_static.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, P, I64, P, P, I,
                                             I64, P, ctypes.c_size_t, ctypes.POINTER(_DebugOut), P]
+        L.sq_quant_weight_fp8.argtypes = [P, I, I64, I64, I64, P, P, P, P]
+        L.sq_quant_act_fp8.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, P, P]
+        L.sq_gemm_fp8.argtypes = [P, P, I64, I64, P, P, I64, P, P, I, I64, P, P]
+        L.sq_w8a8_linear_fp8.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, I64, P, P, I, I64,
+                                         P, ctypes.c_size_t, ctypes.POINTER(_DebugOut), P]
         L.sq_status_string.argtypes = [I]
         L.sq_status_string.restype = ctypes.c_char_p
         L.sq_abi_version.restype = I
@@ -219,6 +224,52 @@ def sq_w8a8_linear_static(x, gamma_f, x_scale_static, wq, w_scale, y, workspace,
                                        _ptr(bias), _ptr(y), ydt, yld, _ptr(workspace), ws_bytes,
                                        dbg, _stream(stream)),
            "sq_w8a8_linear_static")
+
+
+def sq_quant_weight_fp8(w, s, wq, w_scale, *, stream=None) -> None:
+    """wq[N, K] E4M3 bytes (uint8) and w_scale[N] of diag(s) W -- see sq_quant_weight_fp8."""
+    K, N = w.shape
+    _check(lib().sq_quant_weight_fp8(_ptr(w), _dtype(w), K, N, _ld(w), _ptr(s), _ptr(wq),
+                                     _ptr(w_scale), _stream(stream)), "sq_quant_weight_fp8")
+
+
+def sq_quant_act_fp8(x, gamma_f, xq, x_scale, *, norm: bool = False, eps: float = 1e-6,
+                     row_rscale=None, stream=None) -> None:
+    """xq[T, K] E4M3 bytes and x_scale[T] -- see sq_quant_act_fp8."""
+    T, K = x.shape
+    _check(lib().sq_quant_act_fp8(_ptr(x), _dtype(x), T, K, _ld(x),
+                                  SQ_NORM_RMS if norm else SQ_NORM_NONE, _ptr(gamma_f), eps,
+                                  _ptr(xq), _ptr(x_scale), _ptr(row_rscale), _stream(stream)),
+           "sq_quant_act_fp8")
+
+
+def sq_gemm_fp8(xq, x_scale, wq, w_scale, y=None, *, bias=None, acc_out=None, stream=None) -> None:
+    """y = dequant(E4M3 product) + bias, or the fp32 accumulators -- see sq_gemm_fp8."""
+    T, K = xq.shape
+    N = wq.shape[0]
+    ydt, yld = (SQ_BF16, N) if y is None else (_dtype(y), _ld(y))
+    _check(lib().sq_gemm_fp8(_ptr(xq), _ptr(x_scale), T, K, _ptr(wq), _ptr(w_scale), N,
+                             _ptr(bias), _ptr(y), ydt, yld, _ptr(acc_out), _stream(stream)),
+           "sq_gemm_fp8")
+
+
+def sq_w8a8_linear_fp8(x, gamma_f, wq, w_scale, y, workspace, *, norm: bool = False,
+                       eps: float = 1e-6, bias=None, dbg_xq=None, dbg_x_scale=None,
+                       dbg_row_rscale=None, dbg_acc=None, stream=None) -> None:
+    """sq_quant_act_fp8 then sq_gemm_fp8 -- see sq_w8a8_linear_fp8."""
+    T, K = x.shape
+    N = wq.shape[0]
+    dbg = None
+    if any(v is not None for v in (dbg_xq, dbg_x_scale, dbg_row_rscale, dbg_acc)):
+        dbg = ctypes.byref(_DebugOut(_ptr(dbg_xq), _ptr(dbg_x_scale), _ptr(dbg_row_rscale),
+                                     _ptr(dbg_acc)))
+    ydt, yld = (SQ_BF16, N) if y is None else (_dtype(y), _ld(y))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().sq_w8a8_linear_fp8(_ptr(x), _dtype(x), T, K, _ld(x),
+                                    SQ_NORM_RMS if norm else SQ_NORM_NONE, _ptr(gamma_f), eps,
+                                    _ptr(wq), _ptr(w_scale), N, _ptr(bias), _ptr(y), ydt, yld,
+                                    _ptr(workspace), ws_bytes, dbg, _stream(stream)),
+           "sq_w8a8_linear_fp8")
 
 
 def sq_abi_version() -> int:

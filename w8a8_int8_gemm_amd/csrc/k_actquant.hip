@@ -71,6 +71,29 @@ __device__ __forceinline__ u32x2 quant8_div(const float (&xh)[8], float d) {
   return out;
 }
 
+// FP8 E4M3 codes of 8 values: the fp32 quotient x^ / d (IEEE division), then
+// v_cvt_pk_fp8_f32, which rounds to the nearest E4M3 value, ties to even.
+// With d = amax / 448 every quotient is at most 448 up to one rounding, inside
+// the format's finite range.  d == 0 (an all-zero token) gives codes 0.
+__device__ __forceinline__ u32x2 quant8_fp8(const float (&xh)[8], float d) {
+  u32x2 out;
+  out[0] = 0u;
+  out[1] = 0u;
+  if (d == 0.0f) return out;
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = xh[i] / d;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * h], y[4 * h + 1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * h + 2], y[4 * h + 3], w, true);
+    out[h] = (uint32_t)w;
+  }
+  return out;
+}
+
+enum { QF_INT8 = 0, QF_FP8 = 1 };
+
 // ---------------------------------------------------------------------------
 // K <= 8192: one token per wave, WPB tokens per workgroup.  Lane l owns the
 // 8-element chunks l, l + 64, ... (NV of them), so every load of a wave is
@@ -83,12 +106,15 @@ __device__ __forceinline__ u32x2 quant8_div(const float (&xh)[8], float d) {
 // ---------------------------------------------------------------------------
 constexpr int kWavesPerBlock = 8;
 // Up to 16 raw bytes per lane-chunk-slot (bf16 with K <= 4096, fp32 with
-// K <= 2048) the kernel fits 64 VGPRs: ask for 8 waves per SIMD there.
-template <class In, int NV>
-constexpr int quant_act_min_waves() { return In::kBytes * NV <= 16 ? 8 : 1; }
+// K <= 2048) the kernel fits 64 VGPRs: ask for 8 waves per SIMD there (6 for
+// the FP8 codes).
+template <class In, int NV, int QF>
+constexpr int quant_act_min_waves() {
+  return In::kBytes * NV <= 16 ? (QF == 1 ? 6 : 8) : 1;   // FP8: 8 quotients live per chunk
+}
 
-template <class In, int NV, bool NORM, bool STATIC>
-__global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV>())) void k_quant_act(
+template <class In, int NV, bool NORM, bool STATIC, int QF>
+__global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV, QF>())) void k_quant_act(
     const typename In::elem* __restrict__ x, int64_t T, int64_t K, int64_t ld,
     const float* __restrict__ gamma_f, float eps, const float* __restrict__ static_scale,
     int8_t* __restrict__ xq, float* __restrict__ xscale, float* __restrict__ rrow) {
@@ -173,7 +199,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV>()
   asm volatile("" ::: "memory");
 #pragma unroll
   for (int j = 0; j < NV; ++j) In::opaque(raw[j]);
-  const float d = STATIC ? static_scale[0] : am / 127.0f;
+  const float d = STATIC ? static_scale[0] : am / (QF == QF_FP8 ? 448.0f : 127.0f);
   const float rc = 1.0f / d;
   // d == 0: every x^ is 0 (or, for a static step, every code is 0) and rc = 0
   // gives code 0.  1/d overflowing (d tiny): every chunk takes the IEEE
@@ -189,10 +215,15 @@ __global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV>()
     const int ch = j * 64 + lane;
     float xh[8];
     smooth(jc, xh);
-    bool tie;
-    u32x2 c = quant8<STATIC>(xh, rcu, tie);
-    // rare: a quotient near a rounding tie; redo the chunk by IEEE division
-    if (tie || all_div) c = quant8_div<STATIC>(xh, d);
+    u32x2 c;
+    if constexpr (QF == QF_FP8) {
+      c = quant8_fp8(xh, d);
+    } else {
+      bool tie;
+      c = quant8<STATIC>(xh, rcu, tie);
+      // rare: a quotient near a rounding tie; redo the chunk by IEEE division
+      if (tie || all_div) c = quant8_div<STATIC>(xh, d);
+    }
     if (ch < nchunk) *reinterpret_cast<u32x2*>(qrow + ch * 8) = c;
   });
 }
@@ -201,7 +232,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV>()
 // K > 8192: one workgroup per token, three passes over the row (sum of
 // squares, max, quantize); the re-reads hit L2.
 // ---------------------------------------------------------------------------
-template <class In, bool NORM, bool STATIC>
+template <class In, bool NORM, bool STATIC, int QF>
 __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem* __restrict__ x,
                                                         int64_t T, int64_t K, int64_t ld,
                                                         const float* __restrict__ gamma_f,
@@ -252,7 +283,7 @@ __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem*
     __syncthreads();
     am = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
   }
-  const float d = STATIC ? static_scale[0] : am / 127.0f;
+  const float d = STATIC ? static_scale[0] : am / (QF == QF_FP8 ? 448.0f : 127.0f);
   if (threadIdx.x == 0) xscale[r] = d;
   const float rc = 1.0f / d;
   const bool fast = d > 0.0f && rc <= 3.0e38f;
@@ -267,9 +298,13 @@ __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem*
     u32x2 c;
     c[0] = 0u;
     c[1] = 0u;
-    bool tie = true;
-    if (fast) c = quant8<STATIC>(xh, rc, tie);
-    if (d > 0.0f && tie) c = quant8_div<STATIC>(xh, d);
+    if constexpr (QF == QF_FP8) {
+      c = quant8_fp8(xh, d);
+    } else {
+      bool tie = true;
+      if (fast) c = quant8<STATIC>(xh, rc, tie);
+      if (d > 0.0f && tie) c = quant8_div<STATIC>(xh, d);
+    }
     *reinterpret_cast<u32x2*>(xq + r * K + ch * 8) = c;
   }
 }
@@ -278,30 +313,30 @@ __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem*
 // host launcher
 // ---------------------------------------------------------------------------
 
-template <class In, int NV, bool NORM, bool STATIC>
+template <class In, int NV, bool NORM, bool STATIC, int QF>
 static void quant_act_nv(const void* x, int64_t T, int64_t K, int64_t ld, const float* gamma_f,
                          float eps, const float* sscale, int8_t* xq, float* xscale, float* rrow,
                          hipStream_t st) {
   const int64_t blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL((k_quant_act<In, NV, NORM, STATIC>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((k_quant_act<In, NV, NORM, STATIC, QF>), dim3((unsigned)blocks),
                      dim3(64 * kWavesPerBlock), 0, st, (const typename In::elem*)x, T, K, ld,
                      gamma_f, eps, sscale, xq, xscale, rrow);
 }
 
-template <class In, bool NORM, bool STATIC>
+template <class In, bool NORM, bool STATIC, int QF>
 static void quant_act_t(const void* x, int64_t T, int64_t K, int64_t ld, const float* gamma_f,
                         float eps, const float* sscale, int8_t* xq, float* xscale, float* rrow,
                         hipStream_t st) {
   const int64_t nchunk = K / 8;
 #define SQ_QA(NV) \
-  quant_act_nv<In, NV, NORM, STATIC>(x, T, K, ld, gamma_f, eps, sscale, xq, xscale, rrow, st)
+  quant_act_nv<In, NV, NORM, STATIC, QF>(x, T, K, ld, gamma_f, eps, sscale, xq, xscale, rrow, st)
   if (nchunk <= 64) SQ_QA(1);
   else if (nchunk <= 128) SQ_QA(2);
   else if (nchunk <= 256) SQ_QA(4);
   else if (nchunk <= 512) SQ_QA(8);
   else if (nchunk <= 1024) SQ_QA(16);
   else
-    hipLaunchKernelGGL((k_quant_act_wide<In, NORM, STATIC>), dim3((unsigned)T), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_quant_act_wide<In, NORM, STATIC, QF>), dim3((unsigned)T), dim3(256), 0, st,
                        (const typename In::elem*)x, T, K, ld, gamma_f, eps, sscale, xq, xscale,
                        rrow);
 #undef SQ_QA
@@ -309,23 +344,40 @@ static void quant_act_t(const void* x, int64_t T, int64_t K, int64_t ld, const f
 
 template <class In, bool NORM>
 static void quant_act_s(const void* x, int64_t T, int64_t K, int64_t ld, const float* gamma_f,
-                        float eps, const float* sscale, int8_t* xq, float* xscale, float* rrow,
-                        hipStream_t st) {
-  if (sscale) quant_act_t<In, NORM, true>(x, T, K, ld, gamma_f, eps, sscale, xq, xscale, rrow, st);
-  else quant_act_t<In, NORM, false>(x, T, K, ld, gamma_f, eps, sscale, xq, xscale, rrow, st);
+                        float eps, const float* sscale, bool fp8, int8_t* xq, float* xscale,
+                        float* rrow, hipStream_t st) {
+  if (fp8)
+    quant_act_t<In, NORM, false, QF_FP8>(x, T, K, ld, gamma_f, eps, sscale, xq, xscale, rrow, st);
+  else if (sscale)
+    quant_act_t<In, NORM, true, QF_INT8>(x, T, K, ld, gamma_f, eps, sscale, xq, xscale, rrow, st);
+  else
+    quant_act_t<In, NORM, false, QF_INT8>(x, T, K, ld, gamma_f, eps, sscale, xq, xscale, rrow, st);
+}
+
+static void quant_act_any(const void* x, bool bf16, int64_t T, int64_t K, int64_t ld, bool norm,
+                          const float* gamma_f, float eps, const float* sscale, bool fp8,
+                          int8_t* xq, float* xscale, float* rrow, hipStream_t st) {
+  if (T <= 0) return;
+  if (bf16) {
+    if (norm) quant_act_s<Bf16In, true>(x, T, K, ld, gamma_f, eps, sscale, fp8, xq, xscale, rrow, st);
+    else quant_act_s<Bf16In, false>(x, T, K, ld, gamma_f, eps, sscale, fp8, xq, xscale, rrow, st);
+  } else {
+    if (norm) quant_act_s<F32In, true>(x, T, K, ld, gamma_f, eps, sscale, fp8, xq, xscale, rrow, st);
+    else quant_act_s<F32In, false>(x, T, K, ld, gamma_f, eps, sscale, fp8, xq, xscale, rrow, st);
+  }
 }
 
 void launch_quant_act(const void* x, bool bf16, int64_t T, int64_t K, int64_t ld, bool norm,
                       const float* gamma_f, float eps, const float* static_scale, int8_t* xq,
                       float* xscale, float* rrow, hipStream_t st) {
-  if (T <= 0) return;
-  if (bf16) {
-    if (norm) quant_act_s<Bf16In, true>(x, T, K, ld, gamma_f, eps, static_scale, xq, xscale, rrow, st);
-    else quant_act_s<Bf16In, false>(x, T, K, ld, gamma_f, eps, static_scale, xq, xscale, rrow, st);
-  } else {
-    if (norm) quant_act_s<F32In, true>(x, T, K, ld, gamma_f, eps, static_scale, xq, xscale, rrow, st);
-    else quant_act_s<F32In, false>(x, T, K, ld, gamma_f, eps, static_scale, xq, xscale, rrow, st);
-  }
+  quant_act_any(x, bf16, T, K, ld, norm, gamma_f, eps, static_scale, false, xq, xscale, rrow, st);
+}
+
+void launch_quant_act_fp8(const void* x, bool bf16, int64_t T, int64_t K, int64_t ld, bool norm,
+                          const float* gamma_f, float eps, uint8_t* xq, float* xscale, float* rrow,
+                          hipStream_t st) {
+  quant_act_any(x, bf16, T, K, ld, norm, gamma_f, eps, nullptr, true,
+                reinterpret_cast<int8_t*>(xq), xscale, rrow, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -2,28 +2,34 @@
 // fused dequantization epilogue ("06 -- SmoothQuant", section 7: the matmul is
 // a straight INT8 x INT8 -> INT32 product followed by
 // Y = scale_x * scale_w * Y_int32; "Taming the Outliers", step I6: add bias
-// and dequantize).
+// and dequantize), and the same kernel for FP8 E4M3 operands with fp32
+// accumulation ("SmoothQuant and W8A8", One layer, measured: FP8 E4M3).
 //
 //   acc[t, n] = sum_k xq[t, k] * wq[n, k]     (xq [T, K], wq [N, K], K contiguous)
 //   y[t, n]   = fp32(fp32(xs[t] * ws[n]) * fp32(acc)) + bias[n]  -> bf16 / fp32
 //
 // Design (CDNA4):
-//  * v_mfma_i32_32x32x32_i8: 16 int8 of K per lane per operand, int32
-//    accumulators.  The weight tile is the MFMA's A operand (rows = output
-//    channels) and the activation tile its B operand (columns = tokens), so a
-//    lane's 4 consecutive accumulator rows are 4 consecutive output channels
-//    of one token -- one 8-byte bf16 store instead of four 2-byte ones.
-//  * Workgroup tile BT tokens x BN channels, 4 waves in a 2 x 2 grid, each
-//    wave (BT/2) x (BN/2) = (BT/64) x (BN/64) MFMA tiles of 32 x 32.
-//  * K is staged through LDS 128 bytes at a time, double buffered, with
-//    global_load_lds_dwordx4 (HBM/L2 -> LDS without VGPRs).  A 1 KiB load
-//    instruction fills 8 rows of 128 bytes; the 16-byte chunk c of row r is
-//    stored at chunk position c ^ swz(r), so the 32 rows an MFMA operand read
-//    touches spread over all LDS banks.
+//  * v_mfma_i32_32x32x32_i8 (INT8) / v_mfma_f32_32x32x64_f8f6f4 (FP8).  The
+//    weight tile is the MFMA's A operand (rows = output channels) and the
+//    activation tile its B operand (columns = tokens), so a lane's 4
+//    consecutive accumulator rows are 4 consecutive output channels of one
+//    token -- 8 contiguous output bytes.
+//  * Workgroup tile BT tokens x BN channels; WGT x WGN waves, each a
+//    (BT/WGT) x (BN/WGN) grid of 32 x 32 MFMA tiles.  The large-T tile is
+//    256 x 256 with 8 waves of 128 x 64 (2 waves per SIMD).
+//  * K is staged through LDS 64 bytes at a time in 4 buffers, loads issued 3-4
+//    stages ahead with buffer_load_dwordx4 ... lds (HBM/L2 -> LDS without
+//    VGPRs).  A 1 KiB load instruction fills 16 rows of 64 bytes; the 16-byte
+//    chunk c of row r is stored at chunk position c ^ swz(r), so the rows an
+//    MFMA operand read touches spread over all 64 LDS banks.
+//  * Operand reads of the next k-step are interleaved one-for-one with the
+//    MFMAs; one workgroup barrier per stage.
 //  * Tiles are ordered so that the workgroups that share an XCD (the
 //    hardware deals workgroup ids round-robin over the 8 XCDs) take one
 //    contiguous range of tiles, grouped GROUP_T token panels at a time: they
 //    share activation and weight panels in their XCD's L2.
+//  * The bf16 epilogue stages each wave's tile in LDS and writes whole
+//    128-byte row segments.
 #include "sq_common.h"
 #include "sq_internal.h"
 
@@ -81,7 +87,13 @@ __device__ __forceinline__ void issue_rows(__amdgpu_buffer_rsrc_t r, int8_t* dst
 }
 #endif
 
-template <int BT, int BN, int WGT, int WGN, int SWZ, int OUT>
+// F8: the operands are FP8 E4M3 codes (same bytes, same staging) multiplied
+// by v_mfma_f32_32x32x64_f8f6f4 into fp32 accumulators; else INT8 codes into
+// int32 accumulators.  The FP8 instruction sums its products in groups of 8
+// consecutive k (MFMA order, which keeps 16-byte K runs together here), each
+// aligned to the group's largest product with the bits below 2^-13 of it
+// dropped, then adds the group sums in fp32.
+template <int BT, int BN, int WGT, int WGN, int SWZ, int OUT, bool F8>
 __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __restrict__ xq,
                                                    const float* __restrict__ xs, int T, int K,
                                                    const int8_t* __restrict__ wq,
@@ -159,7 +171,8 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
     }
   }
 
-  v16i acc[NTN][NTT];
+  typedef typename std::conditional<F8, v16f, v16i>::type AccT;
+  AccT acc[NTN][NTT];
 #pragma unroll
   for (int i = 0; i < NTN; ++i)
 #pragma unroll
@@ -186,11 +199,13 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
     }
   };
   auto mfmas = [&](const v4i (&a)[NTN], const v4i (&b)[NTT]) {
+    if constexpr (!F8) {
 #pragma unroll
-    for (int i = 0; i < NTN; ++i)
+      for (int i = 0; i < NTN; ++i)
 #pragma unroll
-      for (int j = 0; j < NTT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NTT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
   };
 
   // --- pipeline.  Stage s lives in LDS buffer s % 4.  In iteration s the
@@ -210,6 +225,71 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
   else if (nst == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPS) : "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if constexpr (F8) {
+    // FP8: one v_mfma_f32_32x32x64_f8f6f4 per 32x32 tile per stage.  A lane's
+    // 32 operand bytes are its two 16-byte chunks of the INT8 layout (k-steps
+    // 0 and 1): the A and B operands take the same K positions, so the sum is
+    // over the stage's 64 K values in a permuted order.  Iteration s: wait for
+    // stage s+1 and for this wave's reads of stage s (issued last iteration),
+    // barrier, loads of stage s+4 into the buffer stage s vacated, then the
+    // MFMAs of stage s column by column, each column's B operands of stage s+1
+    // read as soon as its MFMAs have consumed stage s's.
+    typedef int v8i_t __attribute__((ext_vector_type(8)));
+    auto cat = [](const v4i& lo, const v4i& hi) -> v8i_t {
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto fa = [&](int stage, int i, v4i& lo, v4i& hi) {
+      const int8_t* wb = ws_l + (stage & (NS - 1)) * WS;
+      const int row = wn * WTN + i * 32 + frow;
+      lo = *reinterpret_cast<const v4i*>(wb + row * BK + ((fhalf ^ swz<SWZ>(row)) << 4));
+      hi = *reinterpret_cast<const v4i*>(wb + row * BK + (((2 + fhalf) ^ swz<SWZ>(row)) << 4));
+    };
+    auto fb = [&](int stage, int j, v4i& lo, v4i& hi) {
+      const int8_t* xb = xs_l + (stage & (NS - 1)) * XS;
+      const int row = wt * WTT + j * 32 + frow;
+      lo = *reinterpret_cast<const v4i*>(xb + row * BK + ((fhalf ^ swz<SWZ>(row)) << 4));
+      hi = *reinterpret_cast<const v4i*>(xb + row * BK + (((2 + fhalf) ^ swz<SWZ>(row)) << 4));
+    };
+    // A1/B1 are written before they are read whenever a next stage exists; the
+    // zeros only keep the optimizer from treating them as undefined.
+    v4i A0[NTN][2], B0[NTT][2], A1[NTN][2], B1[NTT][2];
+#pragma unroll
+    for (int i = 0; i < NTN; ++i) A1[i][0] = A1[i][1] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < NTT; ++j) B1[j][0] = B1[j][1] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < NTN; ++i) fa(0, i, A0[i][0], A0[i][1]);
+#pragma unroll
+    for (int j = 0; j < NTT; ++j) fb(0, j, B0[j][0], B0[j][1]);
+    auto step8 = [&](int st, v4i (&ca)[NTN][2], v4i (&cb)[NTT][2], v4i (&na)[NTN][2],
+                     v4i (&nb)[NTT][2]) {
+      const int left = nst - 1 - st;          // stages after st
+      if (left >= 3) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * LPS) : "memory");
+      else if (left == 2) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LPS) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (st + NS < nst) issue(st + NS);
+      const bool more = left >= 1;
+#pragma unroll
+      for (int j = 0; j < NTT; ++j) {
+#pragma unroll
+        for (int i = 0; i < NTN; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              cat(ca[i][0], ca[i][1]), cat(cb[j][0], cb[j][1]), acc[i][j], 0, 0, 0, 0, 0, 0);
+        if (more) fb(st + 1, j, nb[j][0], nb[j][1]);
+      }
+      if (more) {
+#pragma unroll
+        for (int i = 0; i < NTN; ++i) fa(st + 1, i, na[i][0], na[i][1]);
+      }
+    };
+    int st = 0;
+    for (; st + 1 < nst; st += 2) {
+      step8(st, A0, B0, A1, B1);
+      step8(st + 1, A1, B1, A0, B0);
+    }
+    if (st < nst) step8(st, A0, B0, A1, B1);
+  } else {
   v4i a0[NTN], b0[NTT], a1[NTN], b1[NTT];
   frags(0, 0, a0, b0);
   // one iteration; FLY = stages still in flight after stage s+1 has landed
@@ -268,6 +348,7 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
   if (st == nst - 3) iter(st++, I1(), BF_());
   if (st == nst - 2) iter(st++, I0(), BF_());
   iter(st, IN(), BF_());
+  }
   __syncthreads();
 
   // --- epilogue.  Lane l of tile (i, j): token t = .. + l%32; channels
@@ -342,7 +423,15 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
           int32_t* dst = reinterpret_cast<int32_t*>(yout) + (int64_t)t * N + n;
           v4i o;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * g + e];
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (F8) {
+              // bit_cast of the vector-element lvalue itself reads element 0
+              // of the vector; go through a scalar copy
+              const float f = acc[i][j][4 * g + e];
+              o[e] = __builtin_bit_cast(int32_t, f);
+            }
+            else o[e] = acc[i][j][4 * g + e];
+          }
           if (full_i32) {
             *reinterpret_cast<v4i*>(dst) = o;
           } else if (t < T) {
@@ -382,7 +471,7 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
 // host launcher
 // ---------------------------------------------------------------------------
 
-template <int BT, int BN, int WGT, int WGN>
+template <int BT, int BN, int WGT, int WGN, bool F8>
 static void gemm_tile(const int8_t* xq, const float* xs, int T, int K, const int8_t* wq,
                       const float* ws, int N, const float* bias, void* y, int ldy, int out,
                       hipStream_t st) {
@@ -391,14 +480,30 @@ static void gemm_tile(const int8_t* xq, const float* xs, int T, int K, const int
   const dim3 grid((unsigned)ntiles), block(64 * WGT * WGN);
   const int group_t = 4;
   if (out == OUT_BF16)
-    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, SWZ, OUT_BF16>), grid, block, 0, st, xq, xs,
-                       T, K, wq, ws, N, bias, y, ldy, group_t);
+    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, SWZ, OUT_BF16, F8>), grid, block, 0, st, xq,
+                       xs, T, K, wq, ws, N, bias, y, ldy, group_t);
   else if (out == OUT_F32)
-    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, SWZ, OUT_F32>), grid, block, 0, st, xq, xs,
-                       T, K, wq, ws, N, bias, y, ldy, group_t);
+    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, SWZ, OUT_F32, F8>), grid, block, 0, st, xq,
+                       xs, T, K, wq, ws, N, bias, y, ldy, group_t);
   else
-    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, SWZ, OUT_I32>), grid, block, 0, st, xq, xs,
-                       T, K, wq, ws, N, bias, y, ldy, group_t);
+    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, SWZ, OUT_I32, F8>), grid, block, 0, st, xq,
+                       xs, T, K, wq, ws, N, bias, y, ldy, group_t);
+}
+
+template <bool F8>
+static void gemm_sizes(const int8_t* xq, const float* xs, int64_t T, int64_t K, const int8_t* wq,
+                       const float* ws, int64_t N, const float* bias, void* y, int64_t ldy,
+                       int out, hipStream_t st) {
+  const int it = (int)T, ik = (int)K, in = (int)N, il = (int)ldy;
+  // 256 x 256 tiles fill the chip when there are at least ~2 per CU;
+  // otherwise smaller tiles trade reuse for occupancy.
+  const int64_t t256 = ((T + 255) / 256) * ((N + 255) / 256);
+  if (t256 >= 384)
+    gemm_tile<256, 256, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+  else if (((T + 255) / 256) * ((N + 127) / 128) >= 256)
+    gemm_tile<256, 128, 2, 2, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+  else
+    gemm_tile<128, 128, 2, 2, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
 }
 
 void launch_gemm(const int8_t* xq, const float* xs, int64_t T, int64_t K, const int8_t* wq,
@@ -409,16 +514,17 @@ void launch_gemm(const int8_t* xq, const float* xs, int64_t T, int64_t K, const 
     launch_gemm_decode(xq, xs, T, K, wq, ws, N, bias, y, ldy, out, st);
     return;
   }
-  const int it = (int)T, ik = (int)K, in = (int)N, il = (int)ldy;
-  // 256 x 256 tiles fill the chip when there are at least ~2 per CU;
-  // otherwise smaller tiles trade reuse for occupancy.
-  const int64_t t256 = ((T + 255) / 256) * ((N + 255) / 256);
-  if (t256 >= 384)
-    gemm_tile<256, 256, 2, 4>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
-  else if (((T + 255) / 256) * ((N + 127) / 128) >= 256)
-    gemm_tile<256, 128, 2, 2>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
-  else
-    gemm_tile<128, 128, 2, 2>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+  gemm_sizes<false>(xq, xs, T, K, wq, ws, N, bias, y, ldy, out, st);
+}
+
+// FP8 E4M3 operands; out 2 = the raw fp32 accumulators.  Few tokens run the
+// tile kernel too (its rows past T read as zeros).
+void launch_gemm_fp8(const uint8_t* xq, const float* xs, int64_t T, int64_t K, const uint8_t* wq,
+                     const float* ws, int64_t N, const float* bias, void* y, int64_t ldy, int out,
+                     hipStream_t st) {
+  if (T <= 0 || N <= 0) return;
+  gemm_sizes<true>(reinterpret_cast<const int8_t*>(xq), xs, T, K,
+                   reinterpret_cast<const int8_t*>(wq), ws, N, bias, y, ldy, out, st);
 }
 
 }  // namespace sqk

@@ -6,10 +6,11 @@
 //    The trick).
 //  * k_fold_w: W^[j, n] = W[j, n] * s_j -- s folded into the weight's input
 //    rows ("06 -- SmoothQuant", section 2).
-//  * k_div127: Delta_n = amax_n / 127 (the symmetric 8-bit step, "Taming the
-//    Outliers", The Problem).
-//  * k_quant_weight_t: codes = round-half-even(W^ / Delta_n), written
-//    transposed to the [N, K] K-contiguous layout the GEMM streams.
+//  * k_div_const: Delta_n = amax_n / 127 (the symmetric 8-bit step, "Taming
+//    the Outliers", The Problem), or amax_n / 448 for FP8 E4M3.
+//  * k_quant_weight_t: codes = round-half-even(W^ / Delta_n) (INT8, or the
+//    nearest E4M3 value for FP8), written transposed to the [N, K]
+//    K-contiguous layout the GEMM streams.
 // The per-output-channel absmax between fold and quant is k_col_absmax with
 // the row scale s (k_calib.hip), so W^ is never materialised.
 #include "sq_common.h"
@@ -47,16 +48,17 @@ __global__ __launch_bounds__(256) void k_fold_w(const typename In::elem* __restr
   *reinterpret_cast<f32x4*>(wout + j * N + n0 + 4) = o1;
 }
 
-__global__ void k_div127(float* __restrict__ p, int64_t n) {
+// Delta_n = amax_n / qmax: 127 for INT8, 448 (the largest finite E4M3) for FP8
+__global__ void k_div_const(float* __restrict__ p, int64_t n, float qmax) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = p[i] / 127.0f;
+  if (i < n) p[i] = p[i] / qmax;
 }
 
 // Tile of 128 input channels (k) x 64 output channels (n).  Thread (tx, ty),
 // tx = tid % 8, ty = tid / 8: columns n0 + 8*tx .. +7 of rows k0 + 4*ty .. +3.
 // Each thread packs its 4 codes per column (4 consecutive k) into one dword of
 // the LDS tile [n][k]; the tile is then written out 32 bytes per thread along k.
-template <class In, bool kRowScale>
+template <class In, bool kRowScale, bool F8>
 __global__ __launch_bounds__(256) void k_quant_weight_t(const typename In::elem* __restrict__ w,
                                                         int64_t K, int64_t N, int64_t ld,
                                                         const float* __restrict__ s,
@@ -96,6 +98,8 @@ __global__ __launch_bounds__(256) void k_quant_weight_t(const typename In::elem*
   uint32_t packed[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) packed[i] = 0u;
+  // quotients W^ / Delta_n (0 where Delta_n == 0, rows past K and columns past N)
+  float qt[4][8];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t k = k0 + ty * 4 + r;
@@ -104,12 +108,22 @@ __global__ __launch_bounds__(256) void k_quant_weight_t(const typename In::elem*
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float wh = kRowScale ? v[i] * sk[r] : v[i];
-      float q = 0.0f;
-      if (d[i] != 0.0f) {
-        q = rintf(wh / d[i]);
-        q = fminf(fmaxf(q, -127.0f), 127.0f);
+      qt[r][i] = (d[i] != 0.0f && ncol && k < K) ? wh / d[i] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (F8) {
+      // nearest E4M3, ties to even; |quotient| <= 448 up to one rounding
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(qt[0][i], qt[1][i], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(qt[2][i], qt[3][i], w, true);
+      packed[i] = (uint32_t)w;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float q = fminf(fmaxf(rintf(qt[r][i]), -127.0f), 127.0f);
+        packed[i] |= code_byte(q) << (8 * r);
       }
-      if (ncol && k < K) packed[i] |= code_byte(q) << (8 * r);
     }
   }
 #pragma unroll
@@ -155,30 +169,41 @@ void launch_fold_w(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, c
     hipLaunchKernelGGL(k_fold_w<F32In>, grid, dim3(256), 0, st, (const float*)w, K, N, ld, s, wout);
 }
 
-void launch_div127(float* p, int64_t n, hipStream_t st) {
+void launch_div_const(float* p, int64_t n, float qmax, hipStream_t st) {
   if (n <= 0) return;
-  hipLaunchKernelGGL(k_div127, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+  hipLaunchKernelGGL(k_div_const, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, qmax);
 }
 
-void launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
+template <bool F8>
+static void quant_weight_f(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
                            const float* s, const float* wscale, int8_t* wq, hipStream_t st) {
   if (K <= 0 || N <= 0) return;
   const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((K + 127) / 128));
   if (bf16) {
     if (s)
-      hipLaunchKernelGGL((k_quant_weight_t<Bf16In, true>), grid, dim3(256), 0, st,
+      hipLaunchKernelGGL((k_quant_weight_t<Bf16In, true, F8>), grid, dim3(256), 0, st,
                          (const uint16_t*)w, K, N, ld, s, wscale, wq);
     else
-      hipLaunchKernelGGL((k_quant_weight_t<Bf16In, false>), grid, dim3(256), 0, st,
+      hipLaunchKernelGGL((k_quant_weight_t<Bf16In, false, F8>), grid, dim3(256), 0, st,
                          (const uint16_t*)w, K, N, ld, s, wscale, wq);
   } else {
     if (s)
-      hipLaunchKernelGGL((k_quant_weight_t<F32In, true>), grid, dim3(256), 0, st,
+      hipLaunchKernelGGL((k_quant_weight_t<F32In, true, F8>), grid, dim3(256), 0, st,
                          (const float*)w, K, N, ld, s, wscale, wq);
     else
-      hipLaunchKernelGGL((k_quant_weight_t<F32In, false>), grid, dim3(256), 0, st,
+      hipLaunchKernelGGL((k_quant_weight_t<F32In, false, F8>), grid, dim3(256), 0, st,
                          (const float*)w, K, N, ld, s, wscale, wq);
   }
+}
+
+void launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
+                           const float* s, const float* wscale, int8_t* wq, hipStream_t st) {
+  quant_weight_f<false>(w, bf16, K, N, ld, s, wscale, wq, st);
+}
+
+void launch_quant_weight_t_fp8(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
+                               const float* s, const float* wscale, uint8_t* wq, hipStream_t st) {
+  quant_weight_f<true>(w, bf16, K, N, ld, s, wscale, reinterpret_cast<int8_t*>(wq), st);
 }
 
 }  // namespace sqk

@@ -20,15 +20,21 @@ void launch_wrow_absmax_s(const void* w, bool bf16, int64_t K, int64_t N, int64_
 void launch_fold_gamma(const float* s, const float* gamma, float* gout, int64_t K, hipStream_t st);
 void launch_fold_w(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, const float* s,
                    float* wout, hipStream_t st);
-void launch_div127(float* p, int64_t n, hipStream_t st);
+void launch_div_const(float* p, int64_t n, float qmax, hipStream_t st);
 void launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
                            const float* s, const float* wscale, int8_t* wq, hipStream_t st);
+void launch_quant_weight_t_fp8(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
+                               const float* s, const float* wscale, uint8_t* wq, hipStream_t st);
 
 // k_actquant.hip
 // static_scale NULL: per-token step; else the device scalar per-tensor step
 void launch_quant_act(const void* x, bool bf16, int64_t T, int64_t K, int64_t ld, bool norm,
                       const float* gamma_f, float eps, const float* static_scale, int8_t* xq,
                       float* xscale, float* rrow, hipStream_t st);
+// per-token FP8 E4M3 codes, step amax / 448
+void launch_quant_act_fp8(const void* x, bool bf16, int64_t T, int64_t K, int64_t ld, bool norm,
+                          const float* gamma_f, float eps, uint8_t* xq, float* xscale, float* rrow,
+                          hipStream_t st);
 void launch_static_scale(const float* a, const float* gamma_f, int64_t K, float* out,
                          hipStream_t st);
 
@@ -36,6 +42,9 @@ void launch_static_scale(const float* a, const float* gamma_f, int64_t K, float*
 void launch_gemm(const int8_t* xq, const float* xs, int64_t T, int64_t K, const int8_t* wq,
                  const float* ws, int64_t N, const float* bias, void* y, int64_t ldy, int out,
                  hipStream_t st);
+void launch_gemm_fp8(const uint8_t* xq, const float* xs, int64_t T, int64_t K, const uint8_t* wq,
+                     const float* ws, int64_t N, const float* bias, void* y, int64_t ldy, int out,
+                     hipStream_t st);
 void launch_gemm_decode(const int8_t* xq, const float* xs, int64_t T, int64_t K, const int8_t* wq,
                         const float* ws, int64_t N, const float* bias, void* y, int64_t ldy,
                         int out, hipStream_t st);

@@ -157,8 +157,47 @@ sq_status sq_quant_weight(const void* w, sq_dtype w_dt, int64_t k, int64_t n, in
   if (n == 0) return SQ_OK;
   sqk::launch_fill_f32(w_scale, n, 0.0f, stream);
   sqk::launch_col_absmax(w, w_dt == SQ_BF16, k, n, ldw, s, w_scale, stream);
-  sqk::launch_div127(w_scale, n, stream);
+  sqk::launch_div_const(w_scale, n, 127.0f, stream);
   sqk::launch_quant_weight_t(w, w_dt == SQ_BF16, k, n, ldw, s, w_scale, wq, stream);
+  return hip_status();
+}
+
+sq_status sq_quant_weight_fp8(const void* w, sq_dtype w_dt, int64_t k, int64_t n, int64_t ldw,
+                              const float* s, uint8_t* wq, float* w_scale, hipStream_t stream) {
+  SQ_TRY(check_k(k));
+  SQ_TRY(check_mat(w, w_dt, k, n, ldw));
+  if (wq == nullptr || w_scale == nullptr) return SQ_ERR_NULL;
+  if (n % 8 != 0 || !aligned16(wq)) return SQ_ERR_UNSUPPORTED;
+  if (n == 0) return SQ_OK;
+  sqk::launch_fill_f32(w_scale, n, 0.0f, stream);
+  sqk::launch_col_absmax(w, w_dt == SQ_BF16, k, n, ldw, s, w_scale, stream);
+  sqk::launch_div_const(w_scale, n, 448.0f, stream);
+  sqk::launch_quant_weight_t_fp8(w, w_dt == SQ_BF16, k, n, ldw, s, w_scale, wq, stream);
+  return hip_status();
+}
+
+sq_status sq_quant_act_fp8(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                           sq_norm norm, const float* gamma_f, float eps, uint8_t* xq,
+                           float* x_scale, float* row_rscale, hipStream_t stream) {
+  SQ_TRY(check_act(x, x_dt, t, k, ldx, norm, eps));
+  if (xq == nullptr || x_scale == nullptr) return SQ_ERR_NULL;
+  if (!aligned16(xq)) return SQ_ERR_UNSUPPORTED;
+  if (t == 0) return SQ_OK;
+  sqk::launch_quant_act_fp8(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps, xq,
+                            x_scale, norm == SQ_NORM_RMS ? row_rscale : nullptr, stream);
+  return hip_status();
+}
+
+sq_status sq_gemm_fp8(const uint8_t* xq, const float* x_scale, int64_t t, int64_t k,
+                      const uint8_t* wq, const float* w_scale, int64_t n, const float* bias,
+                      void* y, sq_dtype y_dt, int64_t ldy, float* acc_out, hipStream_t stream) {
+  SQ_TRY(check_gemm(reinterpret_cast<const int8_t*>(xq), x_scale, t, k,
+                    reinterpret_cast<const int8_t*>(wq), w_scale, n, y, y_dt, ldy,
+                    reinterpret_cast<const int32_t*>(acc_out)));
+  if (t == 0 || n == 0) return SQ_OK;
+  void* out = acc_out != nullptr ? (void*)acc_out : y;
+  sqk::launch_gemm_fp8(xq, x_scale, t, k, wq, w_scale, n, bias, out, acc_out ? n : ldy,
+                       gemm_out(y_dt, reinterpret_cast<const int32_t*>(acc_out)), stream);
   return hip_status();
 }
 
@@ -220,9 +259,9 @@ namespace {
 // the forward of sq_w8a8_linear (static_scale NULL) and sq_w8a8_linear_static
 sq_status linear_impl(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
                       sq_norm norm, const float* gamma_f, float eps, const float* static_scale,
-                      const int8_t* wq, const float* w_scale, int64_t n, const float* bias,
-                      void* y, sq_dtype y_dt, int64_t ldy, void* workspace, size_t ws_bytes,
-                      const sq_debug_out* dbg, hipStream_t stream) {
+                      bool fp8, const int8_t* wq, const float* w_scale, int64_t n,
+                      const float* bias, void* y, sq_dtype y_dt, int64_t ldy, void* workspace,
+                      size_t ws_bytes, const sq_debug_out* dbg, hipStream_t stream) {
   SQ_TRY(check_act(x, x_dt, t, k, ldx, norm, eps));
   if (t == 0) return wq == nullptr ? SQ_ERR_NULL : SQ_OK;   // nothing to compute
   int8_t* xq = dbg ? dbg->xq : nullptr;
@@ -240,13 +279,23 @@ sq_status linear_impl(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_
   // the GEMM's own checks, with the codes and scales that will exist by then
   if (w_scale == nullptr && acc == nullptr) return SQ_ERR_NULL;
   SQ_TRY(check_gemm(xq, xs, t, k, wq, w_scale, n, y, y_dt, ldy, acc));
-  sqk::launch_quant_act(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps,
-                        static_scale, xq, xs, norm == SQ_NORM_RMS ? rrow : nullptr, stream);
+  if (fp8)
+    sqk::launch_quant_act_fp8(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps,
+                              reinterpret_cast<uint8_t*>(xq), xs,
+                              norm == SQ_NORM_RMS ? rrow : nullptr, stream);
+  else
+    sqk::launch_quant_act(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps,
+                          static_scale, xq, xs, norm == SQ_NORM_RMS ? rrow : nullptr, stream);
   SQ_TRY(hip_status());
   if (n == 0) return SQ_OK;
   void* out = acc != nullptr ? (void*)acc : y;
-  sqk::launch_gemm(xq, xs, t, k, wq, w_scale, n, bias, out, acc ? n : ldy, gemm_out(y_dt, acc),
-                   stream);
+  if (fp8)
+    sqk::launch_gemm_fp8(reinterpret_cast<const uint8_t*>(xq), xs, t, k,
+                         reinterpret_cast<const uint8_t*>(wq), w_scale, n, bias, out,
+                         acc ? n : ldy, gemm_out(y_dt, acc), stream);
+  else
+    sqk::launch_gemm(xq, xs, t, k, wq, w_scale, n, bias, out, acc ? n : ldy, gemm_out(y_dt, acc),
+                     stream);
   return hip_status();
 }
 
@@ -259,8 +308,18 @@ sq_status sq_w8a8_linear(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int
                          const float* w_scale, int64_t n, const float* bias, void* y,
                          sq_dtype y_dt, int64_t ldy, void* workspace, size_t ws_bytes,
                          const sq_debug_out* dbg, hipStream_t stream) {
-  return linear_impl(x, x_dt, t, k, ldx, norm, gamma_f, eps, nullptr, wq, w_scale, n, bias, y,
-                     y_dt, ldy, workspace, ws_bytes, dbg, stream);
+  return linear_impl(x, x_dt, t, k, ldx, norm, gamma_f, eps, nullptr, false, wq, w_scale, n, bias,
+                     y, y_dt, ldy, workspace, ws_bytes, dbg, stream);
+}
+
+sq_status sq_w8a8_linear_fp8(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                             sq_norm norm, const float* gamma_f, float eps, const uint8_t* wq,
+                             const float* w_scale, int64_t n, const float* bias, void* y,
+                             sq_dtype y_dt, int64_t ldy, void* workspace, size_t ws_bytes,
+                             const sq_debug_out* dbg, hipStream_t stream) {
+  return linear_impl(x, x_dt, t, k, ldx, norm, gamma_f, eps, nullptr, true,
+                     reinterpret_cast<const int8_t*>(wq), w_scale, n, bias, y, y_dt, ldy,
+                     workspace, ws_bytes, dbg, stream);
 }
 
 sq_status sq_w8a8_linear_static(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
@@ -270,8 +329,8 @@ sq_status sq_w8a8_linear_static(const void* x, sq_dtype x_dt, int64_t t, int64_t
                                 sq_dtype y_dt, int64_t ldy, void* workspace, size_t ws_bytes,
                                 const sq_debug_out* dbg, hipStream_t stream) {
   if (x_scale_static == nullptr) return SQ_ERR_NULL;
-  return linear_impl(x, x_dt, t, k, ldx, norm, gamma_f, eps, x_scale_static, wq, w_scale, n, bias,
-                     y, y_dt, ldy, workspace, ws_bytes, dbg, stream);
+  return linear_impl(x, x_dt, t, k, ldx, norm, gamma_f, eps, x_scale_static, false, wq, w_scale,
+                     n, bias, y, y_dt, ldy, workspace, ws_bytes, dbg, stream);
 }
 
 }  // extern "C"
