@@ -44,7 +44,7 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
         _lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
@@ -61,6 +61,9 @@ def _load():
         _lib.oracle_static_scale.argtypes = [P, I, I64, I64, I64, I, F, P]
         _lib.oracle_static_scale.restype = F
         _lib.oracle_quant_act_static.argtypes = [P, I, I64, I64, I64, I, P, F, P, F, P, P, P]
+        _lib.oracle_static_scale_fp8.argtypes = [P, I, I64, I64, I64, I, F, P]
+        _lib.oracle_static_scale_fp8.restype = F
+        _lib.oracle_quant_act_static_fp8.argtypes = [P, I, I64, I64, I64, I, P, F, P, F, P, P, P]
         _lib.oracle_e4m3_encode_array.argtypes = [P, I64, P]
         _lib.oracle_e4m3_decode_array.argtypes = [P, I64, P]
         _lib.oracle_quant_weight_fp8.argtypes = [P, I64, I64, I64, P, P]
@@ -257,6 +260,38 @@ def prepare_weight_fp8(w, s, gamma=None):
     gp, what = fold(s, gamma, w)
     qw, ws = quant_weight_fp8(what)
     return gp, qw, ws
+
+
+def static_scale_fp8(x_cal: np.ndarray, gamma_f=None, *, norm: bool = False,
+                     eps: float = 1e-6) -> np.float32:
+    """Per-tensor E4M3 activation step: the calibration tokens' maximum of |x^| / 448."""
+    x, bf = _mat(x_cal)
+    T, K = x.shape
+    return np.float32(_load().oracle_static_scale_fp8(_p(x), bf, T, K, K, int(norm), float(eps),
+                                                      _p(_f32(gamma_f))))
+
+
+def quant_act_static_fp8(x: np.ndarray, delta, gamma_f=None, *, norm: bool = False,
+                         r: Optional[np.ndarray] = None, eps: float = 1e-6):
+    """(q [T,K] E4M3 codes, x_scale [T] = delta, r [T] or None): quotients clip to +-448."""
+    x, bf = _mat(x)
+    T, K = x.shape
+    q = np.empty((T, K), np.uint8)
+    xs = np.empty(T, np.float32)
+    rout = np.empty(T, np.float32) if norm else None
+    _load().oracle_quant_act_static_fp8(_p(x), bf, T, K, K, int(norm), _p(_f32(r)), float(eps),
+                                        _p(_f32(gamma_f)), float(np.float32(delta)), _p(q),
+                                        _p(xs), _p(rout))
+    return q, xs, rout
+
+
+def linear_static_fp8(x, delta, gamma_f, qw, w_scale, bias=None, *, norm=False, r=None,
+                      eps=1e-6, out_bf16=True):
+    """E4M3 forward with one static activation step for every token."""
+    q, xs, rr = quant_act_static_fp8(x, delta, gamma_f, norm=norm, r=r, eps=eps)
+    acc = gemm_fp8(q, qw)
+    y = epilogue_f32acc(acc.astype(np.float32), xs, w_scale, bias)
+    return dict(q=q, x_scale=xs, r=rr, acc=acc, y32=y, y=to_bf16(y) if out_bf16 else y)
 
 
 def linear_fp8(x, gamma_f, qw, w_scale, bias=None, *, norm=False, r=None, eps=1e-6,

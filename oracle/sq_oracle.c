@@ -231,10 +231,10 @@ static float smoothed(const void *x, int is_bf16, int64_t i, int norm, float r, 
   return v * (gamma_f ? gamma_f[k] : 1.0f);
 }
 
-/* Static per-tensor step: Delta = fp32( max over every calibration token t and
-   channel k of |x^[t,k]| / 127 ), with x^ formed exactly as in oracle_quant_act. */
-float oracle_static_scale(const void *x, int is_bf16, int64_t T, int64_t K, int64_t ld, int norm,
-                          float eps, const float *gamma_f) {
+/* max over every calibration token t and channel k of |x^[t,k]|, with x^
+   formed exactly as in oracle_quant_act */
+static float static_amax(const void *x, int is_bf16, int64_t T, int64_t K, int64_t ld, int norm,
+                         float eps, const float *gamma_f) {
   float *r = NULL;
   if (norm) {
     r = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1));
@@ -247,7 +247,14 @@ float oracle_static_scale(const void *x, int is_bf16, int64_t T, int64_t K, int6
       amax = fmaxf(amax, fabsf(smoothed(x, is_bf16, t * ld + k, norm, norm ? r[t] : 1.0f,
                                         gamma_f, k)));
   free(r);
-  return amax / 127.0f;
+  return amax;
+}
+
+/* Static per-tensor step: Delta = fp32( max over every calibration token t and
+   channel k of |x^[t,k]| / 127 ). */
+float oracle_static_scale(const void *x, int is_bf16, int64_t T, int64_t K, int64_t ld, int norm,
+                          float eps, const float *gamma_f) {
+  return static_amax(x, is_bf16, T, K, ld, norm, eps, gamma_f) / 127.0f;
 }
 
 /* Static quantization with a fixed step `delta` for every token:
@@ -367,6 +374,47 @@ void oracle_quant_act_fp8(const void *x, int is_bf16, int64_t T, int64_t K, int6
         q[t * K + k] = (d == 0.0f) ? (uint8_t)0 : oracle_e4m3_encode(xh[k] / d);
     }
     free(xh);
+  }
+  free(r);
+}
+
+/* Static per-tensor E4M3 step: Delta = fp32( max over every calibration token
+   and channel of |x^| / 448 ). */
+float oracle_static_scale_fp8(const void *x, int is_bf16, int64_t T, int64_t K, int64_t ld,
+                              int norm, float eps, const float *gamma_f) {
+  return static_amax(x, is_bf16, T, K, ld, norm, eps, gamma_f) / 448.0f;
+}
+
+/* Static E4M3 quantization with a fixed step `delta` for every token:
+   code = e4m3(clip(fp32(x^ / delta), -448, 448)), so values past the
+   calibrated maximum clip to the largest finite magnitude; x_scale[t] = delta;
+   delta == 0 gives codes 0.  r_in / r_out as in oracle_quant_act. */
+void oracle_quant_act_static_fp8(const void *x, int is_bf16, int64_t T, int64_t K, int64_t ld,
+                                 int norm, const float *r_in, float eps, const float *gamma_f,
+                                 float delta, uint8_t *q, float *x_scale, float *r_out) {
+  float *r = NULL;
+  if (norm) {
+    r = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1));
+    if (r_in)
+      memcpy(r, r_in, sizeof(float) * (size_t)T);
+    else
+      oracle_rms_rscale(x, is_bf16, T, K, ld, eps, r);
+    if (r_out) memcpy(r_out, r, sizeof(float) * (size_t)T);
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    x_scale[t] = delta;
+    for (int64_t k = 0; k < K; ++k) {
+      float v = smoothed(x, is_bf16, t * ld + k, norm, norm ? r[t] : 1.0f, gamma_f, k);
+      if (delta == 0.0f) {
+        q[t * K + k] = 0;
+        continue;
+      }
+      float y = v / delta;
+      if (y > 448.0f) y = 448.0f;
+      if (y < -448.0f) y = -448.0f;
+      q[t * K + k] = oracle_e4m3_encode(y);
+    }
   }
   free(r);
 }

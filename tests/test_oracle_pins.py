@@ -588,3 +588,46 @@ def test_gemm_fp8_matches_numpy_fp64():
     acc = oracle.gemm_fp8(q, qw)
     ref = oracle.e4m3_decode(q).astype(np.float64) @ oracle.e4m3_decode(qw).astype(np.float64).T
     np.testing.assert_array_equal(acc, ref)
+
+
+# static per-tensor E4M3 step ("SmoothQuant and W8A8", One layer, measured:
+# one static scale per tensor from the calibration tokens' maximum, in INT8
+# and in FP8 E4M3; Gotchas: values past the calibrated maximum are clipped)
+
+def test_static_fp8_equals_dynamic_fp8_on_the_calibration_maximum():
+    rng = np.random.default_rng(34)
+    x = rng.standard_normal((48, 320)).astype(np.float32)
+    x[:, 17] *= 25
+    g = rng.uniform(0.5, 1.5, 320).astype(np.float32)
+    d = oracle.static_scale_fp8(x, g)
+    t = int(np.argmax(np.abs(x * g).max(axis=1)))
+    qs, xs, _ = oracle.quant_act_static_fp8(x[t:t + 1], d, g)
+    qd, xd, _ = oracle.quant_act_fp8(x[t:t + 1], g)
+    assert xd[0] == d and xs[0] == d
+    np.testing.assert_array_equal(qs, qd)
+    # and the same maximum gives the INT8 static step over 127 instead of 448
+    assert oracle.static_scale(x, g) * F32(127.0) == pytest.approx(float(d) * 448.0, rel=1e-6)
+
+
+def test_static_fp8_clips_past_the_calibrated_maximum():
+    tab = _e4m3_table()
+    pos = sorted((v, c) for c, v in tab.items() if c < 0x80)
+    rng = np.random.default_rng(35)
+    cal = rng.standard_normal((32, 16)).astype(np.float32)
+    d = oracle.static_scale_fp8(cal)
+    x = (rng.standard_normal((8, 16)) * 3).astype(np.float32)    # well past the calibration range
+    q, _, _ = oracle.quant_act_static_fp8(x, d)
+    assert (q & 0x7F).max() == 0x7E                               # 448 reached, never NaN
+    for t in range(8):
+        for k in range(16):
+            a = abs(float(np.float32(x[t, k]) / d))
+            best = 0x7E if a >= 448 else min(pos, key=lambda p: (abs(p[0] - a), p[1] & 1))[1]
+            assert (int(q[t, k]) & 0x7F) == best, (t, k, a)
+            assert (int(q[t, k]) >> 7) == (1 if x[t, k] < 0 else 0)
+
+
+def test_static_fp8_zero_step_gives_zero_codes():
+    d = oracle.static_scale_fp8(np.zeros((3, 64), np.float32))
+    assert d == 0.0
+    q, xs, _ = oracle.quant_act_static_fp8(np.ones((2, 64), np.float32), d)
+    assert not q.any() and not xs.any()
