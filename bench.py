@@ -42,6 +42,7 @@ if ROOT not in sys.path:
 METRIC = "W8A8 smoothed linear TOPS + % of MI355X INT8 MFMA peak (T=8192,K=N=4096)"
 PEAK_INT8_TOPS = 5000.0     # MI355X dense INT8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA, 5.0 PFLOP/s
 WORKLOAD = "qproj_prefill"
 COUNTERS = os.path.join(ROOT, "profiles", "gemm_w8a8_qproj_prefill_counters.json")
 
@@ -170,34 +171,84 @@ def alpha_sweep(sq, torch, inp, wl, x_cal, x, w, bias, dev, sample=256):
     wq = torch.empty((N, K), dtype=torch.int8, device=dev)
     xq = torch.empty((T, K), dtype=torch.int8, device=dev)
     y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    wq8 = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    xq8 = torch.empty((T, K), dtype=torch.uint8, device=dev)
     d = e(1)
     sq.sq_calibrate(x_cal, None, 0.5, a)           # activation absmax once
-    res, res_static = {}, {}
+    res, res_static, res_fp8, res_fp8s = {}, {}, {}, {}
     for alpha in (None, 0.1, 0.25, 0.5, 0.75, 1.0):
         key = "unsmoothed" if alpha is None else f"{alpha:g}"
-        gamma_f = None
-        if alpha is None:                          # unsmoothed: s = 1, gamma_f = 1
-            sq.sq_quant_weight(w, None, wq, wsc)
-        else:
+        gamma_f, s_arg = None, None                # unsmoothed: s = 1, gamma_f = 1
+        if alpha is not None:
             sq.sq_calibrate(None, w, alpha, a, wm, s)   # s from the stored absmax
             sq.sq_smooth_fold(s, None, gp)
-            sq.sq_quant_weight(w, s, wq, wsc)
-            gamma_f = gp
-        for static, out in ((False, res), (True, res_static)):
-            if static:                             # one step from the calibration maximum
+            gamma_f, s_arg = gp, s
+        sq.sq_quant_weight(w, s_arg, wq, wsc)
+        for mode, out in (("per_token", res), ("static", res_static), ("fp8", res_fp8),
+                          ("fp8_static", res_fp8s)):
+            if mode == "static":                   # one step from the calibration maximum
                 sq.sq_act_static_scale(a, gamma_f, d)
                 sq.sq_quant_act_static(x, gamma_f, d, xq, xs)
+                sq.sq_gemm_w8a8(xq, xs, wq, wsc, y, bias=bias)
+            elif mode == "fp8":                    # E4M3 weights and per-token activations
+                sq.sq_quant_weight_fp8(w, s_arg, wq8, wsc)
+                sq.sq_quant_act_fp8(x, gamma_f, xq8, xs)
+                sq.sq_gemm_fp8(xq8, xs, wq8, wsc, y, bias=bias)
+            elif mode == "fp8_static":             # E4M3, one static activation step
+                sq.sq_act_static_scale_fp8(a, gamma_f, d)
+                sq.sq_quant_act_static_fp8(x, gamma_f, d, xq8, xs)
+                sq.sq_gemm_fp8(xq8, xs, wq8, wsc, y, bias=bias)
             else:
                 sq.sq_quant_act(x, gamma_f, xq, xs)
-            sq.sq_gemm_w8a8(xq, xs, wq, wsc, y, bias=bias)
+                sq.sq_gemm_w8a8(xq, xs, wq, wsc, y, bias=bias)
             torch.cuda.synchronize()
             yb = y[torch.from_numpy(rows).to(dev)].view(torch.int16).cpu().numpy().view(np.uint16)
             out[key] = float(np.linalg.norm(f64(yb) - ref)) / ref_norm
     res["static_per_tensor"] = res_static
+    res["fp8_e4m3_per_token"] = res_fp8
+    res["fp8_e4m3_static_per_tensor"] = res_fp8s
     res["tokens"] = int(sample)
     res["reference"] = ("X W + b in fp64 over evenly spaced tokens; relative Frobenius norm; "
-                        "top level: per-token activation steps")
+                        "top level: INT8 per-token activation steps")
     return res
+
+
+def fp8_timing(sq, torch, sets, wl, s, gp, bias, dev, iters=20):
+    """Event times of the FP8 E4M3 weight and activation quantizers and the
+    FP8 GEMM on the headline shape (rotating input sets), the GEMM against
+    the dense FP8 matrix peak."""
+    T, K, N = wl.T, wl.K, wl.N
+    wq8 = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    xq8 = [torch.empty((T, K), dtype=torch.uint8, device=dev) for _ in sets]
+    wsc = torch.empty(N, dtype=torch.float32, device=dev)
+    xs = [torch.empty(T, dtype=torch.float32, device=dev) for _ in sets]
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    calls = {
+        "quant_weight_fp8": lambda i: sq.sq_quant_weight_fp8(sets[i][2], s, wq8, wsc,
+                                                             stream=stream),
+        "quant_act_fp8": lambda i: sq.sq_quant_act_fp8(sets[i][1], gp, xq8[i], xs[i],
+                                                       stream=stream),
+        "gemm_fp8": lambda i: sq.sq_gemm_fp8(xq8[i], xs[i], wq8, wsc, y, bias=bias,
+                                             stream=stream),
+    }
+    out = {}
+    for name, fn in calls.items():
+        for i in range(len(sets)):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(iters):
+            fn(i % len(sets))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name + "_us"] = e0.elapsed_time(e1) * 1e3 / iters
+    ops = 2.0 * T * K * N
+    ach = ops / (out["gemm_fp8_us"] * 1e-6) / 1e12
+    out["gemm_fp8"] = {"achieved": ach, "unit": "TFLOP/s", "peak": PEAK_FP8_TFLOPS,
+                       "frac": ach / PEAK_FP8_TFLOPS}
+    return out
 
 
 def static_act_timing(sq, torch, sets, gp, a, xq, xs, dev, iters=20):
@@ -449,6 +500,7 @@ def main():
         out["quant_act_static_vs_per_token"] = static_act_timing(sq, torch, sets, gp, a, xq, xs,
                                                                  dev)
         out["decode_gemm"] = decode_gemm(sq, torch, dev)
+        out["fp8"] = fp8_timing(sq, torch, sets, wl, s, gp, bias, dev)
     if not args.no_cpu_baseline:
         print("timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_seconds)

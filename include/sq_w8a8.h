@@ -249,6 +249,17 @@ sq_status sq_w8a8_linear_static(const void *x, sq_dtype x_dt, int64_t t, int64_t
  * sq_w8a8_linear_fp8: sq_quant_act_fp8 then sq_gemm_fp8, workspace and debug
  *   outputs as sq_w8a8_linear (dbg->xq receives the E4M3 bytes, dbg->acc the
  *   fp32 accumulators as raw 32-bit words).
+ *
+ * Static per-tensor E4M3 step (the same layer sweep takes one static scale per
+ * tensor in FP8 as in INT8; "SmoothQuant and W8A8", Gotchas: values past the
+ * calibrated maximum clip):
+ * sq_act_static_scale_fp8: as sq_act_static_scale with 448 in place of 127:
+ *   x_scale_static[0] = fp32(max_j fp32(a[j] * |gamma_f[j]|) / 448).
+ * sq_quant_act_static_fp8: as sq_quant_act_fp8 with the device scalar step
+ *   *x_scale_static for every token: code = nearest E4M3 of clip(fp32(x^ /
+ *   step), -448, 448), ties to even; step 0 gives codes 0; x_scale[t] = step.
+ * sq_w8a8_linear_static_fp8: sq_quant_act_static_fp8 then sq_gemm_fp8,
+ *   otherwise as sq_w8a8_linear_fp8.  SQ_ERR_NULL if x_scale_static is NULL.
  */
 sq_status sq_quant_weight_fp8(const void *w, sq_dtype w_dt, int64_t k, int64_t n, int64_t ldw,
                               const float *s, uint8_t *wq, float *w_scale, hipStream_t stream);
@@ -264,6 +275,19 @@ sq_status sq_w8a8_linear_fp8(const void *x, sq_dtype x_dt, int64_t t, int64_t k,
                              const float *bias, void *y, sq_dtype y_dt, int64_t ldy,
                              void *workspace, size_t ws_bytes, const sq_debug_out *dbg,
                              hipStream_t stream);
+sq_status sq_act_static_scale_fp8(const float *a, const float *gamma_f, int64_t k,
+                                  float *x_scale_static, hipStream_t stream);
+sq_status sq_quant_act_static_fp8(const void *x, sq_dtype x_dt, int64_t t, int64_t k,
+                                  int64_t ldx, sq_norm norm, const float *gamma_f, float eps,
+                                  const float *x_scale_static, uint8_t *xq, float *x_scale,
+                                  float *row_rscale, hipStream_t stream);
+sq_status sq_w8a8_linear_static_fp8(const void *x, sq_dtype x_dt, int64_t t, int64_t k,
+                                    int64_t ldx, sq_norm norm, const float *gamma_f, float eps,
+                                    const float *x_scale_static, const uint8_t *wq,
+                                    const float *w_scale, int64_t n, const float *bias, void *y,
+                                    sq_dtype y_dt, int64_t ldy, void *workspace,
+                                    size_t ws_bytes, const sq_debug_out *dbg,
+                                    hipStream_t stream);
 
 /* Static description of a status code (host memory, never NULL). */
 const char *sq_status_string(sq_status status);

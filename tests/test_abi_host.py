@@ -164,6 +164,24 @@ def test_fp8_validation(L):
                None, 0, None, None) == sq.SQ_ERR_WORKSPACE
 
 
+def test_static_fp8_validation(L):
+    st = L.sq_act_static_scale_fp8
+    assert st(None, None, 64, A16, None) == sq.SQ_ERR_NULL
+    assert st(A16, None, 64, None, None) == sq.SQ_ERR_NULL
+    assert st(A16, None, 0, A16, None) == sq.SQ_ERR_SHAPE
+    assert st(A16, None, 96, A16, None) == sq.SQ_ERR_UNSUPPORTED
+    qs = L.sq_quant_act_static_fp8
+    assert qs(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, None, A16, A16, None, None) == sq.SQ_ERR_NULL
+    assert qs(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, A16, None, A16, None, None) == sq.SQ_ERR_NULL
+    assert qs(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, A16, MIS, A16, None, None) == sq.SQ_ERR_UNSUPPORTED
+    assert qs(A16, sq.SQ_BF16, 0, 64, 64, 0, None, 1e-6, A16, A16, A16, None, None) == sq.SQ_OK
+    ls = L.sq_w8a8_linear_static_fp8
+    assert ls(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, None, A16, A16, 8, None, A16,
+              sq.SQ_BF16, 8, A16, 1 << 20, None, None) == sq.SQ_ERR_NULL
+    assert ls(A16, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, A16, A16, A16, 8, None, A16,
+              sq.SQ_BF16, 8, None, 0, None, None) == sq.SQ_ERR_WORKSPACE
+
+
 def test_row_limits(L):
     big = (1 << 24) + 1
     assert L.sq_quant_act(A16, sq.SQ_BF16, big, 64, 64, 0, None, 1e-6, A16, A16, None,

@@ -242,3 +242,112 @@ def test_linear_fp8_end_to_end(name, sizes):
     e_gpu, e_ref = oracle.rel_error(ref, to_np(y)), oracle.rel_error(ref, out["y"])
     say(f"  fp8 layer error gpu {e_gpu:.4%} oracle {e_ref:.4%}")
     assert e_gpu <= e_ref * 1.01 + 1e-6
+
+
+# --- static per-tensor E4M3 step -------------------------------------------
+
+def _check_step(d_gpu, d_ref, norm):
+    """Bit-exact without a norm; in norm mode within one fp32 ulp (the RMSNorm
+    factor of the maximal token comes from fp64 sums in different orders)."""
+    a = int(np.array([d_gpu], np.float32).view(np.int32)[0])
+    b = int(np.array([d_ref], np.float32).view(np.int32)[0])
+    assert abs(a - b) <= (1 if norm else 0), (d_gpu, d_ref)
+
+
+def _gpu_static_scale_fp8(xc, gp, *, norm):
+    a = f32(xc.shape[1])
+    sq.sq_calibrate(xc, None, 0.5, a, norm=norm, gamma=None)
+    d = f32(1)
+    sq.sq_act_static_scale_fp8(a, gp, d)
+    return d
+
+
+@pytest.mark.parametrize("T,K,norm,dt", [(64, 512, False, "bf16"), (37, 1344, True, "bf16"),
+                                         (96, 320, False, "f32"), (8, 16384, False, "bf16"),
+                                         (24, 8192, True, "bf16")])
+def test_static_fp8_step_and_codes(T, K, norm, dt):
+    wl = synth.WORKLOADS["rmsnorm_qkv" if norm else "qproj_prefill"].with_sizes(
+        T=T, Tc=2 * T, K=K, N=64)
+    if dt == "f32":
+        wl = wl.with_sizes(io_dtype="f32")
+    say(f"fp8 static step T={T} K={K} norm={norm} {dt}")
+    inp = synth.make_inputs(wl)
+    rng = np.random.default_rng(T + K + 1)
+    gp_h = rng.uniform(0.3, 2.0, K).astype(np.float32)
+    gp = to_dev(gp_h)
+    d = _gpu_static_scale_fp8(to_dev(inp.x_cal), gp, norm=norm)
+    _check_step(to_np(d)[0], oracle.static_scale_fp8(inp.x_cal, gp_h, norm=norm), norm)
+    d_ref = to_np(d)[0]
+    xq, xs, rr = _u8((T, K)), f32(T), f32(T)
+    sq.sq_quant_act_static_fp8(to_dev(inp.x), gp, d, xq, xs, norm=norm,
+                               row_rscale=rr if norm else None)
+    torch.cuda.synchronize()
+    q_ref, xs_ref, _ = oracle.quant_act_static_fp8(inp.x, d_ref, gp_h, norm=norm,
+                                                   r=to_np(rr) if norm else None)
+    np.testing.assert_array_equal(to_np(xq), q_ref)
+    np.testing.assert_array_equal(to_np(xs), xs_ref)
+
+
+def test_static_fp8_clipping_and_zero_step():
+    say("fp8 static clipping and zero step")
+    rng = np.random.default_rng(4)
+    K, T = 1024, 40
+    x = (rng.standard_normal((T, K)) * 4).astype(np.float32)
+    x[:, 7] *= 50                                       # far past the step's range
+    x[3] = 0.0
+    xd = to_dev(x)
+    for delta in (np.float32(0.05), np.float32(1e-3), np.float32(0.0), np.float32(1e-40)):
+        d = to_dev(np.array([delta], np.float32))
+        xq, xs = _u8((T, K)), f32(T)
+        sq.sq_quant_act_static_fp8(xd, None, d, xq, xs)
+        torch.cuda.synchronize()
+        q_ref, xs_ref, _ = oracle.quant_act_static_fp8(x, delta)
+        np.testing.assert_array_equal(to_np(xq), q_ref)
+        np.testing.assert_array_equal(to_np(xs), xs_ref)
+        if delta > 0:
+            assert (to_np(xq) & 0x7F).max() == 0x7E     # clipped to 448, never NaN
+
+
+@pytest.mark.parametrize("name,sizes", [("qproj_prefill", dict(T=300, Tc=512, K=1024, N=640)),
+                                        ("rmsnorm_qkv", dict(T=130, Tc=256, K=2048, N=384))])
+def test_static_fp8_linear_end_to_end(name, sizes):
+    wl = synth.WORKLOADS[name].with_sizes(**sizes)
+    say(f"fp8 static linear {name} {sizes}")
+    inp = synth.make_inputs(wl)
+    T, K, N = wl.T, wl.K, wl.N
+    g = None if inp.gamma is None else to_dev(inp.gamma)
+    xc, w = to_dev(inp.x_cal), to_dev(inp.w)
+    _, _, s = gpu_calibrate(xc, w, wl.alpha, norm=wl.norm, gamma=g)
+    gp = f32(K)
+    sq.sq_smooth_fold(s, g, gp)
+    wq, wsc = _u8((N, K)), f32(N)
+    sq.sq_quant_weight_fp8(w, s, wq, wsc)
+    d = _gpu_static_scale_fp8(xc, gp, norm=wl.norm)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=DEV)
+    work = torch.empty(sq.sq_linear_workspace_bytes(T, K), dtype=torch.uint8, device=DEV)
+    dbg_xq, dbg_xs, rr = _u8((T, K)), f32(T), f32(T)
+    bias = to_dev(inp.bias)
+    sq.sq_w8a8_linear_static_fp8(to_dev(inp.x), gp, d, wq, wsc, y, work, norm=wl.norm, bias=bias,
+                                 dbg_xq=dbg_xq, dbg_x_scale=dbg_xs,
+                                 dbg_row_rscale=rr if wl.norm else None)
+    acc = torch.empty((T, N), dtype=torch.float32, device=DEV)
+    sq.sq_gemm_fp8(dbg_xq, dbg_xs, wq, wsc, None, acc_out=acc)
+    torch.cuda.synchronize()
+    gp_h, s_h = to_np(gp), to_np(s)
+    _check_step(to_np(d)[0], oracle.static_scale_fp8(inp.x_cal, gp_h, norm=wl.norm), wl.norm)
+    d_ref = to_np(d)[0]
+    _, qw_ref, ws_ref = oracle.prepare_weight_fp8(inp.w, s_h, inp.gamma)
+    np.testing.assert_array_equal(to_np(wq), qw_ref)
+    out = oracle.linear_static_fp8(inp.x, d_ref, gp_h, qw_ref, ws_ref, inp.bias, norm=wl.norm,
+                                   r=to_np(rr) if wl.norm else None)
+    np.testing.assert_array_equal(to_np(dbg_xq), out["q"])
+    np.testing.assert_array_equal(to_np(dbg_xs), out["x_scale"])
+    y_fed = oracle.to_bf16(oracle.epilogue_f32acc(to_np(acc), out["x_scale"], ws_ref, inp.bias))
+    np.testing.assert_array_equal(to_np(y), y_fed)
+    yo = synth.bf16_bits_to_f32(out["y"])
+    yg = synth.bf16_bits_to_f32(to_np(y))
+    slack = np.abs(out["x_scale"][:, None] * ws_ref[None, :]) * _acc_bound(out["q"], qw_ref)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(yo), 2.0 ** -126))) - 7)
+    assert np.all(np.abs(yg - yo) <= np.maximum(2e-3 * np.abs(yo), 1e-2) + slack + ulp)
+    ref = oracle.reference_fp64(inp.x, inp.w, inp.bias, norm=wl.norm, gamma=inp.gamma)
+    say(f"  fp8 static-step layer error {oracle.rel_error(ref, to_np(y)):.4%}")

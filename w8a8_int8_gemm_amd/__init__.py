@@ -65,6 +65,11 @@ def lib() -> ctypes.CDLL:
         L.sq_gemm_fp8.argtypes = [P, P, I64, I64, P, P, I64, P, P, I, I64, P, P]
         L.sq_w8a8_linear_fp8.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, I64, P, P, I, I64,
                                          P, ctypes.c_size_t, ctypes.POINTER(_DebugOut), P]
+        L.sq_act_static_scale_fp8.argtypes = [P, P, I64, P, P]
+        L.sq_quant_act_static_fp8.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, P, P, P]
+        L.sq_w8a8_linear_static_fp8.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, P, I64, P, P,
+                                                I, I64, P, ctypes.c_size_t,
+                                                ctypes.POINTER(_DebugOut), P]
         L.sq_status_string.argtypes = [I]
         L.sq_status_string.restype = ctypes.c_char_p
         L.sq_abi_version.restype = I
@@ -274,3 +279,42 @@ def sq_w8a8_linear_fp8(x, gamma_f, wq, w_scale, y, workspace, *, norm: bool = Fa
 
 def sq_abi_version() -> int:
     return int(lib().sq_abi_version())
+
+
+def sq_act_static_scale_fp8(a, gamma_f, x_scale_static, *, stream=None) -> None:
+    """x_scale_static[0] = max_j(a[j] * |gamma_f[j]|) / 448 -- see sq_act_static_scale_fp8."""
+    K = a.shape[0]
+    _check(lib().sq_act_static_scale_fp8(_ptr(a), _ptr(gamma_f), K, _ptr(x_scale_static),
+                                         _stream(stream)), "sq_act_static_scale_fp8")
+
+
+def sq_quant_act_static_fp8(x, gamma_f, x_scale_static, xq, x_scale, *, norm: bool = False,
+                            eps: float = 1e-6, row_rscale=None, stream=None) -> None:
+    """xq[T, K] E4M3 bytes with one fixed step for every token -- see sq_quant_act_static_fp8."""
+    T, K = x.shape
+    _check(lib().sq_quant_act_static_fp8(_ptr(x), _dtype(x), T, K, _ld(x),
+                                         SQ_NORM_RMS if norm else SQ_NORM_NONE, _ptr(gamma_f),
+                                         eps, _ptr(x_scale_static), _ptr(xq), _ptr(x_scale),
+                                         _ptr(row_rscale), _stream(stream)),
+           "sq_quant_act_static_fp8")
+
+
+def sq_w8a8_linear_static_fp8(x, gamma_f, x_scale_static, wq, w_scale, y, workspace, *,
+                              norm: bool = False, eps: float = 1e-6, bias=None, dbg_xq=None,
+                              dbg_x_scale=None, dbg_row_rscale=None, dbg_acc=None,
+                              stream=None) -> None:
+    """sq_w8a8_linear_fp8 with the static step -- see sq_w8a8_linear_static_fp8."""
+    T, K = x.shape
+    N = wq.shape[0]
+    dbg = None
+    if any(v is not None for v in (dbg_xq, dbg_x_scale, dbg_row_rscale, dbg_acc)):
+        dbg = ctypes.byref(_DebugOut(_ptr(dbg_xq), _ptr(dbg_x_scale), _ptr(dbg_row_rscale),
+                                     _ptr(dbg_acc)))
+    ydt, yld = (SQ_BF16, N) if y is None else (_dtype(y), _ld(y))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().sq_w8a8_linear_static_fp8(_ptr(x), _dtype(x), T, K, _ld(x),
+                                           SQ_NORM_RMS if norm else SQ_NORM_NONE, _ptr(gamma_f),
+                                           eps, _ptr(x_scale_static), _ptr(wq), _ptr(w_scale), N,
+                                           _ptr(bias), _ptr(y), ydt, yld, _ptr(workspace),
+                                           ws_bytes, dbg, _stream(stream)),
+           "sq_w8a8_linear_static_fp8")

@@ -74,7 +74,10 @@ __device__ __forceinline__ u32x2 quant8_div(const float (&xh)[8], float d) {
 // FP8 E4M3 codes of 8 values: the fp32 quotient x^ / d (IEEE division), then
 // v_cvt_pk_fp8_f32, which rounds to the nearest E4M3 value, ties to even.
 // With d = amax / 448 every quotient is at most 448 up to one rounding, inside
-// the format's finite range.  d == 0 (an all-zero token) gives codes 0.
+// the format's finite range.  A static step (CLAMP) can see larger quotients:
+// they clip to +-448 first (the conversion would give NaN from 480 up).
+// d == 0 (an all-zero token, or a zero static step) gives codes 0.
+template <bool CLAMP = false>
 __device__ __forceinline__ u32x2 quant8_fp8(const float (&xh)[8], float d) {
   u32x2 out;
   out[0] = 0u;
@@ -82,7 +85,10 @@ __device__ __forceinline__ u32x2 quant8_fp8(const float (&xh)[8], float d) {
   if (d == 0.0f) return out;
   float y[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = xh[i] / d;
+  for (int i = 0; i < 8; ++i) {
+    y[i] = xh[i] / d;
+    if (CLAMP) y[i] = fminf(fmaxf(y[i], -448.0f), 448.0f);
+  }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * h], y[4 * h + 1], 0, false);
@@ -217,7 +223,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV, Q
     smooth(jc, xh);
     u32x2 c;
     if constexpr (QF == QF_FP8) {
-      c = quant8_fp8(xh, d);
+      c = quant8_fp8<STATIC>(xh, d);
     } else {
       bool tie;
       c = quant8<STATIC>(xh, rcu, tie);
@@ -299,7 +305,7 @@ __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem*
     c[0] = 0u;
     c[1] = 0u;
     if constexpr (QF == QF_FP8) {
-      c = quant8_fp8(xh, d);
+      c = quant8_fp8<STATIC>(xh, d);
     } else {
       bool tie = true;
       if (fast) c = quant8<STATIC>(xh, rc, tie);
@@ -346,7 +352,9 @@ template <class In, bool NORM>
 static void quant_act_s(const void* x, int64_t T, int64_t K, int64_t ld, const float* gamma_f,
                         float eps, const float* sscale, bool fp8, int8_t* xq, float* xscale,
                         float* rrow, hipStream_t st) {
-  if (fp8)
+  if (fp8 && sscale)
+    quant_act_t<In, NORM, true, QF_FP8>(x, T, K, ld, gamma_f, eps, sscale, xq, xscale, rrow, st);
+  else if (fp8)
     quant_act_t<In, NORM, false, QF_FP8>(x, T, K, ld, gamma_f, eps, sscale, xq, xscale, rrow, st);
   else if (sscale)
     quant_act_t<In, NORM, true, QF_INT8>(x, T, K, ld, gamma_f, eps, sscale, xq, xscale, rrow, st);
@@ -374,33 +382,33 @@ void launch_quant_act(const void* x, bool bf16, int64_t T, int64_t K, int64_t ld
 }
 
 void launch_quant_act_fp8(const void* x, bool bf16, int64_t T, int64_t K, int64_t ld, bool norm,
-                          const float* gamma_f, float eps, uint8_t* xq, float* xscale, float* rrow,
-                          hipStream_t st) {
-  quant_act_any(x, bf16, T, K, ld, norm, gamma_f, eps, nullptr, true,
+                          const float* gamma_f, float eps, const float* static_scale, uint8_t* xq,
+                          float* xscale, float* rrow, hipStream_t st) {
+  quant_act_any(x, bf16, T, K, ld, norm, gamma_f, eps, static_scale, true,
                 reinterpret_cast<int8_t*>(xq), xscale, rrow, st);
 }
 
 // ---------------------------------------------------------------------------
 // Static step from channel maxima: out[0] = fp32( max_j fp32(a[j] * |g[j]|) /
-// 127 ), g NULL = 1.  Rounding is monotone and sign symmetric, so with a[j] the
+// qmax ), g NULL = 1, qmax 127 (INT8) or 448 (FP8 E4M3).  Rounding is monotone and sign symmetric, so with a[j] the
 // channel maximum of |x| (of |fp32(h * r_t)| in norm mode) this is the maximum
 // of |x^| over every calibration token and channel.  One workgroup.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_static_scale(const float* __restrict__ a,
                                                       const float* __restrict__ g, int64_t K,
-                                                      float* __restrict__ out) {
+                                                      float qmax, float* __restrict__ out) {
   __shared__ float red[4];
   float m = 0.0f;
   for (int64_t j = threadIdx.x; j < K; j += 256) m = fmaxf(m, a[j] * (g ? fabsf(g[j]) : 1.0f));
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) out[0] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) / 127.0f;
+  if (threadIdx.x == 0) out[0] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) / qmax;
 }
 
-void launch_static_scale(const float* a, const float* gamma_f, int64_t K, float* out,
+void launch_static_scale(const float* a, const float* gamma_f, int64_t K, float qmax, float* out,
                          hipStream_t st) {
-  hipLaunchKernelGGL(k_static_scale, dim3(1), dim3(256), 0, st, a, gamma_f, K, out);
+  hipLaunchKernelGGL(k_static_scale, dim3(1), dim3(256), 0, st, a, gamma_f, K, qmax, out);
 }
 
 }  // namespace sqk

@@ -31,11 +31,13 @@ void launch_quant_weight_t_fp8(const void* w, bool bf16, int64_t K, int64_t N, i
 void launch_quant_act(const void* x, bool bf16, int64_t T, int64_t K, int64_t ld, bool norm,
                       const float* gamma_f, float eps, const float* static_scale, int8_t* xq,
                       float* xscale, float* rrow, hipStream_t st);
-// per-token FP8 E4M3 codes, step amax / 448
+// FP8 E4M3 codes; static_scale NULL: per-token step amax / 448, else the
+// device scalar per-tensor step (quotients clip to +-448)
 void launch_quant_act_fp8(const void* x, bool bf16, int64_t T, int64_t K, int64_t ld, bool norm,
-                          const float* gamma_f, float eps, uint8_t* xq, float* xscale, float* rrow,
-                          hipStream_t st);
-void launch_static_scale(const float* a, const float* gamma_f, int64_t K, float* out,
+                          const float* gamma_f, float eps, const float* static_scale, uint8_t* xq,
+                          float* xscale, float* rrow, hipStream_t st);
+// out[0] = max_j fp32(a[j] * |gamma_f[j]|) / qmax
+void launch_static_scale(const float* a, const float* gamma_f, int64_t K, float qmax, float* out,
                          hipStream_t st);
 
 // k_gemm.hip / k_gemm_decode.hip; out: 0 = bf16, 1 = fp32, 2 = int32 accumulators

@@ -183,8 +183,31 @@ sq_status sq_quant_act_fp8(const void* x, sq_dtype x_dt, int64_t t, int64_t k, i
   if (xq == nullptr || x_scale == nullptr) return SQ_ERR_NULL;
   if (!aligned16(xq)) return SQ_ERR_UNSUPPORTED;
   if (t == 0) return SQ_OK;
-  sqk::launch_quant_act_fp8(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps, xq,
-                            x_scale, norm == SQ_NORM_RMS ? row_rscale : nullptr, stream);
+  sqk::launch_quant_act_fp8(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps,
+                            nullptr, xq, x_scale, norm == SQ_NORM_RMS ? row_rscale : nullptr,
+                            stream);
+  return hip_status();
+}
+
+sq_status sq_act_static_scale_fp8(const float* a, const float* gamma_f, int64_t k,
+                                  float* x_scale_static, hipStream_t stream) {
+  SQ_TRY(check_k(k));
+  if (a == nullptr || x_scale_static == nullptr) return SQ_ERR_NULL;
+  sqk::launch_static_scale(a, gamma_f, k, 448.0f, x_scale_static, stream);
+  return hip_status();
+}
+
+sq_status sq_quant_act_static_fp8(const void* x, sq_dtype x_dt, int64_t t, int64_t k,
+                                  int64_t ldx, sq_norm norm, const float* gamma_f, float eps,
+                                  const float* x_scale_static, uint8_t* xq, float* x_scale,
+                                  float* row_rscale, hipStream_t stream) {
+  SQ_TRY(check_act(x, x_dt, t, k, ldx, norm, eps));
+  if (x_scale_static == nullptr || xq == nullptr || x_scale == nullptr) return SQ_ERR_NULL;
+  if (!aligned16(xq)) return SQ_ERR_UNSUPPORTED;
+  if (t == 0) return SQ_OK;
+  sqk::launch_quant_act_fp8(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps,
+                            x_scale_static, xq, x_scale,
+                            norm == SQ_NORM_RMS ? row_rscale : nullptr, stream);
   return hip_status();
 }
 
@@ -217,7 +240,7 @@ sq_status sq_act_static_scale(const float* a, const float* gamma_f, int64_t k,
                               float* x_scale_static, hipStream_t stream) {
   SQ_TRY(check_k(k));
   if (a == nullptr || x_scale_static == nullptr) return SQ_ERR_NULL;
-  sqk::launch_static_scale(a, gamma_f, k, x_scale_static, stream);
+  sqk::launch_static_scale(a, gamma_f, k, 127.0f, x_scale_static, stream);
   return hip_status();
 }
 
@@ -256,7 +279,8 @@ size_t sq_linear_workspace_bytes(int64_t t, int64_t k) {
 
 namespace {
 
-// the forward of sq_w8a8_linear (static_scale NULL) and sq_w8a8_linear_static
+// the forward of sq_w8a8_linear (static_scale NULL), sq_w8a8_linear_static and
+// their FP8 forms (fp8)
 sq_status linear_impl(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
                       sq_norm norm, const float* gamma_f, float eps, const float* static_scale,
                       bool fp8, const int8_t* wq, const float* w_scale, int64_t n,
@@ -281,7 +305,7 @@ sq_status linear_impl(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_
   SQ_TRY(check_gemm(xq, xs, t, k, wq, w_scale, n, y, y_dt, ldy, acc));
   if (fp8)
     sqk::launch_quant_act_fp8(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps,
-                              reinterpret_cast<uint8_t*>(xq), xs,
+                              static_scale, reinterpret_cast<uint8_t*>(xq), xs,
                               norm == SQ_NORM_RMS ? rrow : nullptr, stream);
   else
     sqk::launch_quant_act(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps,
@@ -331,6 +355,19 @@ sq_status sq_w8a8_linear_static(const void* x, sq_dtype x_dt, int64_t t, int64_t
   if (x_scale_static == nullptr) return SQ_ERR_NULL;
   return linear_impl(x, x_dt, t, k, ldx, norm, gamma_f, eps, x_scale_static, false, wq, w_scale,
                      n, bias, y, y_dt, ldy, workspace, ws_bytes, dbg, stream);
+}
+
+sq_status sq_w8a8_linear_static_fp8(const void* x, sq_dtype x_dt, int64_t t, int64_t k,
+                                    int64_t ldx, sq_norm norm, const float* gamma_f, float eps,
+                                    const float* x_scale_static, const uint8_t* wq,
+                                    const float* w_scale, int64_t n, const float* bias, void* y,
+                                    sq_dtype y_dt, int64_t ldy, void* workspace,
+                                    size_t ws_bytes, const sq_debug_out* dbg,
+                                    hipStream_t stream) {
+  if (x_scale_static == nullptr) return SQ_ERR_NULL;
+  return linear_impl(x, x_dt, t, k, ldx, norm, gamma_f, eps, x_scale_static, true,
+                     reinterpret_cast<const int8_t*>(wq), w_scale, n, bias, y, y_dt, ldy,
+                     workspace, ws_bytes, dbg, stream);
 }
 
 }  // extern "C"
