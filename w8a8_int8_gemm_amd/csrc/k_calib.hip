@@ -1,9 +1,12 @@
 // k_calib.hip -- calibration kernels for gfx950.
 //
-//  * k_col_absmax: out[c] = max(out[c], max_r |M[r, c] * rs[r]|) over a
-//    row-major matrix -- the per-input-channel activation absmax over
-//    calibration tokens ("Taming the Outliers", System Architecture step C2)
-//    and, with rs = s, the per-output-channel absmax of the smoothed weight.
+//  * k_col_absmax: out[c] = max(out[c], max_r |M[r, c] * rs[r]| / qdiv) over
+//    a row-major matrix -- the per-input-channel activation absmax over
+//    calibration tokens ("Taming the Outliers", System Architecture step C2,
+//    qdiv = 1) and, with rs = s, the per-output-channel step of the smoothed
+//    weight (qdiv = 127 or 448).  Division by a positive constant rounds
+//    monotonically, so the maximum of the rounded quotients is the rounded
+//    quotient of the maximum: the step comes out exact with no extra pass.
 //  * k_rms_act_absmax: the same absmax taken of an RMSNorm output computed on
 //    the fly (the smoothed linears read a norm's output: "SmoothQuant and
 //    W8A8", The trick).
@@ -33,7 +36,7 @@ template <class In, bool kRowScale, int U>
 __global__ __launch_bounds__(256) void k_col_absmax(const typename In::elem* __restrict__ m,
                                                     int64_t rows, int64_t cols, int64_t ld,
                                                     const float* __restrict__ rs,
-                                                    float* __restrict__ out) {
+                                                    float qdiv, float* __restrict__ out) {
   __shared__ float red[4][512];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -81,8 +84,8 @@ __global__ __launch_bounds__(256) void k_col_absmax(const typename In::elem* __r
     const int c = threadIdx.x + h * 256;
     const int64_t col = (int64_t)blockIdx.x * 512 + c;
     if (col < cols) {
-      float v = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
-      atomic_max_nonneg(out + col, v);
+      const float v = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
+      atomic_max_nonneg(out + col, v / qdiv);
     }
   }
 }
@@ -231,24 +234,24 @@ static int col_absmax_grid_y(int64_t rows, int64_t gx) {
 }
 
 void launch_col_absmax(const void* m, bool bf16, int64_t rows, int64_t cols, int64_t ld,
-                       const float* rs, float* out, hipStream_t st) {
+                       const float* rs, float qdiv, float* out, hipStream_t st) {
   if (rows <= 0 || cols <= 0) return;
   const int64_t gx = (cols + 511) / 512;
   const dim3 grid((unsigned)gx, (unsigned)col_absmax_grid_y(rows, gx));
   if (bf16) {
     if (rs)
       hipLaunchKernelGGL((k_col_absmax<Bf16In, true, 8>), grid, dim3(256), 0, st,
-                         (const uint16_t*)m, rows, cols, ld, rs, out);
+                         (const uint16_t*)m, rows, cols, ld, rs, qdiv, out);
     else
       hipLaunchKernelGGL((k_col_absmax<Bf16In, false, 8>), grid, dim3(256), 0, st,
-                         (const uint16_t*)m, rows, cols, ld, rs, out);
+                         (const uint16_t*)m, rows, cols, ld, rs, qdiv, out);
   } else {
     if (rs)
       hipLaunchKernelGGL((k_col_absmax<F32In, true, 4>), grid, dim3(256), 0, st,
-                         (const float*)m, rows, cols, ld, rs, out);
+                         (const float*)m, rows, cols, ld, rs, qdiv, out);
     else
       hipLaunchKernelGGL((k_col_absmax<F32In, false, 4>), grid, dim3(256), 0, st,
-                         (const float*)m, rows, cols, ld, rs, out);
+                         (const float*)m, rows, cols, ld, rs, qdiv, out);
   }
 }
 

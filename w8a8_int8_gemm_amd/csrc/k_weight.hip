@@ -6,13 +6,13 @@
 //    The trick).
 //  * k_fold_w: W^[j, n] = W[j, n] * s_j -- s folded into the weight's input
 //    rows ("06 -- SmoothQuant", section 2).
-//  * k_div_const: Delta_n = amax_n / 127 (the symmetric 8-bit step, "Taming
-//    the Outliers", The Problem), or amax_n / 448 for FP8 E4M3.
 //  * k_quant_weight_t: codes = round-half-even(W^ / Delta_n) (INT8, or the
 //    nearest E4M3 value for FP8), written transposed to the [N, K]
 //    K-contiguous layout the GEMM streams.
-// The per-output-channel absmax between fold and quant is k_col_absmax with
-// the row scale s (k_calib.hip), so W^ is never materialised.
+// The per-output-channel step between fold and quant is k_col_absmax with the
+// row scale s and the divisor 127 (the symmetric 8-bit step, "Taming the
+// Outliers", The Problem) or 448 (FP8 E4M3), in k_calib.hip, so W^ is never
+// materialised.
 #include "sq_common.h"
 #include "sq_internal.h"
 
@@ -46,12 +46,6 @@ __global__ __launch_bounds__(256) void k_fold_w(const typename In::elem* __restr
   }
   *reinterpret_cast<f32x4*>(wout + j * N + n0) = o0;
   *reinterpret_cast<f32x4*>(wout + j * N + n0 + 4) = o1;
-}
-
-// Delta_n = amax_n / qmax: 127 for INT8, 448 (the largest finite E4M3) for FP8
-__global__ void k_div_const(float* __restrict__ p, int64_t n, float qmax) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = p[i] / qmax;
 }
 
 // Tile of 128 input channels (k) x 64 output channels (n).  Thread (tx, ty),
@@ -167,11 +161,6 @@ void launch_fold_w(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, c
                        wout);
   else
     hipLaunchKernelGGL(k_fold_w<F32In>, grid, dim3(256), 0, st, (const float*)w, K, N, ld, s, wout);
-}
-
-void launch_div_const(float* p, int64_t n, float qmax, hipStream_t st) {
-  if (n <= 0) return;
-  hipLaunchKernelGGL(k_div_const, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, qmax);
 }
 
 template <bool F8>

@@ -9,8 +9,9 @@ namespace sqk {
 
 // k_calib.hip
 void launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
+// out[c] = max(out[c], max_r |m[r,c] * row_scale[r]| / qdiv) (row_scale NULL = 1)
 void launch_col_absmax(const void* m, bool bf16, int64_t rows, int64_t cols, int64_t ld,
-                       const float* row_scale, float* out, hipStream_t st);
+                       const float* row_scale, float qdiv, float* out, hipStream_t st);
 void launch_rms_act_absmax(const void* h, bool bf16, int64_t rows, int64_t K, int64_t ld,
                            const float* gamma, float eps, float* out, hipStream_t st);
 void launch_wrow_absmax_s(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
@@ -20,7 +21,6 @@ void launch_wrow_absmax_s(const void* w, bool bf16, int64_t K, int64_t N, int64_
 void launch_fold_gamma(const float* s, const float* gamma, float* gout, int64_t K, hipStream_t st);
 void launch_fold_w(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, const float* s,
                    float* wout, hipStream_t st);
-void launch_div_const(float* p, int64_t n, float qmax, hipStream_t st);
 void launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
                            const float* s, const float* wscale, int8_t* wq, hipStream_t st);
 void launch_quant_weight_t_fp8(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,

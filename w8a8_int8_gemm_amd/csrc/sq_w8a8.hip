@@ -125,7 +125,7 @@ sq_status sq_calibrate(const void* x_cal, sq_dtype x_dt, int64_t t_cal, int64_t 
     if (norm == SQ_NORM_RMS)
       sqk::launch_rms_act_absmax(x_cal, x_dt == SQ_BF16, t_cal, k, ldx, gamma, eps, a, stream);
     else
-      sqk::launch_col_absmax(x_cal, x_dt == SQ_BF16, t_cal, k, ldx, nullptr, a, stream);
+      sqk::launch_col_absmax(x_cal, x_dt == SQ_BF16, t_cal, k, ldx, nullptr, 1.0f, a, stream);
   }
   if (w != nullptr)
     sqk::launch_wrow_absmax_s(w, w_dt == SQ_BF16, k, n, ldw, a, alpha, wmax, s, stream);
@@ -156,8 +156,7 @@ sq_status sq_quant_weight(const void* w, sq_dtype w_dt, int64_t k, int64_t n, in
   if (n % 8 != 0 || !aligned16(wq)) return SQ_ERR_UNSUPPORTED;
   if (n == 0) return SQ_OK;
   sqk::launch_fill_f32(w_scale, n, 0.0f, stream);
-  sqk::launch_col_absmax(w, w_dt == SQ_BF16, k, n, ldw, s, w_scale, stream);
-  sqk::launch_div_const(w_scale, n, 127.0f, stream);
+  sqk::launch_col_absmax(w, w_dt == SQ_BF16, k, n, ldw, s, 127.0f, w_scale, stream);
   sqk::launch_quant_weight_t(w, w_dt == SQ_BF16, k, n, ldw, s, w_scale, wq, stream);
   return hip_status();
 }
@@ -170,8 +169,7 @@ sq_status sq_quant_weight_fp8(const void* w, sq_dtype w_dt, int64_t k, int64_t n
   if (n % 8 != 0 || !aligned16(wq)) return SQ_ERR_UNSUPPORTED;
   if (n == 0) return SQ_OK;
   sqk::launch_fill_f32(w_scale, n, 0.0f, stream);
-  sqk::launch_col_absmax(w, w_dt == SQ_BF16, k, n, ldw, s, w_scale, stream);
-  sqk::launch_div_const(w_scale, n, 448.0f, stream);
+  sqk::launch_col_absmax(w, w_dt == SQ_BF16, k, n, ldw, s, 448.0f, w_scale, stream);
   sqk::launch_quant_weight_t_fp8(w, w_dt == SQ_BF16, k, n, ldw, s, w_scale, wq, stream);
   return hip_status();
 }
