@@ -64,6 +64,11 @@ def _load():
         _lib.oracle_static_scale_fp8.argtypes = [P, I, I64, I64, I64, I, F, P]
         _lib.oracle_static_scale_fp8.restype = F
         _lib.oracle_quant_act_static_fp8.argtypes = [P, I, I64, I64, I64, I, P, F, P, F, P, P, P]
+        _lib.oracle_ln_stats.argtypes = [P, I, I64, I64, I64, F, P, P]
+        _lib.oracle_act_absmax_ln.argtypes = [P, I, I64, I64, I64, P, P, F, P]
+        _lib.oracle_fold_ln.argtypes = [P, I64, P, P, P, P]
+        _lib.oracle_quant_act_ln.argtypes = [P, I, I64, I64, I64, P, P, F, P, P, P, P, P, P]
+        _lib.oracle_fold_prev.argtypes = [P, I64, P, I, I64, I64, P, P, P]
         _lib.oracle_e4m3_encode_array.argtypes = [P, I64, P]
         _lib.oracle_e4m3_decode_array.argtypes = [P, I64, P]
         _lib.oracle_quant_weight_fp8.argtypes = [P, I64, I64, I64, P, P]
@@ -375,6 +380,92 @@ def linear_static(x, delta, gamma_f, qw, w_scale, bias=None, *, norm=False, r=No
     acc = int_gemm(q, qw)
     y = epilogue(acc, xs, w_scale, bias)
     return dict(q=q, x_scale=xs, r=rr, acc=acc, y32=y, y=to_bf16(y) if out_bf16 else y)
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm form and the fold into the previous linear
+# ---------------------------------------------------------------------------
+
+def ln_stats(h: np.ndarray, eps: float = 1e-6):
+    """(mean [T], r [T]) fp32: LayerNorm row mean and 1/sqrt(var + eps)."""
+    h, bf = _mat(h)
+    T, K = h.shape
+    m, r = np.empty(T, np.float32), np.empty(T, np.float32)
+    _load().oracle_ln_stats(_p(h), bf, T, K, K, float(eps), _p(m), _p(r))
+    return m, r
+
+
+def act_absmax_ln(h: np.ndarray, gamma=None, beta=None, eps: float = 1e-6) -> np.ndarray:
+    """Per-channel absmax of LN(h) with the norm's own gamma and beta."""
+    h, bf = _mat(h)
+    T, K = h.shape
+    a = np.empty(K, np.float32)
+    _load().oracle_act_absmax_ln(_p(h), bf, T, K, K, _p(_f32(gamma)), _p(_f32(beta)),
+                                 float(eps), _p(a))
+    return a
+
+
+def fold_ln(s: np.ndarray, gamma=None, beta=None):
+    """(gamma' = gamma/s, beta' = beta/s)."""
+    s = _f32(s)
+    K = s.shape[0]
+    gout, bout = np.empty(K, np.float32), np.empty(K, np.float32)
+    _load().oracle_fold_ln(_p(s), K, _p(_f32(gamma)), _p(_f32(beta)), _p(gout), _p(bout))
+    return gout, bout
+
+
+def quant_act_ln(h: np.ndarray, gamma_f=None, beta_f=None, *, mean=None, r=None,
+                 eps: float = 1e-6):
+    """(q [T,K] int8, x_scale [T], mean [T], r [T]) of the smoothed LayerNorm output."""
+    h, bf = _mat(h)
+    T, K = h.shape
+    q = np.empty((T, K), np.int8)
+    xs = np.empty(T, np.float32)
+    mo, ro = np.empty(T, np.float32), np.empty(T, np.float32)
+    _load().oracle_quant_act_ln(_p(h), bf, T, K, K, _p(_f32(mean)), _p(_f32(r)), float(eps),
+                                _p(_f32(gamma_f)), _p(_f32(beta_f)), _p(q), _p(xs), _p(mo),
+                                _p(ro))
+    return q, xs, mo, ro
+
+
+def linear_ln(h, gamma_f, beta_f, qw, w_scale, bias=None, *, mean=None, r=None, eps=1e-6,
+              out_bf16=True):
+    """The online forward behind a smoothed LayerNorm."""
+    q, xs, mo, ro = quant_act_ln(h, gamma_f, beta_f, mean=mean, r=r, eps=eps)
+    acc = int_gemm(q, qw)
+    y = epilogue(acc, xs, w_scale, bias)
+    return dict(q=q, x_scale=xs, mean=mo, r=ro, acc=acc, y32=y, y=to_bf16(y) if out_bf16 else y)
+
+
+def fold_prev(s: np.ndarray, w_prev: np.ndarray, bias=None):
+    """(W_prev [K_prev, K] with column j divided by s_j as fp32, bias / s or None)."""
+    s = _f32(s)
+    K = s.shape[0]
+    wp, bf = _mat(w_prev)
+    K_prev = wp.shape[0]
+    assert wp.shape[1] == K
+    wout = np.empty((K_prev, K), np.float32)
+    bout = None if bias is None else np.empty(K, np.float32)
+    _load().oracle_fold_prev(_p(s), K, _p(wp), bf, K_prev, K, _p(wout), _p(_f32(bias)), _p(bout))
+    return wout, bout
+
+
+def reference_ln_fp64(h, w, bias=None, *, gamma=None, beta=None, eps=1e-6) -> np.ndarray:
+    """Unsmoothed, unquantized LayerNorm -> linear in fp64."""
+    hf = (h.astype(np.uint32) << 16).view(np.float32) if h.dtype == np.uint16 else h
+    wf = (w.astype(np.uint32) << 16).view(np.float32) if w.dtype == np.uint16 else w
+    X = hf.astype(np.float64)
+    mu = X.mean(axis=1, keepdims=True)
+    var = ((X - mu) ** 2).mean(axis=1, keepdims=True)
+    X = (X - mu) / np.sqrt(var + float(np.float32(eps)))
+    if gamma is not None:
+        X = X * np.asarray(gamma, np.float64)[None, :]
+    if beta is not None:
+        X = X + np.asarray(beta, np.float64)[None, :]
+    Y = X @ wf.astype(np.float64)
+    if bias is not None:
+        Y = Y + np.asarray(bias, np.float64)[None, :]
+    return Y
 
 
 def reference_fp64(x, w, bias=None, *, norm=False, gamma=None, eps=1e-6) -> np.ndarray:

@@ -41,6 +41,14 @@
  *                  (448 is E4M3's largest finite value), code = the E4M3
  *                  value nearest fp32(x / step), ties to even; products summed
  *                  exactly (fp64) in place of the int64 sum.
+ *   ln_*           the LayerNorm form of the smoothed norm ("SmoothQuant:
+ *                  Weight-Only vs W8A8", Integration with Transformers: S^-1
+ *                  folds into the LayerNorm's gamma and beta).  The pages give
+ *                  no formula: mean and variance over the row in fp64,
+ *                  r = 1/sqrt(var + eps), LN(h) = fp32(fp32(fp32(h - mean) * r)
+ *                  * gamma) + beta, every step rounded to fp32.
+ *   fold_prev      1/s folded into the output columns of the linear in front
+ *                  ("06 -- SmoothQuant", section 7).
  *   int_gemm       acc = sum_k q[t,k] * qw[n,k] in int64 ("06 -- SmoothQuant",
  *                  section 7: INT8 x INT8 -> INT32).
  *   epilogue       y = (Delta_t * Delta_n) * acc + bias ("06 -- SmoothQuant",
@@ -433,6 +441,116 @@ void oracle_gemm_fp8(const uint8_t *q, const uint8_t *qw, int64_t T, int64_t K, 
       for (int64_t k = 0; k < K; ++k) s += lut[q[t * K + k]] * lut[qw[n * K + k]];
       acc[t * N + n] = s;
     }
+}
+
+/* ---------------------------------------------------------------------------
+ * LayerNorm form ("SmoothQuant: Weight-Only vs W8A8", Integration with
+ * Transformers) and the fold into the previous linear ("06 -- SmoothQuant",
+ * section 7).
+ * ------------------------------------------------------------------------- */
+
+/* Row statistics: mean[t] = fp32(mu), r[t] = fp32(1 / sqrt(var + eps)) with
+   mu = (sum_k h) / K and var = (sum_k (h - mu)^2) / K, both sums in fp64 in
+   index order (mu kept in fp64 for the variance). */
+void oracle_ln_stats(const void *h, int is_bf16, int64_t T, int64_t K, int64_t ld, float eps,
+                     float *mean, float *r) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double s1 = 0.0;
+    for (int64_t k = 0; k < K; ++k) s1 += (double)elem(h, is_bf16, t * ld + k);
+    const double mu = s1 / (double)K;
+    double s2 = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const double d = (double)elem(h, is_bf16, t * ld + k) - mu;
+      s2 += d * d;
+    }
+    mean[t] = (float)mu;
+    r[t] = (float)(1.0 / sqrt(s2 / (double)K + (double)eps));
+  }
+}
+
+/* one LayerNorm output element with per-channel gamma, beta (NULL: 1, 0) */
+static float ln_elem(float h, float m, float r, const float *gamma, const float *beta, int64_t k) {
+  const float c = h - m;
+  const float n = c * r;
+  const float g = n * (gamma ? gamma[k] : 1.0f);
+  return g + (beta ? beta[k] : 0.0f);
+}
+
+/* a[j] = max_t |LN(h)[t,j]| with the norm's own gamma and beta: the
+   calibration absmax of the linear's input in LayerNorm mode. */
+void oracle_act_absmax_ln(const void *h, int is_bf16, int64_t T, int64_t K, int64_t ld,
+                          const float *gamma, const float *beta, float eps, float *a) {
+  float *m = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1));
+  float *r = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1));
+  oracle_ln_stats(h, is_bf16, T, K, ld, eps, m, r);
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < K; ++j) {
+    float mx = 0.0f;
+    for (int64_t t = 0; t < T; ++t)
+      mx = fmaxf(mx, fabsf(ln_elem(elem(h, is_bf16, t * ld + j), m[t], r[t], gamma, beta, j)));
+    a[j] = mx;
+  }
+  free(m);
+  free(r);
+}
+
+/* gamma'_j = fp32(gamma_j / s_j), beta'_j = fp32(beta_j / s_j) (NULL gamma:
+   1; NULL beta: beta' = 0) */
+void oracle_fold_ln(const float *s, int64_t K, const float *gamma, const float *beta,
+                    float *gamma_out, float *beta_out) {
+  for (int64_t j = 0; j < K; ++j) {
+    gamma_out[j] = (gamma ? gamma[j] : 1.0f) / s[j];
+    beta_out[j] = (beta ? beta[j] : 0.0f) / s[j];
+  }
+}
+
+/* Per-token dynamic symmetric INT8 of the smoothed LayerNorm output
+   x^ = LN(h; gamma_f, beta_f); mean/r from mean_in/r_in if given, else as in
+   oracle_ln_stats; mean_out/r_out (nullable) receive them. */
+void oracle_quant_act_ln(const void *h, int is_bf16, int64_t T, int64_t K, int64_t ld,
+                         const float *mean_in, const float *r_in, float eps,
+                         const float *gamma_f, const float *beta_f, int8_t *q, float *x_scale,
+                         float *mean_out, float *r_out) {
+  float *m = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1));
+  float *r = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1));
+  oracle_ln_stats(h, is_bf16, T, K, ld, eps, m, r);
+  if (mean_in) memcpy(m, mean_in, sizeof(float) * (size_t)T);
+  if (r_in) memcpy(r, r_in, sizeof(float) * (size_t)T);
+  if (mean_out) memcpy(mean_out, m, sizeof(float) * (size_t)T);
+  if (r_out) memcpy(r_out, r, sizeof(float) * (size_t)T);
+#pragma omp parallel
+  {
+    float *xh = (float *)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      float amax = 0.0f;
+      for (int64_t k = 0; k < K; ++k) {
+        xh[k] = ln_elem(elem(h, is_bf16, t * ld + k), m[t], r[t], gamma_f, beta_f, k);
+        amax = fmaxf(amax, fabsf(xh[k]));
+      }
+      const float d = amax / 127.0f;
+      x_scale[t] = d;
+      for (int64_t k = 0; k < K; ++k)
+        q[t * K + k] = (d == 0.0f) ? (int8_t)0 : code_of(xh[k] / d);
+    }
+    free(xh);
+  }
+  free(m);
+  free(r);
+}
+
+/* The previous linear's output channel j is the next linear's input channel
+   j: w_out[i, j] = fp32(W_prev[i, j] / s_j) for W_prev [K_prev, K] (leading
+   dimension ld, output [K_prev, K] dense) and bias_out[j] = fp32(b_j / s_j)
+   (bias NULL: bias_out untouched). */
+void oracle_fold_prev(const float *s, int64_t K, const void *w_prev, int is_bf16, int64_t K_prev,
+                      int64_t ld, float *w_out, const float *bias, float *bias_out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < K_prev; ++i)
+    for (int64_t j = 0; j < K; ++j) w_out[i * K + j] = elem(w_prev, is_bf16, i * ld + j) / s[j];
+  if (bias && bias_out)
+    for (int64_t j = 0; j < K; ++j) bias_out[j] = bias[j] / s[j];
 }
 
 /* acc[t,n] = sum_k q[t,k] * qw[n,k] in int64; q is [T,K], qw is [N,K].

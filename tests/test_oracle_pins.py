@@ -631,3 +631,116 @@ def test_static_fp8_zero_step_gives_zero_codes():
     assert d == 0.0
     q, xs, _ = oracle.quant_act_static_fp8(np.ones((2, 64), np.float32), d)
     assert not q.any() and not xs.any()
+
+
+# LayerNorm form of the smoothed norm ("SmoothQuant: Weight-Only vs W8A8",
+# Integration with Transformers: S^-1 folds into gamma and beta) and the fold
+# into the previous linear's output columns ("06 -- SmoothQuant", section 7)
+
+def _ln_rows(seed, T=24, K=320, shift=3.0):
+    rng = np.random.default_rng(seed)
+    h = (rng.standard_normal((T, K)) + shift * rng.standard_normal((T, 1))).astype(np.float32)
+    h[:, 11] *= 20
+    return h
+
+
+def test_ln_stats_against_exact_sums():
+    h = _ln_rows(40)
+    m, r = oracle.ln_stats(h, eps=1e-5)
+    for t in range(h.shape[0]):
+        row = [float(v) for v in h[t]]
+        mu = math.fsum(row) / len(row)                       # correctly rounded sum
+        var = math.fsum((v - mu) ** 2 for v in row) / len(row)
+        assert abs(float(m[t]) - mu) <= abs(mu) * 2 ** -23 + 1e-12
+        rr = 1.0 / math.sqrt(var + float(F32(1e-5)))
+        assert abs(float(r[t]) - rr) <= rr * 2 ** -23
+
+
+def test_ln_absmax_against_torch_layer_norm():
+    torch = pytest.importorskip("torch")
+    h = _ln_rows(41)
+    rng = np.random.default_rng(42)
+    g = rng.uniform(0.5, 1.5, h.shape[1]).astype(np.float32)
+    b = rng.uniform(-0.3, 0.3, h.shape[1]).astype(np.float32)
+    a = oracle.act_absmax_ln(h, g, b, eps=1e-5)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(h.astype(np.float64)), (h.shape[1],),
+                                         torch.from_numpy(g.astype(np.float64)),
+                                         torch.from_numpy(b.astype(np.float64)),
+                                         eps=float(F32(1e-5))).abs().max(dim=0).values.numpy()
+    np.testing.assert_allclose(a, ref, rtol=4 * 2 ** -23, atol=1e-6)
+
+
+def test_ln_fold_invariance_and_alpha_one():
+    h = _ln_rows(43)
+    K = h.shape[1]
+    rng = np.random.default_rng(44)
+    g = rng.uniform(0.5, 1.5, K).astype(np.float32)
+    b = rng.uniform(-0.3, 0.3, K).astype(np.float32)
+    w = (rng.standard_normal((K, 48)) * 0.02).astype(np.float32)
+    a = oracle.act_absmax_ln(h, g, b)
+    s = oracle.smooth_factor(a, oracle.weight_absmax(w), 0.5)
+    gp, bp = oracle.fold_ln(s, g, b)
+    _, what = oracle.fold(s, None, w)
+    # (LN(h) * gamma/s + beta/s) diag(s) W = (LN(h) * gamma + beta) W, fp64 with the fp32 tensors
+    n = (h - h.mean(1, keepdims=True)) / np.sqrt(h.astype(np.float64).var(1, keepdims=True) + 1e-6)
+    lhs = (n * gp.astype(np.float64) + bp.astype(np.float64)) @ what.astype(np.float64)
+    rhs = (n * g.astype(np.float64) + b.astype(np.float64)) @ w.astype(np.float64)
+    assert np.abs(lhs - rhs).max() <= 1e-5 * np.abs(rhs).max()
+    # alpha = 1: s = a, every smoothed channel then peaks at 1 (up to the roundings)
+    s1 = oracle.smooth_factor(a, oracle.weight_absmax(w), 1.0)
+    np.testing.assert_array_equal(s1, a)
+    g1, b1 = oracle.fold_ln(s1, g, b)
+    np.testing.assert_allclose(oracle.act_absmax_ln(h, g1, b1), 1.0, rtol=4 * 2 ** -23)
+
+
+def test_quant_act_ln_reduces_to_rms_on_zero_mean_rows():
+    # rows built of +-v pairs have an exactly zero mean: LayerNorm with beta = 0
+    # is then the RMSNorm form, whose quantizer is pinned above
+    rng = np.random.default_rng(45)
+    half = rng.standard_normal((16, 160)).astype(np.float32)
+    half[:, 3] *= 25
+    h = np.empty((16, 320), np.float32)
+    h[:, 0::2], h[:, 1::2] = half, -half
+    g = rng.uniform(0.5, 1.5, 320).astype(np.float32)
+    q, xs, m, r = oracle.quant_act_ln(h, g, None)
+    assert not m.any()
+    qr, xr, rr = oracle.quant_act(h, g, norm=True)
+    np.testing.assert_array_equal(r, rr)
+    np.testing.assert_array_equal(xs, xr)
+    np.testing.assert_array_equal(q, qr)
+
+
+def test_quant_act_ln_half_step_bound():
+    torch = pytest.importorskip("torch")
+    h = _ln_rows(46)
+    rng = np.random.default_rng(47)
+    g = rng.uniform(0.2, 1.5, h.shape[1]).astype(np.float32)
+    b = rng.uniform(-0.5, 0.5, h.shape[1]).astype(np.float32)
+    q, xs, _, _ = oracle.quant_act_ln(h, g, b)
+    ln = torch.nn.functional.layer_norm(torch.from_numpy(h.astype(np.float64)), (h.shape[1],),
+                                        torch.from_numpy(g.astype(np.float64)),
+                                        torch.from_numpy(b.astype(np.float64)),
+                                        eps=float(F32(1e-6))).numpy()
+    np.testing.assert_allclose(xs, np.abs(ln).max(1) / 127, rtol=8 * 2 ** -23)
+    err = np.abs(ln - q.astype(np.float64) * xs[:, None].astype(np.float64))
+    assert np.all(err <= xs[:, None] * (0.5 + 1e-4))
+    assert np.abs(q).max() == 127 and q.min() >= -127
+
+
+def test_fold_prev_invariance_and_exact_powers_of_two():
+    rng = np.random.default_rng(48)
+    Kp, K, N, T = 96, 128, 40, 12
+    x = rng.standard_normal((T, Kp))
+    wp = (rng.standard_normal((Kp, K)) * 0.05).astype(np.float32)
+    bp = rng.standard_normal(K).astype(np.float32)
+    w = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    s = rng.uniform(0.05, 20, K).astype(np.float32)
+    wpf, bpf = oracle.fold_prev(s, wp, bp)
+    _, what = oracle.fold(s, None, w)
+    lhs = (x @ wpf.astype(np.float64) + bpf.astype(np.float64)) @ what.astype(np.float64)
+    rhs = (x @ wp.astype(np.float64) + bp.astype(np.float64)) @ w.astype(np.float64)
+    assert np.abs(lhs - rhs).max() <= 1e-5 * np.abs(rhs).max()
+    s2 = np.exp2(rng.integers(-6, 7, K)).astype(np.float32)
+    wq2, bq2 = oracle.fold_prev(s2, wp, bp)
+    np.testing.assert_array_equal(wq2.astype(np.float64) * s2[None, :], wp.astype(np.float64))
+    np.testing.assert_array_equal(bq2.astype(np.float64) * s2, bp.astype(np.float64))
