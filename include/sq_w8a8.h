@@ -289,6 +289,61 @@ sq_status sq_w8a8_linear_static_fp8(const void *x, sq_dtype x_dt, int64_t t, int
                                     size_t ws_bytes, const sq_debug_out *dbg,
                                     hipStream_t stream);
 
+/*
+ * Whole-block integration: which linears are smoothed, and the two other
+ * places 1/s can be folded ("SmoothQuant and W8A8", The trick and Gotchas:
+ * the norm in front of q/k/v pairs with those three, the norm in front of the
+ * MLP with gate and up; the output and down projections are left unsmoothed
+ * and take plain per-token W8A8, i.e. s = NULL, gamma_f = NULL).  The linears a
+ * norm feeds share one s: pass their weights concatenated along n ([k, q+k+v]
+ * or [k, gate+up]), which also makes them one GEMM.
+ *
+ * LayerNorm form ("SmoothQuant: Weight-Only vs W8A8", Integration with
+ * Transformers: S^-1 folds into the LayerNorm's gamma and beta).  The pages
+ * give no formula; here
+ *   m_t = fp32(mu_t), r_t = fp32(1 / sqrt(var_t + eps)), mu_t and var_t the
+ *         row's mean and mean squared deviation from mu_t, summed in fp64
+ *   LN(h)[t,j] = fp32( fp32( fp32(h - m_t) * r_t ) * gamma_j ) + beta_j  (fp32)
+ * sq_calibrate_ln: as sq_calibrate in norm mode with a[j] = max_t |LN(h)[t,j]|
+ *   under the norm's own gamma and beta (NULL = ones / zeros).  k <= 8192.
+ * sq_smooth_fold_ln: gamma_out[j] = fp32(gamma_j / s_j), beta_out[j] =
+ *   fp32(beta_j / s_j) (NULL gamma = ones, NULL beta = zeros); all outputs
+ *   required.
+ * sq_quant_act_ln: per-token INT8 of x^ = LN(h) with gamma' = gamma_f and
+ *   beta' = beta_f (both required, 16-byte aligned), as sq_quant_act
+ *   otherwise; row_mean / row_rscale (nullable) receive m_t and r_t.
+ * sq_w8a8_linear_ln: sq_quant_act_ln then sq_gemm_w8a8, as sq_w8a8_linear
+ *   (dbg->row_rscale receives r_t); row_mean (nullable) receives m_t.
+ *
+ * sq_fold_prev_linear: 1/s folded into the output columns of the linear whose
+ * output is this linear's input ("06 -- SmoothQuant", section 7):
+ *   w_out[i, j]  = fp32(W_prev[i, j] / s_j)   W_prev [k_prev, k] fp32 or bf16
+ *                                             (leading dimension ldw); w_out
+ *                                             fp32 [k_prev, k], leading
+ *                                             dimension ldo (multiple of 4)
+ *   bias_out[j]  = fp32(bias_j / s_j)          when bias != NULL
+ * The next linear then quantizes its input with gamma_f = NULL; W_prev' is
+ * quantized like any weight (sq_quant_weight with its own s or NULL).
+ */
+sq_status sq_calibrate_ln(const void *x_cal, sq_dtype x_dt, int64_t t_cal, int64_t k, int64_t ldx,
+                          const float *gamma, const float *beta, float eps, const void *w,
+                          sq_dtype w_dt, int64_t n, int64_t ldw, float alpha, unsigned flags,
+                          float *a, float *wmax, float *s, hipStream_t stream);
+sq_status sq_smooth_fold_ln(const float *s, int64_t k, const float *gamma, const float *beta,
+                            float *gamma_out, float *beta_out, hipStream_t stream);
+sq_status sq_quant_act_ln(const void *x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                          const float *gamma_f, const float *beta_f, float eps, int8_t *xq,
+                          float *x_scale, float *row_mean, float *row_rscale,
+                          hipStream_t stream);
+sq_status sq_w8a8_linear_ln(const void *x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                            const float *gamma_f, const float *beta_f, float eps,
+                            const int8_t *wq, const float *w_scale, int64_t n, const float *bias,
+                            void *y, sq_dtype y_dt, int64_t ldy, void *workspace, size_t ws_bytes,
+                            const sq_debug_out *dbg, float *row_mean, hipStream_t stream);
+sq_status sq_fold_prev_linear(const float *s, int64_t k, const void *w_prev, sq_dtype w_dt,
+                              int64_t k_prev, int64_t ldw, float *w_out, int64_t ldo,
+                              const float *bias, float *bias_out, hipStream_t stream);
+
 /* Static description of a status code (host memory, never NULL). */
 const char *sq_status_string(sq_status status);
 

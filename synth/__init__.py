@@ -78,6 +78,9 @@ class Workload:
     io_dtype: str = "bf16"              # activations/weights in, output out
     bias_sigma: float = 0.05
     alphas: tuple = ()                  # alpha sweep (reported)
+    layernorm: bool = False             # LayerNorm (gamma and beta) instead of RMSNorm
+    beta_sigma: float = 0.0             # LayerNorm beta ~ N(0, beta_sigma^2)
+    row_shift: float = 0.0              # per-token offset ~ N(0, row_shift^2) (LN removes it)
 
     def with_sizes(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -101,6 +104,12 @@ WORKLOADS = {
     "gate_up": Workload("gate_up", 104, T=4096, K=4096, N=28672, Tc=8192,
                         sigma_x=0.3, n_outliers=12, outlier_mult=30.0,
                         sigma_w=0.02, alpha=0.5),
+    # LayerNorm -> fused QKV: the LayerNorm form of the smoothed norm (its
+    # gamma and beta both take 1/s); tokens carry an offset the norm removes
+    "layernorm_qkv": Workload("layernorm_qkv", 106, T=2048, K=4096, N=6144, Tc=16384,
+                              sigma_x=1.0, n_outliers=16, outlier_mult=50.0,
+                              sigma_w=0.02, alpha=0.85, norm=True, gamma_range=(0.5, 1.5),
+                              layernorm=True, beta_sigma=0.1, row_shift=2.0),
     # decode-shaped GEMM plus a large calibration pass
     "decode": Workload("decode", 105, T=16, K=8192, N=8192, Tc=128 * 2048,
                        sigma_x=1.0, n_outliers=24, outlier_mult=60.0,
@@ -158,6 +167,7 @@ class Inputs:
     bias: np.ndarray              # [N] fp32
     outliers: np.ndarray
     meta: dict = field(default_factory=dict)
+    beta: Optional[np.ndarray] = None   # [K] fp32 LayerNorm bias, or None
 
     @property
     def io_bf16(self) -> bool:
@@ -182,6 +192,17 @@ def make_inputs(w: Workload, *, calib: bool = True, evaluation: bool = True,
     if w.norm:
         gamma = rng1.uniform(w.gamma_range[0], w.gamma_range[1], size=w.K).astype(np.float32)
 
+    beta = None
+    if w.layernorm:
+        beta = np.random.Generator(np.random.PCG64(st[6])).normal(
+            0.0, w.beta_sigma, size=w.K).astype(np.float32)
+    shift_rng = np.random.Generator(np.random.PCG64(st[7]))
+
+    def shifted(a):
+        if w.row_shift > 0 and a is not None:
+            a += shift_rng.normal(0.0, w.row_shift, size=(a.shape[0], 1)).astype(np.float32)
+        return a
+
     x_cal = None
     if calib or target is not None:
         x_cal = _gaussian_rows(st[2], w.Tc, w.K, w.sigma_x, threads)
@@ -193,10 +214,12 @@ def make_inputs(w: Workload, *, calib: bool = True, evaluation: bool = True,
         mults = np.full(len(outl), w.outlier_mult, dtype=np.float32)
     if x_cal is not None:
         x_cal[:, outl] *= mults
+        shifted(x_cal)
     x = None
     if evaluation:
         x = _gaussian_rows(st[3], w.T, w.K, w.sigma_x, threads)
         x[:, outl] *= mults
+        shifted(x)
     wt = _gaussian_rows(st[4], w.K, w.N, w.sigma_w, threads)
     bias = np.random.Generator(np.random.PCG64(st[5])).normal(0.0, w.bias_sigma, size=w.N).astype(np.float32)
 
@@ -207,4 +230,4 @@ def make_inputs(w: Workload, *, calib: bool = True, evaluation: bool = True,
     elif not calib:
         x_cal = None
     return Inputs(w, x_cal, x, wt, gamma, bias, outl,
-                  meta={"outlier_mult": mults.tolist()})
+                  meta={"outlier_mult": mults.tolist()}, beta=beta)

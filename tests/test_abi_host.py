@@ -182,6 +182,38 @@ def test_static_fp8_validation(L):
               sq.SQ_BF16, 8, None, 0, None, None) == sq.SQ_ERR_WORKSPACE
 
 
+def test_layernorm_and_fold_prev_validation(L):
+    c = L.sq_calibrate_ln
+    assert c(A16, sq.SQ_BF16, 8, 64, 64, None, None, 1e-6, None, sq.SQ_BF16, 0, 0, 0.5, 0,
+             None, None, None, None) == sq.SQ_ERR_NULL
+    assert c(A16, sq.SQ_BF16, 8, 16384, 16384, None, None, 1e-6, None, sq.SQ_BF16, 0, 0, 0.5, 0,
+             A16, None, None, None) == sq.SQ_ERR_UNSUPPORTED
+    assert c(A16, sq.SQ_BF16, 8, 64, 64, None, None, -1.0, None, sq.SQ_BF16, 0, 0, 0.5, 0,
+             A16, None, None, None) == sq.SQ_ERR_SHAPE
+    assert c(None, sq.SQ_BF16, 0, 64, 64, None, None, 1e-6, A16, sq.SQ_BF16, 8, 8, 1.5, 0,
+             A16, A16, A16, None) == sq.SQ_ERR_ALPHA
+    f = L.sq_smooth_fold_ln
+    assert f(A16, 64, None, None, A16, None, None) == sq.SQ_ERR_NULL
+    assert f(A16, 96, None, None, A16, A16, None) == sq.SQ_ERR_UNSUPPORTED
+    q = L.sq_quant_act_ln
+    assert q(A16, sq.SQ_BF16, 4, 64, 64, None, A16, 1e-6, A16, A16, None, None, None) == sq.SQ_ERR_NULL
+    assert q(A16, sq.SQ_BF16, 4, 64, 64, A16, None, 1e-6, A16, A16, None, None, None) == sq.SQ_ERR_NULL
+    assert q(A16, sq.SQ_BF16, 4, 64, 64, A16, MIS, 1e-6, A16, A16, None, None, None) == sq.SQ_ERR_UNSUPPORTED
+    assert q(A16, sq.SQ_BF16, 0, 64, 64, A16, A16, 1e-6, A16, A16, None, None, None) == sq.SQ_OK
+    lin = L.sq_w8a8_linear_ln
+    assert lin(A16, sq.SQ_BF16, 4, 64, 64, None, A16, 1e-6, A16, A16, 8, None, A16, sq.SQ_BF16, 8,
+               A16, 1 << 20, None, None, None) == sq.SQ_ERR_NULL
+    assert lin(A16, sq.SQ_BF16, 4, 64, 64, A16, A16, 1e-6, A16, A16, 8, None, A16, sq.SQ_BF16, 8,
+               None, 0, None, None, None) == sq.SQ_ERR_WORKSPACE
+    fp = L.sq_fold_prev_linear
+    assert fp(None, 64, A16, sq.SQ_BF16, 8, 64, A16, 64, None, None, None) == sq.SQ_ERR_NULL
+    assert fp(A16, 64, A16, sq.SQ_BF16, 8, 32, A16, 64, None, None, None) == sq.SQ_ERR_SHAPE
+    assert fp(A16, 64, A16, sq.SQ_BF16, 8, 64, A16, 62, None, None, None) == sq.SQ_ERR_SHAPE
+    assert fp(A16, 64, A16, sq.SQ_BF16, 8, 64, A16, 66, None, None, None) == sq.SQ_ERR_UNSUPPORTED
+    assert fp(A16, 64, A16, sq.SQ_BF16, 8, 64, A16, 64, A16, None, None) == sq.SQ_ERR_NULL
+    assert fp(A16, 64, A16, sq.SQ_I8, 8, 64, A16, 64, None, None, None) == sq.SQ_ERR_DTYPE
+
+
 def test_row_limits(L):
     big = (1 << 24) + 1
     assert L.sq_quant_act(A16, sq.SQ_BF16, big, 64, 64, 0, None, 1e-6, A16, A16, None,

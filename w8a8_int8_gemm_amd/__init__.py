@@ -70,6 +70,13 @@ def lib() -> ctypes.CDLL:
         L.sq_w8a8_linear_static_fp8.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, P, I64, P, P,
                                                 I, I64, P, ctypes.c_size_t,
                                                 ctypes.POINTER(_DebugOut), P]
+        L.sq_calibrate_ln.argtypes = [P, I, I64, I64, I64, P, P, F, P, I, I64, I64, F,
+                                      ctypes.c_uint, P, P, P, P]
+        L.sq_smooth_fold_ln.argtypes = [P, I64, P, P, P, P, P]
+        L.sq_quant_act_ln.argtypes = [P, I, I64, I64, I64, P, P, F, P, P, P, P, P]
+        L.sq_w8a8_linear_ln.argtypes = [P, I, I64, I64, I64, P, P, F, P, P, I64, P, P, I, I64, P,
+                                        ctypes.c_size_t, ctypes.POINTER(_DebugOut), P, P]
+        L.sq_fold_prev_linear.argtypes = [P, I64, P, I, I64, I64, P, I64, P, P, P]
         L.sq_status_string.argtypes = [I]
         L.sq_status_string.restype = ctypes.c_char_p
         L.sq_abi_version.restype = I
@@ -318,3 +325,60 @@ def sq_w8a8_linear_static_fp8(x, gamma_f, x_scale_static, wq, w_scale, y, worksp
                                            _ptr(bias), _ptr(y), ydt, yld, _ptr(workspace),
                                            ws_bytes, dbg, _stream(stream)),
            "sq_w8a8_linear_static_fp8")
+
+
+# --- LayerNorm form and the fold into the previous linear ---------------------
+
+def sq_calibrate_ln(x_cal, w, alpha: float, a, wmax=None, s=None, *, gamma=None, beta=None,
+                    eps: float = 1e-6, accumulate: bool = False, stream=None) -> None:
+    """a[K] absmax of LN(x_cal) (x_cal None: a used as given), wmax[K], s[K] --
+    see sq_calibrate_ln."""
+    K = a.shape[0]
+    xt, xdt, xld = (0, SQ_BF16, K) if x_cal is None else (x_cal.shape[0], _dtype(x_cal), _ld(x_cal))
+    N, wdt, wld = (0, SQ_BF16, 0) if w is None else (w.shape[1], _dtype(w), _ld(w))
+    flags = SQ_CALIB_ACCUMULATE if accumulate else 0
+    _check(lib().sq_calibrate_ln(_ptr(x_cal), xdt, xt, K, xld, _ptr(gamma), _ptr(beta), eps,
+                                 _ptr(w), wdt, N, wld, alpha, flags, _ptr(a), _ptr(wmax), _ptr(s),
+                                 _stream(stream)), "sq_calibrate_ln")
+
+
+def sq_smooth_fold_ln(s, gamma, beta, gamma_out, beta_out, *, stream=None) -> None:
+    """gamma_out = gamma / s, beta_out = beta / s -- see sq_smooth_fold_ln."""
+    _check(lib().sq_smooth_fold_ln(_ptr(s), s.shape[0], _ptr(gamma), _ptr(beta), _ptr(gamma_out),
+                                   _ptr(beta_out), _stream(stream)), "sq_smooth_fold_ln")
+
+
+def sq_quant_act_ln(x, gamma_f, beta_f, xq, x_scale, *, eps: float = 1e-6, row_mean=None,
+                    row_rscale=None, stream=None) -> None:
+    """Per-token INT8 of the smoothed LayerNorm output -- see sq_quant_act_ln."""
+    T, K = x.shape
+    _check(lib().sq_quant_act_ln(_ptr(x), _dtype(x), T, K, _ld(x), _ptr(gamma_f), _ptr(beta_f),
+                                 eps, _ptr(xq), _ptr(x_scale), _ptr(row_mean), _ptr(row_rscale),
+                                 _stream(stream)), "sq_quant_act_ln")
+
+
+def sq_w8a8_linear_ln(x, gamma_f, beta_f, wq, w_scale, y, workspace, *, eps: float = 1e-6,
+                      bias=None, dbg_xq=None, dbg_x_scale=None, dbg_row_rscale=None,
+                      dbg_acc=None, row_mean=None, stream=None) -> None:
+    """sq_quant_act_ln then sq_gemm_w8a8 -- see sq_w8a8_linear_ln."""
+    T, K = x.shape
+    N = wq.shape[0]
+    dbg = None
+    if any(v is not None for v in (dbg_xq, dbg_x_scale, dbg_row_rscale, dbg_acc)):
+        dbg = ctypes.byref(_DebugOut(_ptr(dbg_xq), _ptr(dbg_x_scale), _ptr(dbg_row_rscale),
+                                     _ptr(dbg_acc)))
+    ydt, yld = (SQ_BF16, N) if y is None else (_dtype(y), _ld(y))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().sq_w8a8_linear_ln(_ptr(x), _dtype(x), T, K, _ld(x), _ptr(gamma_f), _ptr(beta_f),
+                                   eps, _ptr(wq), _ptr(w_scale), N, _ptr(bias), _ptr(y), ydt, yld,
+                                   _ptr(workspace), ws_bytes, dbg, _ptr(row_mean),
+                                   _stream(stream)), "sq_w8a8_linear_ln")
+
+
+def sq_fold_prev_linear(s, w_prev, w_out, *, bias=None, bias_out=None, stream=None) -> None:
+    """w_out = W_prev with column j divided by s_j (fp32), bias_out = bias / s --
+    see sq_fold_prev_linear."""
+    Kp, K = w_prev.shape
+    _check(lib().sq_fold_prev_linear(_ptr(s), K, _ptr(w_prev), _dtype(w_prev), Kp, _ld(w_prev),
+                                     _ptr(w_out), _ld(w_out), _ptr(bias), _ptr(bias_out),
+                                     _stream(stream)), "sq_fold_prev_linear")

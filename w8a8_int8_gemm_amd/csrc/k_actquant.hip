@@ -316,6 +316,190 @@ __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem*
 }
 
 // ---------------------------------------------------------------------------
+// LayerNorm form ("SmoothQuant: Weight-Only vs W8A8", Integration with
+// Transformers: 1/s folded into the LayerNorm's gamma and beta):
+//   m_t = fp32(mean), r_t = fp32(1/sqrt(var + eps)) (fp64 sums, the variance
+//   about the fp64 mean), x^ = fp32(fp32(fp32(h - m_t) * r_t) * gamma'_k) +
+//   beta'_k, then the per-token INT8 quantizer above.
+// K <= 8192: one token per wave, the row's raw values in VGPRs from the load
+// to the store; gamma' and beta' come through the caches (every token reads
+// the same K floats).
+// ---------------------------------------------------------------------------
+template <class In, int NV>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void k_quant_act_ln(
+    const typename In::elem* __restrict__ x, int64_t T, int64_t K, int64_t ld,
+    const float* __restrict__ gamma_f, const float* __restrict__ beta_f, float eps,
+    int8_t* __restrict__ xq, float* __restrict__ xscale, float* __restrict__ mrow,
+    float* __restrict__ rrow) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nchunk = (int)(K >> 3);
+  const int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  if (r >= T) return;
+  const typename In::elem* row = x + r * ld;
+  typename In::Raw raw[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int ch = j * 64 + lane;
+    raw[j] = In::raw8(row + (ch < nchunk ? ch : 0) * 8);
+  }
+  double s1 = 0.0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    float v[8];
+    In::widen(raw[j], v);
+    if (j * 64 + lane < nchunk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s1 += (double)v[i];
+  }
+  const double mu = wave_sum(s1) / (double)K;
+  double s2 = 0.0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    float v[8];
+    In::widen(raw[j], v);
+    if (j * 64 + lane < nchunk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double d = (double)v[i] - mu;
+        s2 += d * d;
+      }
+  }
+  s2 = wave_sum(s2);
+  const float mt = (float)mu;
+  const float rt = (float)(1.0 / sqrt(s2 / (double)K + (double)eps));
+  if (lane == 0) {
+    if (mrow != nullptr) mrow[r] = mt;
+    if (rrow != nullptr) rrow[r] = rt;
+  }
+  auto smooth = [&](int j, float (&xh)[8]) {
+    const int ch = j * 64 + lane;
+    float v[8];
+    In::widen(raw[j], v);
+    const f32x4 g0 = *reinterpret_cast<const f32x4*>(gamma_f + ch * 8);
+    const f32x4 g1 = *reinterpret_cast<const f32x4*>(gamma_f + ch * 8 + 4);
+    const f32x4 b0 = *reinterpret_cast<const f32x4*>(beta_f + ch * 8);
+    const f32x4 b1 = *reinterpret_cast<const f32x4*>(beta_f + ch * 8 + 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float n = (v[i] - mt) * rt;
+      xh[i] = n * (i < 4 ? g0[i] : g1[i - 4]) + (i < 4 ? b0[i] : b1[i - 4]);
+    }
+  };
+  float am = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    if (j * 64 + lane < nchunk) {
+      float xh[8];
+      smooth(j, xh);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(xh[i]));
+    }
+  }
+  am = wave_max(am);
+  const float d = am / 127.0f;
+  const float rc = 1.0f / d;
+  const bool fast = rc <= 3.0e38f;
+  const float rcu = fast ? rc : 0.0f;
+  const bool all_div = !fast && d > 0.0f;
+  if (lane == 0) xscale[r] = d;
+  int8_t* qrow = xq + r * K;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int ch = j * 64 + lane;
+    if (ch < nchunk) {
+      float xh[8];
+      smooth(j, xh);
+      bool tie;
+      u32x2 c = quant8(xh, rcu, tie);
+      if (tie || all_div) c = quant8_div(xh, d);
+      *reinterpret_cast<u32x2*>(qrow + ch * 8) = c;
+    }
+  }
+}
+
+// K > 8192: one workgroup per token, four passes over the row (sum, squared
+// deviations, maximum, quantize); the re-reads hit L2.
+template <class In>
+__global__ __launch_bounds__(256) void k_quant_act_ln_wide(
+    const typename In::elem* __restrict__ x, int64_t T, int64_t K, int64_t ld,
+    const float* __restrict__ gamma_f, const float* __restrict__ beta_f, float eps,
+    int8_t* __restrict__ xq, float* __restrict__ xscale, float* __restrict__ mrow,
+    float* __restrict__ rrow) {
+  __shared__ double red_d[4];
+  __shared__ float red_f[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t nchunk = K >> 3;
+  const int64_t r = blockIdx.x;
+  const typename In::elem* row = x + r * ld;
+  auto block_sum = [&](double v) {
+    v = wave_sum(v);
+    __syncthreads();
+    if (lane == 0) red_d[wave] = v;
+    __syncthreads();
+    return (red_d[0] + red_d[1]) + (red_d[2] + red_d[3]);
+  };
+  double s1 = 0.0;
+  for (int64_t ch = threadIdx.x; ch < nchunk; ch += 256) {
+    float v[8];
+    In::load8(row + ch * 8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s1 += (double)v[i];
+  }
+  const double mu = block_sum(s1) / (double)K;
+  double s2 = 0.0;
+  for (int64_t ch = threadIdx.x; ch < nchunk; ch += 256) {
+    float v[8];
+    In::load8(row + ch * 8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double dd = (double)v[i] - mu;
+      s2 += dd * dd;
+    }
+  }
+  s2 = block_sum(s2);
+  const float mt = (float)mu;
+  const float rt = (float)(1.0 / sqrt(s2 / (double)K + (double)eps));
+  if (threadIdx.x == 0) {
+    if (mrow != nullptr) mrow[r] = mt;
+    if (rrow != nullptr) rrow[r] = rt;
+  }
+  auto smooth = [&](int64_t ch, float (&xh)[8]) {
+    float v[8];
+    In::load8(row + ch * 8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xh[i] = (v[i] - mt) * rt * gamma_f[ch * 8 + i] + beta_f[ch * 8 + i];
+  };
+  float am = 0.0f;
+  for (int64_t ch = threadIdx.x; ch < nchunk; ch += 256) {
+    float xh[8];
+    smooth(ch, xh);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(xh[i]));
+  }
+  am = wave_max(am);
+  if (lane == 0) red_f[wave] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+  const float d = am / 127.0f;
+  const float rc = 1.0f / d;
+  const bool fast = rc <= 3.0e38f;
+  if (threadIdx.x == 0) xscale[r] = d;
+  for (int64_t ch = threadIdx.x; ch < nchunk; ch += 256) {
+    float xh[8];
+    smooth(ch, xh);
+    u32x2 c;
+    c[0] = 0u;
+    c[1] = 0u;
+    bool tie = true;
+    if (fast) c = quant8(xh, rc, tie);
+    if (d > 0.0f && tie) c = quant8_div(xh, d);
+    *reinterpret_cast<u32x2*>(xq + r * K + ch * 8) = c;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------
 
@@ -386,6 +570,42 @@ void launch_quant_act_fp8(const void* x, bool bf16, int64_t T, int64_t K, int64_
                           float* xscale, float* rrow, hipStream_t st) {
   quant_act_any(x, bf16, T, K, ld, norm, gamma_f, eps, static_scale, true,
                 reinterpret_cast<int8_t*>(xq), xscale, rrow, st);
+}
+
+template <class In, int NV>
+static void quant_act_ln_nv(const void* x, int64_t T, int64_t K, int64_t ld, const float* g,
+                            const float* b, float eps, int8_t* xq, float* xscale, float* mrow,
+                            float* rrow, hipStream_t st) {
+  const int64_t blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL((k_quant_act_ln<In, NV>), dim3((unsigned)blocks), dim3(64 * kWavesPerBlock),
+                     0, st, (const typename In::elem*)x, T, K, ld, g, b, eps, xq, xscale, mrow,
+                     rrow);
+}
+
+template <class In>
+static void quant_act_ln_t(const void* x, int64_t T, int64_t K, int64_t ld, const float* g,
+                           const float* b, float eps, int8_t* xq, float* xscale, float* mrow,
+                           float* rrow, hipStream_t st) {
+  const int64_t nchunk = K / 8;
+  if (nchunk <= 64) quant_act_ln_nv<In, 1>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
+  else if (nchunk <= 128) quant_act_ln_nv<In, 2>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
+  else if (nchunk <= 256) quant_act_ln_nv<In, 4>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
+  else if (nchunk <= 512) quant_act_ln_nv<In, 8>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
+  else if (nchunk <= 1024)
+    quant_act_ln_nv<In, 16>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
+  else
+    hipLaunchKernelGGL((k_quant_act_ln_wide<In>), dim3((unsigned)T), dim3(256), 0, st,
+                       (const typename In::elem*)x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow);
+}
+
+void launch_quant_act_ln(const void* x, bool bf16, int64_t T, int64_t K, int64_t ld,
+                         const float* gamma_f, const float* beta_f, float eps, int8_t* xq,
+                         float* xscale, float* mrow, float* rrow, hipStream_t st) {
+  if (T <= 0) return;
+  if (bf16)
+    quant_act_ln_t<Bf16In>(x, T, K, ld, gamma_f, beta_f, eps, xq, xscale, mrow, rrow, st);
+  else
+    quant_act_ln_t<F32In>(x, T, K, ld, gamma_f, beta_f, eps, xq, xscale, mrow, rrow, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -10,6 +10,9 @@
 //  * k_rms_act_absmax: the same absmax taken of an RMSNorm output computed on
 //    the fly (the smoothed linears read a norm's output: "SmoothQuant and
 //    W8A8", The trick).
+//  * k_ln_act_absmax: the same for a LayerNorm output ("SmoothQuant:
+//    Weight-Only vs W8A8", Integration with Transformers), gamma and beta
+//    included.
 //  * k_wrow_absmax_s: per-input-channel weight absmax and the smoothing
 //    factor s_j = a_j^alpha / w_j^(1-alpha) ("06 -- SmoothQuant", section 3).
 //
@@ -165,6 +168,126 @@ __global__ __launch_bounds__(256) void k_rms_act_absmax(const typename In::elem*
 }
 
 // ---------------------------------------------------------------------------
+// LayerNorm-mode calibration absmax.  Same row-per-wave layout.  Per row: the
+// fp64 mean, the fp64 sum of squared deviations from it, m_t = fp32(mean) and
+// r_t = fp32(1/sqrt(var + eps)); then per column the running maximum and
+// minimum of n = fp32(fp32(h - m_t) * r_t).  f(n) = fp32(fp32(n * gamma_j) +
+// beta_j) is monotone in n (fp32 multiply and add round monotonically), so
+// max_t |f(n_t)| = max(|f(max_t n)|, |f(min_t n)|): gamma and beta are applied
+// once per column at the end, exactly.  Maxima and minima are combined across
+// waves in LDS through an order-preserving map of the float bits.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned int ordered_bits(float f) {
+  const unsigned int u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_ordered_bits(unsigned int o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+template <class In, int NV, int SPLIT>
+__global__ __launch_bounds__(256) void k_ln_act_absmax(const typename In::elem* __restrict__ h,
+                                                       int64_t rows, int64_t K, int64_t ld,
+                                                       const float* __restrict__ gamma,
+                                                       const float* __restrict__ beta, float eps,
+                                                       float* __restrict__ out) {
+  // SPLIT waves share a row: each takes the whole row for the statistics and
+  // keeps the running maximum and minimum of its own NV / SPLIT chunks.
+  constexpr int NM = NV / SPLIT;
+  constexpr int RPB = 4 / SPLIT;           // rows per workgroup pass
+  extern __shared__ unsigned int lmm[];   // [K] maxima, then [K] minima (ordered bits)
+  unsigned int* lmax = lmm;
+  unsigned int* lmin = lmm + K;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int slice = wave % SPLIT;
+  const int64_t nchunk = K >> 3;
+  for (int64_t c = threadIdx.x; c < K; c += 256) {
+    lmax[c] = 0u;            // below every ordered value
+    lmin[c] = 0xffffffffu;   // above every ordered value
+  }
+  float mx[NM][8], mn[NM][8];
+#pragma unroll
+  for (int j = 0; j < NM; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      mx[j][i] = -INFINITY;
+      mn[j][i] = INFINITY;
+    }
+  const double dK = (double)K;
+  bool any = false;
+  for (int64_t r = (int64_t)blockIdx.x * RPB + wave / SPLIT; r < rows;
+       r += (int64_t)gridDim.x * RPB) {
+    any = true;
+    typename In::Raw raw[NV];
+    const typename In::elem* row = h + r * ld;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t ch = (int64_t)j * 64 + lane;
+      raw[j] = In::raw8(row + (ch < nchunk ? ch : 0) * 8);
+    }
+    double s1 = 0.0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      float v[8];
+      In::widen(raw[j], v);
+      if ((int64_t)j * 64 + lane < nchunk)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s1 += (double)v[i];
+    }
+    const double mu = wave_sum(s1) / dK;
+    double s2 = 0.0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      float v[8];
+      In::widen(raw[j], v);
+      if ((int64_t)j * 64 + lane < nchunk)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const double d = (double)v[i] - mu;
+          s2 += d * d;
+        }
+    }
+    s2 = wave_sum(s2);
+    const float mt = (float)mu;
+    const float rt = (float)(1.0 / sqrt(s2 / dK + (double)eps));
+#pragma unroll
+    for (int jj = 0; jj < NM; ++jj) {
+      float v[8];
+      In::widen(raw[slice * NM + jj], v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float n = (v[i] - mt) * rt;
+        mx[jj][i] = fmaxf(mx[jj][i], n);
+        mn[jj][i] = fminf(mn[jj][i], n);
+      }
+    }
+  }
+  __syncthreads();
+  if (any) {
+#pragma unroll
+    for (int jj = 0; jj < NM; ++jj) {
+      const int64_t ch = (int64_t)(slice * NM + jj) * 64 + lane;
+      if (ch < nchunk)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          atomicMax(&lmax[ch * 8 + i], ordered_bits(mx[jj][i]));
+          atomicMin(&lmin[ch * 8 + i], ordered_bits(mn[jj][i]));
+        }
+    }
+  }
+  __syncthreads();
+  for (int64_t c = threadIdx.x; c < K; c += 256) {
+    if (lmax[c] == 0u) continue;   // this workgroup saw no row
+    const float g = gamma ? gamma[c] : 1.0f;
+    const float b = beta ? beta[c] : 0.0f;
+    const float hi = from_ordered_bits(lmax[c]) * g + b;
+    const float lo = from_ordered_bits(lmin[c]) * g + b;
+    atomic_max_nonneg(out + c, fmaxf(fabsf(hi), fabsf(lo)));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Weight row absmax and smoothing factor.  One wave per input channel j
 // (row j of the [K, N] weight).  s_j = fp32(a_j^alpha / w_j^(1-alpha)) in
 // fp64, floored at 1e-5; s_j = 1 for an all-zero row.
@@ -282,6 +405,38 @@ void launch_rms_act_absmax(const void* h, bool bf16, int64_t rows, int64_t K, in
   if (rows <= 0 || K <= 0) return;
   if (bf16) rms_absmax_t<Bf16In>(h, rows, K, ld, gamma, eps, out, st);
   else rms_absmax_t<F32In>(h, rows, K, ld, gamma, eps, out, st);
+}
+
+template <class In, int NV>
+static void ln_absmax_nv(const void* h, int64_t rows, int64_t K, int64_t ld, const float* gamma,
+                         const float* beta, float eps, float* out, hipStream_t st) {
+  // a lane holds the row's raw chunks plus 16 floats of maxima and minima per
+  // chunk it tracks: wider rows share the tracking among 2 or 4 waves
+  constexpr int SPLIT = NV >= 16 ? 4 : (NV >= 8 && In::kBytes == 4) ? 2 : 1;
+  int64_t blocks = (rows + 4 / SPLIT - 1) / (4 / SPLIT);
+  if (blocks > 512) blocks = 512;
+  hipLaunchKernelGGL((k_ln_act_absmax<In, NV, SPLIT>), dim3((unsigned)blocks), dim3(256),
+                     (size_t)K * 2 * sizeof(unsigned int), st, (const typename In::elem*)h, rows,
+                     K, ld, gamma, beta, eps, out);
+}
+
+template <class In>
+static void ln_absmax_t(const void* h, int64_t rows, int64_t K, int64_t ld, const float* gamma,
+                        const float* beta, float eps, float* out, hipStream_t st) {
+  const int64_t nv = (K + 511) / 512;
+  if (nv <= 1) ln_absmax_nv<In, 1>(h, rows, K, ld, gamma, beta, eps, out, st);
+  else if (nv <= 2) ln_absmax_nv<In, 2>(h, rows, K, ld, gamma, beta, eps, out, st);
+  else if (nv <= 4) ln_absmax_nv<In, 4>(h, rows, K, ld, gamma, beta, eps, out, st);
+  else if (nv <= 8) ln_absmax_nv<In, 8>(h, rows, K, ld, gamma, beta, eps, out, st);
+  else ln_absmax_nv<In, 16>(h, rows, K, ld, gamma, beta, eps, out, st);
+}
+
+void launch_ln_act_absmax(const void* h, bool bf16, int64_t rows, int64_t K, int64_t ld,
+                          const float* gamma, const float* beta, float eps, float* out,
+                          hipStream_t st) {
+  if (rows <= 0 || K <= 0) return;
+  if (bf16) ln_absmax_t<Bf16In>(h, rows, K, ld, gamma, beta, eps, out, st);
+  else ln_absmax_t<F32In>(h, rows, K, ld, gamma, beta, eps, out, st);
 }
 
 void launch_wrow_absmax_s(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,

@@ -6,6 +6,12 @@
 //    The trick).
 //  * k_fold_w: W^[j, n] = W[j, n] * s_j -- s folded into the weight's input
 //    rows ("06 -- SmoothQuant", section 2).
+//  * k_fold_beta: beta'_j = beta_j / s_j, the LayerNorm bias taking its share
+//    of 1/s ("SmoothQuant: Weight-Only vs W8A8", Integration with
+//    Transformers).
+//  * k_fold_prev: W_prev'[i, j] = W_prev[i, j] / s_j -- 1/s folded into the
+//    output columns of the linear whose output is this linear's input ("06 --
+//    SmoothQuant", section 7), with its bias b'_j = b_j / s_j.
 //  * k_quant_weight_t: codes = round-half-even(W^ / Delta_n) (INT8, or the
 //    nearest E4M3 value for FP8), written transposed to the [N, K]
 //    K-contiguous layout the GEMM streams.
@@ -22,6 +28,38 @@ __global__ void k_fold_gamma(const float* __restrict__ s, const float* __restric
                              float* __restrict__ gout, int64_t K) {
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (j < K) gout[j] = (gamma ? gamma[j] : 1.0f) / s[j];
+}
+
+__global__ void k_fold_beta(const float* __restrict__ s, const float* __restrict__ beta,
+                            float* __restrict__ bout, int64_t K) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j < K) bout[j] = (beta ? beta[j] : 0.0f) / s[j];
+}
+
+// 8 consecutive output columns of one row of W_prev [Kp, K] per thread (the
+// bias folds like a LayerNorm beta, k_fold_beta)
+template <class In>
+__global__ __launch_bounds__(256) void k_fold_prev(const typename In::elem* __restrict__ w,
+                                                   int64_t Kp, int64_t K, int64_t ld,
+                                                   const float* __restrict__ s,
+                                                   float* __restrict__ wout, int64_t ldo) {
+  const int64_t chunks_per_row = K >> 3;
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= Kp * chunks_per_row) return;
+  const int64_t i = c / chunks_per_row;
+  const int64_t j0 = (c - i * chunks_per_row) * 8;
+  float v[8];
+  In::load8(w + i * ld + j0, v);
+  const f32x4 s0 = *reinterpret_cast<const f32x4*>(s + j0);
+  const f32x4 s1 = *reinterpret_cast<const f32x4*>(s + j0 + 4);
+  f32x4 o0, o1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o0[e] = v[e] / s0[e];
+    o1[e] = v[4 + e] / s1[e];
+  }
+  *reinterpret_cast<f32x4*>(wout + i * ldo + j0) = o0;
+  *reinterpret_cast<f32x4*>(wout + i * ldo + j0 + 4) = o1;
 }
 
 // 8 consecutive elements of one row per thread
@@ -149,6 +187,25 @@ void launch_fold_gamma(const float* s, const float* gamma, float* gout, int64_t 
   if (K <= 0) return;
   hipLaunchKernelGGL(k_fold_gamma, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, s, gamma,
                      gout, K);
+}
+
+void launch_fold_beta(const float* s, const float* beta, float* bout, int64_t K, hipStream_t st) {
+  if (K <= 0) return;
+  hipLaunchKernelGGL(k_fold_beta, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, s, beta,
+                     bout, K);
+}
+
+void launch_fold_prev(const void* w, bool bf16, int64_t Kp, int64_t K, int64_t ld, const float* s,
+                      float* wout, int64_t ldo, hipStream_t st) {
+  const int64_t chunks = Kp * (K >> 3);
+  if (chunks <= 0) return;
+  const dim3 grid((unsigned)((chunks + 255) / 256));
+  if (bf16)
+    hipLaunchKernelGGL(k_fold_prev<Bf16In>, grid, dim3(256), 0, st, (const uint16_t*)w, Kp, K, ld,
+                       s, wout, ldo);
+  else
+    hipLaunchKernelGGL(k_fold_prev<F32In>, grid, dim3(256), 0, st, (const float*)w, Kp, K, ld, s,
+                       wout, ldo);
 }
 
 void launch_fold_w(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, const float* s,

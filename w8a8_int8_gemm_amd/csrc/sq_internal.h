@@ -14,6 +14,9 @@ void launch_col_absmax(const void* m, bool bf16, int64_t rows, int64_t cols, int
                        const float* row_scale, float qdiv, float* out, hipStream_t st);
 void launch_rms_act_absmax(const void* h, bool bf16, int64_t rows, int64_t K, int64_t ld,
                            const float* gamma, float eps, float* out, hipStream_t st);
+void launch_ln_act_absmax(const void* h, bool bf16, int64_t rows, int64_t K, int64_t ld,
+                          const float* gamma, const float* beta, float eps, float* out,
+                          hipStream_t st);
 void launch_wrow_absmax_s(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
                           const float* a, float alpha, float* wmax, float* s, hipStream_t st);
 
@@ -21,6 +24,9 @@ void launch_wrow_absmax_s(const void* w, bool bf16, int64_t K, int64_t N, int64_
 void launch_fold_gamma(const float* s, const float* gamma, float* gout, int64_t K, hipStream_t st);
 void launch_fold_w(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, const float* s,
                    float* wout, hipStream_t st);
+void launch_fold_beta(const float* s, const float* beta, float* bout, int64_t K, hipStream_t st);
+void launch_fold_prev(const void* w, bool bf16, int64_t Kp, int64_t K, int64_t ld, const float* s,
+                      float* wout, int64_t ldo, hipStream_t st);
 void launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
                            const float* s, const float* wscale, int8_t* wq, hipStream_t st);
 void launch_quant_weight_t_fp8(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
@@ -37,6 +43,10 @@ void launch_quant_act_fp8(const void* x, bool bf16, int64_t T, int64_t K, int64_
                           const float* gamma_f, float eps, const float* static_scale, uint8_t* xq,
                           float* xscale, float* rrow, hipStream_t st);
 // out[0] = max_j fp32(a[j] * |gamma_f[j]|) / qmax
+// LayerNorm form, per-token INT8; gamma_f and beta_f non-NULL
+void launch_quant_act_ln(const void* x, bool bf16, int64_t T, int64_t K, int64_t ld,
+                         const float* gamma_f, const float* beta_f, float eps, int8_t* xq,
+                         float* xscale, float* mrow, float* rrow, hipStream_t st);
 void launch_static_scale(const float* a, const float* gamma_f, int64_t K, float qmax, float* out,
                          hipStream_t st);
 

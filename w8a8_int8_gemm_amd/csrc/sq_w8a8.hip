@@ -279,11 +279,18 @@ namespace {
 
 // the forward of sq_w8a8_linear (static_scale NULL), sq_w8a8_linear_static and
 // their FP8 forms (fp8)
+// LayerNorm form: the norm's beta' and the optional mean output
+struct LnArgs {
+  const float* beta_f;
+  float* row_mean;
+};
+
 sq_status linear_impl(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
                       sq_norm norm, const float* gamma_f, float eps, const float* static_scale,
                       bool fp8, const int8_t* wq, const float* w_scale, int64_t n,
                       const float* bias, void* y, sq_dtype y_dt, int64_t ldy, void* workspace,
-                      size_t ws_bytes, const sq_debug_out* dbg, hipStream_t stream) {
+                      size_t ws_bytes, const sq_debug_out* dbg, hipStream_t stream,
+                      const LnArgs* ln = nullptr) {
   SQ_TRY(check_act(x, x_dt, t, k, ldx, norm, eps));
   if (t == 0) return wq == nullptr ? SQ_ERR_NULL : SQ_OK;   // nothing to compute
   int8_t* xq = dbg ? dbg->xq : nullptr;
@@ -301,7 +308,10 @@ sq_status linear_impl(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_
   // the GEMM's own checks, with the codes and scales that will exist by then
   if (w_scale == nullptr && acc == nullptr) return SQ_ERR_NULL;
   SQ_TRY(check_gemm(xq, xs, t, k, wq, w_scale, n, y, y_dt, ldy, acc));
-  if (fp8)
+  if (ln != nullptr)
+    sqk::launch_quant_act_ln(x, x_dt == SQ_BF16, t, k, ldx, gamma_f, ln->beta_f, eps, xq, xs,
+                             ln->row_mean, rrow, stream);
+  else if (fp8)
     sqk::launch_quant_act_fp8(x, x_dt == SQ_BF16, t, k, ldx, norm == SQ_NORM_RMS, gamma_f, eps,
                               static_scale, reinterpret_cast<uint8_t*>(xq), xs,
                               norm == SQ_NORM_RMS ? rrow : nullptr, stream);
@@ -366,6 +376,84 @@ sq_status sq_w8a8_linear_static_fp8(const void* x, sq_dtype x_dt, int64_t t, int
   return linear_impl(x, x_dt, t, k, ldx, norm, gamma_f, eps, x_scale_static, true,
                      reinterpret_cast<const int8_t*>(wq), w_scale, n, bias, y, y_dt, ldy,
                      workspace, ws_bytes, dbg, stream);
+}
+
+// --- LayerNorm form and the fold into the previous linear --------------------
+
+sq_status sq_calibrate_ln(const void* x_cal, sq_dtype x_dt, int64_t t_cal, int64_t k, int64_t ldx,
+                          const float* gamma, const float* beta, float eps, const void* w,
+                          sq_dtype w_dt, int64_t n, int64_t ldw, float alpha, unsigned flags,
+                          float* a, float* wmax, float* s, hipStream_t stream) {
+  SQ_TRY(check_k(k));
+  if (a == nullptr) return SQ_ERR_NULL;
+  if ((flags & ~SQ_CALIB_ACCUMULATE) != 0u) return SQ_ERR_UNSUPPORTED;
+  if (x_cal != nullptr) {
+    SQ_TRY(check_act(x_cal, x_dt, t_cal, k, ldx, SQ_NORM_RMS, eps));
+    if (k > kMaxNormCalibK) return SQ_ERR_UNSUPPORTED;
+  }
+  if (w != nullptr) {
+    SQ_TRY(check_mat(w, w_dt, k, n, ldw));
+    if (n % 8 != 0) return SQ_ERR_UNSUPPORTED;
+    if (wmax == nullptr || s == nullptr) return SQ_ERR_NULL;
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ALPHA;
+  }
+  if (x_cal == nullptr && w == nullptr) return SQ_OK;
+  if (x_cal != nullptr) {
+    if ((flags & SQ_CALIB_ACCUMULATE) == 0u) sqk::launch_fill_f32(a, k, 0.0f, stream);
+    sqk::launch_ln_act_absmax(x_cal, x_dt == SQ_BF16, t_cal, k, ldx, gamma, beta, eps, a, stream);
+  }
+  if (w != nullptr)
+    sqk::launch_wrow_absmax_s(w, w_dt == SQ_BF16, k, n, ldw, a, alpha, wmax, s, stream);
+  return hip_status();
+}
+
+sq_status sq_smooth_fold_ln(const float* s, int64_t k, const float* gamma, const float* beta,
+                            float* gamma_out, float* beta_out, hipStream_t stream) {
+  SQ_TRY(check_k(k));
+  if (s == nullptr || gamma_out == nullptr || beta_out == nullptr) return SQ_ERR_NULL;
+  sqk::launch_fold_gamma(s, gamma, gamma_out, k, stream);
+  sqk::launch_fold_beta(s, beta, beta_out, k, stream);
+  return hip_status();
+}
+
+sq_status sq_quant_act_ln(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                          const float* gamma_f, const float* beta_f, float eps, int8_t* xq,
+                          float* x_scale, float* row_mean, float* row_rscale,
+                          hipStream_t stream) {
+  SQ_TRY(check_act(x, x_dt, t, k, ldx, SQ_NORM_RMS, eps));
+  if (gamma_f == nullptr || beta_f == nullptr || xq == nullptr || x_scale == nullptr)
+    return SQ_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(gamma_f) || !aligned16(beta_f)) return SQ_ERR_UNSUPPORTED;
+  if (t == 0) return SQ_OK;
+  sqk::launch_quant_act_ln(x, x_dt == SQ_BF16, t, k, ldx, gamma_f, beta_f, eps, xq, x_scale,
+                           row_mean, row_rscale, stream);
+  return hip_status();
+}
+
+sq_status sq_w8a8_linear_ln(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                            const float* gamma_f, const float* beta_f, float eps,
+                            const int8_t* wq, const float* w_scale, int64_t n, const float* bias,
+                            void* y, sq_dtype y_dt, int64_t ldy, void* workspace, size_t ws_bytes,
+                            const sq_debug_out* dbg, float* row_mean, hipStream_t stream) {
+  if (gamma_f == nullptr || beta_f == nullptr) return SQ_ERR_NULL;
+  if (!aligned16(gamma_f) || !aligned16(beta_f)) return SQ_ERR_UNSUPPORTED;
+  const LnArgs ln{beta_f, row_mean};
+  return linear_impl(x, x_dt, t, k, ldx, SQ_NORM_RMS, gamma_f, eps, nullptr, false, wq, w_scale, n,
+                     bias, y, y_dt, ldy, workspace, ws_bytes, dbg, stream, &ln);
+}
+
+sq_status sq_fold_prev_linear(const float* s, int64_t k, const void* w_prev, sq_dtype w_dt,
+                              int64_t k_prev, int64_t ldw, float* w_out, int64_t ldo,
+                              const float* bias, float* bias_out, hipStream_t stream) {
+  SQ_TRY(check_k(k));
+  if (s == nullptr || w_out == nullptr) return SQ_ERR_NULL;
+  SQ_TRY(check_mat(w_prev, w_dt, k_prev, k, ldw));
+  if (ldo < k) return SQ_ERR_SHAPE;
+  if (!aligned16(w_out) || ldo % 4 != 0 || !aligned16(s)) return SQ_ERR_UNSUPPORTED;
+  if (bias != nullptr && bias_out == nullptr) return SQ_ERR_NULL;
+  sqk::launch_fold_prev(w_prev, w_dt == SQ_BF16, k_prev, k, ldw, s, w_out, ldo, stream);
+  if (bias != nullptr) sqk::launch_fold_beta(s, bias, bias_out, k, stream);   // b_j / s_j
+  return hip_status();
 }
 
 }  // extern "C"
