@@ -335,6 +335,83 @@ def decode_gemm(sq, torch, dev, T=16, K=8192, N=8192, copies=5, iters=50):
             "algorithmic": "K*N weight bytes + T*K + scales + 2*T*N output bytes per call"}
 
 
+def block_timing(sq, torch, dev, T=2048, H=4096, KV=1024, I=14336, iters=10):
+    """The online forward of one decoder layer's four W8A8 linears, wired as
+    the pages map them: RMSNorm -> q|k|v and RMSNorm -> gate|up through the
+    fused norm + smooth + quantize kernel, o_proj and down_proj plain per-token
+    (Llama-8B-like shapes, T tokens of prefill).  Weights are random INT8
+    codes with random steps (timing only).  Also the LayerNorm form of the
+    q|k|v input's quantizer and its calibration pass, in GB/s."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(107)
+    stream = torch.cuda.current_stream()
+
+    def act(t, k):
+        x = torch.randn((t, k), device=dev, generator=g)
+        x[:, :16] *= 30.0
+        return x.to(torch.bfloat16)
+
+    def weight(k, n):
+        wq = torch.randint(-127, 128, (n, k), dtype=torch.int8, device=dev, generator=g)
+        return wq, torch.rand(n, device=dev, generator=g) * 1e-3
+
+    layers = {"qkv": (H, H + 2 * KV, True), "o_proj": (H, H, False),
+              "gate_up": (H, 2 * I, True), "down": (I, H, False)}
+    out, tot_ops, tot_us = {}, 0.0, 0.0
+    for name, (K, N, norm) in layers.items():
+        x = act(T, K)
+        wq, wsc = weight(K, N)
+        gam = torch.rand(K, device=dev, generator=g) + 0.5 if norm else None
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        work = torch.empty(sq.sq_linear_workspace_bytes(T, K), dtype=torch.uint8, device=dev)
+
+        def call():
+            sq.sq_w8a8_linear(x, gam, wq, wsc, y, work, norm=norm, stream=stream)
+
+        call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / iters
+        ops = 2.0 * T * K * N
+        out[name] = {"K": K, "N": N, "norm": norm, "us": us, "tops": ops / (us * 1e-6) / 1e12}
+        tot_ops += ops
+        tot_us += us
+    out["layer_linears_tops"] = tot_ops / (tot_us * 1e-6) / 1e12
+    out["layer_linears_us"] = tot_us
+
+    # LayerNorm form: quantizer on the q|k|v input, calibration over 16384 tokens
+    x = act(T, H)
+    xc = act(16384, H)
+    gam = torch.rand(H, device=dev, generator=g) + 0.5
+    bet = torch.randn(H, device=dev, generator=g) * 0.1
+    xq = torch.empty((T, H), dtype=torch.int8, device=dev)
+    xs = torch.empty(T, dtype=torch.float32, device=dev)
+    a = torch.empty(H, dtype=torch.float32, device=dev)
+    for name, fn, byts in (
+            ("quant_act_ln", lambda: sq.sq_quant_act_ln(x, gam, bet, xq, xs, stream=stream),
+             3.0 * T * H + 4.0 * T),
+            ("calibrate_ln", lambda: sq.sq_calibrate_ln(xc, None, 0.5, a, gamma=gam, beta=bet,
+                                                        stream=stream), 2.0 * 16384 * H)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / iters
+        out[name] = {"us": us, "gbs": byts / (us * 1e-6) / 1e9}
+    out["shapes"] = (f"T={T}, hidden {H}, q|k|v {H}+{KV}+{KV}, gate|up 2x{I}, down {I}->{H}; "
+                     "LayerNorm calibration over 16384 tokens")
+    return out
+
+
 def cpu_baseline(inp, wl, target_s: float):
     import numpy as np  # noqa: F401
 
@@ -501,6 +578,7 @@ def main():
                                                                  dev)
         out["decode_gemm"] = decode_gemm(sq, torch, dev)
         out["fp8"] = fp8_timing(sq, torch, sets, wl, s, gp, bias, dev)
+        out["decoder_layer"] = block_timing(sq, torch, dev)
     if not args.no_cpu_baseline:
         print("timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_seconds)

@@ -177,10 +177,10 @@ def test_gemm_fp8_group_arithmetic():
     assert np.all(np.abs(got - oracle.gemm_fp8(q, qw)[:, 0]) <= _acc_bound(q, qw)[:, 0])
 
 
-def test_gemm_fp8_exact_when_every_partial_sum_is_representable():
-    say("fp8 gemm exact small integers")
-    rng = np.random.default_rng(42)
-    T, N, K = 200, 136, 4096
+@pytest.mark.parametrize("T,N,K", [(200, 136, 4096), (1500, 4096, 128), (1800, 6104, 64)])
+def test_gemm_fp8_exact_when_every_partial_sum_is_representable(T, N, K):
+    say(f"fp8 gemm exact small integers T={T} N={N} K={K}")
+    rng = np.random.default_rng(42 + T)
     vals = np.array([-4, -3, -2, -1, 0, 1, 2, 3, 4], np.float32)
     q = oracle.e4m3_encode(rng.choice(vals, (T, K)))
     qw = oracle.e4m3_encode(rng.choice(vals, (N, K)))

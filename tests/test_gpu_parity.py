@@ -228,7 +228,9 @@ def test_quant_act_ties_and_fallback():
 
 GEMM_SHAPES = [(300, 520, 704), (256, 256, 4096), (513, 1000, 128), (1, 520, 704), (16, 520, 704),
                (17, 264, 640), (33, 96, 192), (64, 1024, 1024), (65, 8, 64), (1000, 40, 64),
-               (384, 2056, 512)]
+               (384, 2056, 512),
+               # 128 x 256 tiles (ragged T), then 256 x 256 tiles (ragged T and N)
+               (1500, 4096, 256), (1800, 6104, 128)]
 
 
 @pytest.mark.parametrize("T,N,K", GEMM_SHAPES)

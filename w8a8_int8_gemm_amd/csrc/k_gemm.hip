@@ -490,18 +490,36 @@ static void gemm_tile(const int8_t* xq, const float* xs, int T, int K, const int
                        xs, T, K, wq, ws, N, bias, y, ldy, group_t);
 }
 
+// compute units of the current device (looked up once per device)
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <bool F8>
 static void gemm_sizes(const int8_t* xq, const float* xs, int64_t T, int64_t K, const int8_t* wq,
                        const float* ws, int64_t N, const float* bias, void* y, int64_t ldy,
                        int out, hipStream_t st) {
   const int it = (int)T, ik = (int)K, in = (int)N, il = (int)ldy;
-  // 256 x 256 tiles fill the chip when there are at least ~2 per CU;
-  // otherwise smaller tiles trade reuse for occupancy.
+  // 256 x 256 tiles (8 waves) have the most reuse and win whenever they keep
+  // at least 3/4 of the compute units busy; below that 128 x 256 tiles (8
+  // waves), then 128 x 128 (4 waves), trade reuse for occupancy (measured on
+  // the 2048-token q|k|v, o, down and gate|up shapes).
+  const int64_t busy = 3 * (int64_t)cu_count() / 4;
   const int64_t t256 = ((T + 255) / 256) * ((N + 255) / 256);
-  if (t256 >= 384)
+  const int64_t t128x256 = ((T + 127) / 128) * ((N + 255) / 256);
+  if (t256 >= busy)
     gemm_tile<256, 256, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
-  else if (((T + 255) / 256) * ((N + 127) / 128) >= 256)
-    gemm_tile<256, 128, 2, 2, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+  else if (t128x256 >= busy)
+    gemm_tile<128, 256, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
   else
     gemm_tile<128, 128, 2, 2, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
 }
