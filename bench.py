@@ -412,6 +412,132 @@ def block_timing(sq, torch, dev, T=2048, H=4096, KV=1024, I=14336, iters=10):
     return out
 
 
+def decode_calibration(sq, torch, dev, Tc=262144, K=8192, iters=5):
+    """The decode workload's calibration pass: per-channel absmax of a
+    262144 x 8192 bf16 calibration set (4 GiB, 24 outlier channels x60),
+    far larger than the Infinity Cache.  Drawn on the GPU (N(0,1) bf16)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(105)
+    xc = torch.randn((Tc, K), dtype=torch.bfloat16, device=dev, generator=g)
+    for c in torch.randperm(K, generator=torch.Generator().manual_seed(105))[:24].tolist():
+        xc[:, c].mul_(60.0)
+    a = torch.empty(K, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sq.sq_calibrate(xc, None, 0.5, a, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        sq.sq_calibrate(xc, None, 0.5, a, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    del xc
+    byts = 2.0 * Tc * K
+    return {"workload": f"calibration absmax Tc={Tc} K={K} bf16", "us": us,
+            "achieved": byts / (us * 1e-6) / 1e9, "unit": "GB/s",
+            "frac_of_peak": byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "algorithmic": "2 bytes per calibration element"}
+
+
+def decode_linear_graph(sq, torch, dev, T=16, K=8192, N=8192, iters=50):
+    """The decode linear (quantizer + GEMM, one sq_w8a8_linear call) launched
+    eagerly and replayed from a captured HIP graph: the launch cost the graph
+    removes at 16 tokens."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(106)
+    x = torch.randn((T, K), dtype=torch.bfloat16, device=dev, generator=g)
+    wq = torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev, generator=g)
+    wsc = torch.rand(N, device=dev, generator=g) * 1e-3
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    work = torch.empty(sq.sq_linear_workspace_bytes(T, K), dtype=torch.uint8, device=dev)
+
+    def fwd():
+        sq.sq_w8a8_linear(x, None, wq, wsc, y, work)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / iters
+
+    eager_us = timed(fwd)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fwd()
+    graph_us = timed(graph.replay)
+    return {"workload": f"decode linear T={T} K={K} N={N} (weight in cache)", "eager_us": eager_us,
+            "graph_replay_us": graph_us}
+
+
+def config_step(sq, torch, dev, name, steps=10, warmup=3):
+    """The same whole step (calibrate, fold, quantize the weight, the online
+    linear) on another workload's own synthetic inputs: the RMSNorm -> q|k|v
+    and the MLP gate|up configurations.  One input set (no rotation)."""
+    import numpy as np
+
+    import synth
+
+    wl = synth.WORKLOADS[name]
+    T, K, N = wl.T, wl.K, wl.N
+    inp = synth.make_inputs(wl)
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    x_cal, x, w, bias = d(inp.x_cal), d(inp.x), d(inp.w), d(inp.bias)
+    gamma = None if inp.gamma is None else d(inp.gamma)
+    del inp
+    f = lambda n: torch.empty(n, dtype=torch.float32, device=dev)  # noqa: E731
+    a, wm, s, gp, wsc = f(K), f(K), f(K), f(K), f(N)
+    wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    work = torch.empty(sq.sq_linear_workspace_bytes(T, K), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    calls = [
+        ("calibrate", lambda: sq.sq_calibrate(x_cal, w, wl.alpha, a, wm, s, norm=wl.norm,
+                                              gamma=gamma, stream=stream)),
+        ("smooth_fold", lambda: sq.sq_smooth_fold(s, gamma, gp, stream=stream)),
+        ("quant_weight", lambda: sq.sq_quant_weight(w, s, wq, wsc, stream=stream)),
+        ("linear", lambda: sq.sq_w8a8_linear(x, gp, wq, wsc, y, work, norm=wl.norm, bias=bias,
+                                             stream=stream)),
+    ]
+    for _ in range(warmup):
+        for _, c in calls:
+            c()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        for j, (_, c) in enumerate(calls):
+            c()
+            evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    per = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps * 1e3
+           for j, (n, _) in enumerate(calls)}
+    ops = 2.0 * T * K * N
+    return {"workload": f"{name}: T={T} K={K} N={N} calib_tokens={wl.Tc} norm={wl.norm}",
+            "ms_per_step": ms, "step_tops": ops / (ms * 1e-3) / 1e12,
+            "linear_us": per["linear"], "linear_tops": ops / (per["linear"] * 1e-6) / 1e12,
+            "calls_us": per}
+
+
 def cpu_baseline(inp, wl, target_s: float):
     import numpy as np  # noqa: F401
 
@@ -579,6 +705,9 @@ def main():
         out["decode_gemm"] = decode_gemm(sq, torch, dev)
         out["fp8"] = fp8_timing(sq, torch, sets, wl, s, gp, bias, dev)
         out["decoder_layer"] = block_timing(sq, torch, dev)
+        out["decode_calibration"] = decode_calibration(sq, torch, dev)
+        out["configs"] = {n: config_step(sq, torch, dev, n) for n in ("rmsnorm_qkv", "gate_up")}
+        out["decode_linear_graph"] = decode_linear_graph(sq, torch, dev)
     if not args.no_cpu_baseline:
         print("timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_seconds)
