@@ -69,6 +69,7 @@ def _load():
         _lib.oracle_fold_ln.argtypes = [P, I64, P, P, P, P]
         _lib.oracle_quant_act_ln.argtypes = [P, I, I64, I64, I64, P, P, F, P, P, P, P, P, P]
         _lib.oracle_fold_prev.argtypes = [P, I64, P, I, I64, I64, P, P, P]
+        _lib.oracle_smoothed_act.argtypes = [P, I, I64, I64, I64, I, P, F, P, P]
         _lib.oracle_e4m3_encode_array.argtypes = [P, I64, P]
         _lib.oracle_e4m3_decode_array.argtypes = [P, I64, P]
         _lib.oracle_quant_weight_fp8.argtypes = [P, I64, I64, I64, P, P]
@@ -380,6 +381,59 @@ def linear_static(x, delta, gamma_f, qw, w_scale, bias=None, *, norm=False, r=No
     acc = int_gemm(q, qw)
     y = epilogue(acc, xs, w_scale, bias)
     return dict(q=q, x_scale=xs, r=rr, acc=acc, y32=y, y=to_bf16(y) if out_bf16 else y)
+
+
+# ---------------------------------------------------------------------------
+# GPTQ on the migrated weights
+# ---------------------------------------------------------------------------
+
+def smoothed_act(x: np.ndarray, gamma_f=None, *, norm: bool = False,
+                 r: Optional[np.ndarray] = None, eps: float = 1e-6) -> np.ndarray:
+    """x^ [T,K] fp32 exactly as the activation quantizer forms it."""
+    x, bf = _mat(x)
+    T, K = x.shape
+    out = np.empty((T, K), np.float32)
+    _load().oracle_smoothed_act(_p(x), bf, T, K, K, int(norm), _p(_f32(r)), float(eps),
+                                _p(_f32(gamma_f)), _p(out))
+    return out
+
+
+def gptq(w_hat: np.ndarray, xhat: np.ndarray, *, damp: float = 0.01):
+    """GPTQ error-compensating rounding of the migrated weight ("06 --
+    SmoothQuant", section 10: SmoothQuant migration first, then GPTQ on the
+    migrated weights).  The pages name the step only; this follows the
+    published GPTQ algorithm, unblocked, in fp64:
+      H = X^T X over the calibration tokens' x^ (any positive scale: the codes
+          do not depend on it); a dead input (H_jj = 0) gets H_jj = 1 and its
+          weight row zeroed; H += damp * mean(diag H) * I;
+      U = the upper Cholesky factor of H^-1 (H^-1 = U^T U);
+      the per-output-channel step of the plain quantizer, w_scale[n] =
+          fp32(max_j |W^[j,n]| / 127), fixed;
+      for each input channel j in order: q_j = clamp(rne(W[j,:] / w_scale),
+          +-127) (0 where w_scale is 0), e = (W[j,:] - w_scale * q_j) / U_jj,
+          and every later row k takes W[k,:] -= U_jk * e.
+    w_hat [K,N] fp32, xhat [T,K] fp32.  Returns (qw [N,K] int8, w_scale [N])."""
+    W = np.asarray(w_hat, np.float32)
+    K, N = W.shape
+    ws = (np.abs(W).max(axis=0) / np.float32(127)).astype(np.float32)
+    X = np.asarray(xhat, np.float32).astype(np.float64)
+    H = X.T @ X
+    W = W.astype(np.float64)
+    dead = np.diag(H) == 0
+    H[dead, dead] = 1.0
+    W[dead, :] = 0.0
+    H[np.diag_indices(K)] += damp * np.mean(np.diag(H))
+    U = np.linalg.cholesky(np.linalg.inv(H)).T
+    d = ws.astype(np.float64)
+    live = d > 0
+    Q = np.zeros((K, N), np.int8)
+    for j in range(K):
+        q = np.zeros(N)
+        q[live] = np.clip(np.rint(W[j, live] / d[live]), -127, 127)
+        Q[j] = q.astype(np.int8)
+        e = (W[j] - d * q) / U[j, j]
+        W[j + 1:] -= np.outer(U[j, j + 1:], e)
+    return np.ascontiguousarray(Q.T), ws
 
 
 # ---------------------------------------------------------------------------

@@ -258,6 +258,26 @@ static float static_amax(const void *x, int is_bf16, int64_t T, int64_t K, int64
   return amax;
 }
 
+/* x^ of every element, as the activation quantizer forms it (r_in: the RMSNorm
+   factors to use in norm mode, NULL: computed as in oracle_rms_rscale); out is
+   fp32 [T, K].  GPTQ's Hessian is taken over these values. */
+void oracle_smoothed_act(const void *x, int is_bf16, int64_t T, int64_t K, int64_t ld, int norm,
+                         const float *r_in, float eps, const float *gamma_f, float *out) {
+  float *r = NULL;
+  if (norm) {
+    r = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1));
+    if (r_in)
+      memcpy(r, r_in, sizeof(float) * (size_t)T);
+    else
+      oracle_rms_rscale(x, is_bf16, T, K, ld, eps, r);
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t k = 0; k < K; ++k)
+      out[t * K + k] = smoothed(x, is_bf16, t * ld + k, norm, norm ? r[t] : 1.0f, gamma_f, k);
+  free(r);
+}
+
 /* Static per-tensor step: Delta = fp32( max over every calibration token t and
    channel k of |x^[t,k]| / 127 ). */
 float oracle_static_scale(const void *x, int is_bf16, int64_t T, int64_t K, int64_t ld, int norm,

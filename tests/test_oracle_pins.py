@@ -744,3 +744,94 @@ def test_fold_prev_invariance_and_exact_powers_of_two():
     wq2, bq2 = oracle.fold_prev(s2, wp, bp)
     np.testing.assert_array_equal(wq2.astype(np.float64) * s2[None, :], wp.astype(np.float64))
     np.testing.assert_array_equal(bq2.astype(np.float64) * s2, bp.astype(np.float64))
+
+
+# GPTQ on the migrated weights ("06 -- SmoothQuant", section 10 names the
+# step; the algorithm is the published GPTQ, restated in oracle.gptq)
+
+def _rtn(w_hat):
+    return oracle.quant_weight(w_hat)
+
+
+def test_gptq_with_uncorrelated_inputs_is_round_to_nearest():
+    # every calibration token lights one channel: H is diagonal (damping
+    # keeps it so), U is diagonal and no error reaches another row
+    rng = np.random.default_rng(60)
+    K, N = 40, 24
+    x = np.zeros((4 * K, K), np.float32)
+    for t in range(4 * K):
+        x[t, t % K] = rng.uniform(0.5, 3.0)
+    w = (rng.standard_normal((K, N)) * 0.05).astype(np.float32)
+    q, ws = oracle.gptq(w, x)
+    q0, ws0 = _rtn(w)
+    np.testing.assert_array_equal(ws, ws0)
+    np.testing.assert_array_equal(q, q0)
+
+
+def test_gptq_two_inputs_closed_form():
+    # K = 2: with row 0 rounded, the row-1 weight minimizing the output error
+    # (w - w')^T H (w - w') is w1 + (H01 / H11) (w0 - Delta q0)
+    rng = np.random.default_rng(61)
+    for trial in range(20):
+        x = rng.standard_normal((50, 2)).astype(np.float32)
+        x[:, 1] += rng.uniform(-2, 2) * x[:, 0]
+        w = (rng.standard_normal((2, 12)) * 0.05).astype(np.float32)
+        q, ws = oracle.gptq(w, x, damp=0.01)
+        X = x.astype(np.float64)
+        H = X.T @ X
+        H += 0.01 * np.mean(np.diag(H)) * np.eye(2)
+        d = ws.astype(np.float64)
+        q0 = np.clip(np.rint(w[0].astype(np.float64) / d), -127, 127)
+        w1 = w[1].astype(np.float64) + H[0, 1] / H[1, 1] * (w[0] - d * q0)
+        np.testing.assert_array_equal(q[:, 0], q0.astype(np.int8))
+        np.testing.assert_array_equal(q[:, 1], np.clip(np.rint(w1 / d), -127, 127).astype(np.int8))
+
+
+def test_gptq_matches_the_explicit_inverse_formulation():
+    # the same greedy rounding written with the explicit inverse Hessian of the
+    # remaining inputs (optimal brain surgeon updates, the inverse shrunk by
+    # Gaussian elimination after each input) instead of a Cholesky factor
+    rng = np.random.default_rng(62)
+    K, N, T = 24, 10, 200
+    x = (rng.standard_normal((T, K)) @ rng.standard_normal((K, K))).astype(np.float32)
+    w = (rng.standard_normal((K, N)) * 0.05).astype(np.float32)
+    q, ws = oracle.gptq(w, x)
+    X = x.astype(np.float64)
+    H = X.T @ X
+    H += 0.01 * np.mean(np.diag(H)) * np.eye(K)
+    Hi = np.linalg.inv(H)
+    W = w.astype(np.float64)
+    d = ws.astype(np.float64)
+    for j in range(K):
+        qj = np.clip(np.rint(W[j] / d), -127, 127)
+        assert np.array_equal(q[:, j], qj.astype(np.int8)), j
+        err = (W[j] - d * qj) / Hi[j, j]
+        W -= np.outer(Hi[:, j], err)             # rows already done change too but are never read
+        Hi = Hi - np.outer(Hi[:, j], Hi[j, :]) / Hi[j, j]
+
+
+def test_gptq_lowers_the_layer_error_on_correlated_inputs():
+    rng = np.random.default_rng(63)
+    K, N, T = 96, 48, 600
+    mix = np.eye(K) + rng.standard_normal((K, K)) / np.sqrt(K)
+    x = (rng.standard_normal((T, K)) @ mix).astype(np.float32)
+    w = (rng.standard_normal((K, N)) * 0.05).astype(np.float32)
+    q, ws = oracle.gptq(w, x)
+    q0, _ = _rtn(w)
+    X = x.astype(np.float64)
+
+    def err(codes):
+        return np.linalg.norm(X @ (w.astype(np.float64) - (codes.T * ws[None, :].astype(np.float64))))
+
+    assert err(q) < 0.85 * err(q0)
+
+
+def test_gptq_dead_inputs_and_zero_columns():
+    rng = np.random.default_rng(64)
+    K, N = 16, 8
+    x = rng.standard_normal((40, K)).astype(np.float32)
+    x[:, 5] = 0.0                                   # an input channel calibration never saw
+    w = (rng.standard_normal((K, N)) * 0.05).astype(np.float32)
+    w[:, 3] = 0.0                                   # an output channel with no weight
+    q, ws = oracle.gptq(w, x)
+    assert not q[:, 5].any() and not q[3].any() and ws[3] == 0
