@@ -538,6 +538,43 @@ def config_step(sq, torch, dev, name, steps=10, warmup=3):
             "calls_us": per}
 
 
+def gptq_timing(sq, torch, inp, wl, d, dev, iters=2):
+    """GPTQ rounding of the headline weight (K = N = 4096) with the Hessian of
+    the 8192 calibration tokens: one sq_quant_weight_gptq call, event-timed,
+    and its weight error through the calibration x^ next to round-to-nearest
+    (computed on the GPU in fp64 from the codes)."""
+    T, K, N = wl.Tc, wl.K, wl.N
+    x_cal, w = d(inp.x_cal), d(inp.w)
+    f = lambda n: torch.empty(n, dtype=torch.float32, device=dev)  # noqa: E731
+    a, wm, s, gp, wsc, wsr = f(K), f(K), f(K), f(K), f(N), f(N)
+    sq.sq_calibrate(x_cal, w, wl.alpha, a, wm, s)
+    sq.sq_smooth_fold(s, None, gp)
+    wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    wr = torch.empty((N, K), dtype=torch.int8, device=dev)
+    sq.sq_quant_weight(w, s, wr, wsr)
+    work = torch.empty(sq.sq_gptq_workspace_bytes(T, K, N), dtype=torch.uint8, device=dev)
+    sq.sq_quant_weight_gptq(x_cal, gp, w, s, wq, wsc, work)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        sq.sq_quant_weight_gptq(x_cal, gp, w, s, wq, wsc, work)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    del work
+    # proxy error through the calibration x^ (fp64 on the GPU, reporting only)
+    xh = (x_cal.double() * gp.double()).float().double()
+    what = (w.float() * s[:, None]).double()
+
+    def werr(codes, step):
+        return float(torch.linalg.norm(xh @ (what - codes.double().t() * step.double()[None, :])))
+
+    ratio = werr(wq, wsc) / werr(wr, wsr)
+    return {"workload": f"GPTQ K={K} N={N} calibration tokens {T}", "ms": ms,
+            "calibration_weight_error_vs_round_to_nearest": ratio}
+
+
 def cpu_baseline(inp, wl, target_s: float):
     import numpy as np  # noqa: F401
 
@@ -707,6 +744,7 @@ def main():
         out["decoder_layer"] = block_timing(sq, torch, dev)
         out["decode_calibration"] = decode_calibration(sq, torch, dev)
         out["configs"] = {n: config_step(sq, torch, dev, n) for n in ("rmsnorm_qkv", "gate_up")}
+        out["gptq"] = gptq_timing(sq, torch, inp, wl, d, dev)
         out["decode_linear_graph"] = decode_linear_graph(sq, torch, dev)
     if not args.no_cpu_baseline:
         print("timing the CPU oracle", file=sys.stderr, flush=True)

@@ -344,6 +344,38 @@ sq_status sq_fold_prev_linear(const float *s, int64_t k, const void *w_prev, sq_
                               int64_t k_prev, int64_t ldw, float *w_out, int64_t ldo,
                               const float *bias, float *bias_out, hipStream_t stream);
 
+/*
+ * GPTQ on the migrated weight ("06 -- SmoothQuant", section 10: the
+ * production recipe runs SmoothQuant's migration, then GPTQ's error-
+ * compensating rounding on the migrated weights).  The pages name the step
+ * only; this follows the published GPTQ algorithm, in fp64:
+ *   x^      the calibration activations exactly as the activation quantizer
+ *           forms them (x_cal with gamma_f, RMSNorm in norm mode)
+ *   H       = x^T x^ [k, k]; an input with H_jj = 0 gets H_jj = 1 and a zero
+ *           weight row; H += damp * mean(diag H) * I
+ *   U       the upper Cholesky factor of H^-1
+ *   W^      = fp32(W[j, n] * s_j) (s NULL = ones), the step
+ *           w_scale[n] = fp32(max_j |W^[j, n]| / 127) as in sq_quant_weight
+ *   rows j = 0 .. k-1 in order: wq[n, j] = clamp(rne(W^[j, n] / w_scale[n]),
+ *           -127, 127) (0 where w_scale[n] = 0), e = (W^[j, :] - w_scale *
+ *           wq[:, j]) / U_jj, and every later row k takes W^[k, :] -= U_jk * e.
+ * Arguments as sq_quant_act (x_cal side) and sq_quant_weight (w side);
+ * damp >= 0 (0.01 is the usual value); row_rscale (nullable, norm mode)
+ * receives the calibration rows' r_t.  workspace: at least
+ * sq_gptq_workspace_bytes(t_cal, k, n) bytes of device memory, 256-byte
+ * aligned (about 16 k^2 + 8 k n bytes).  k <= 16384, n % 8 == 0; t_cal = 0
+ * or n = 0 is SQ_ERR_SHAPE.  The rounding order is the algorithm's; sums
+ * inside it (the Hessian, the factorizations, the blocked updates) are
+ * reordered, so codes can differ from another evaluation only where a
+ * quotient lies within rounding of a half-integer.
+ */
+size_t sq_gptq_workspace_bytes(int64_t t_cal, int64_t k, int64_t n);
+sq_status sq_quant_weight_gptq(const void *x_cal, sq_dtype x_dt, int64_t t_cal, int64_t ldx,
+                               sq_norm norm, const float *gamma_f, float eps, const void *w,
+                               sq_dtype w_dt, int64_t k, int64_t n, int64_t ldw, const float *s,
+                               float damp, int8_t *wq, float *w_scale, float *row_rscale,
+                               void *workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Static description of a status code (host memory, never NULL). */
 const char *sq_status_string(sq_status status);
 

@@ -398,7 +398,7 @@ def smoothed_act(x: np.ndarray, gamma_f=None, *, norm: bool = False,
     return out
 
 
-def gptq(w_hat: np.ndarray, xhat: np.ndarray, *, damp: float = 0.01):
+def gptq(w_hat: np.ndarray, xhat: np.ndarray, *, damp: float = 0.01, return_quotients=False):
     """GPTQ error-compensating rounding of the migrated weight ("06 --
     SmoothQuant", section 10: SmoothQuant migration first, then GPTQ on the
     migrated weights).  The pages name the step only; this follows the
@@ -412,7 +412,10 @@ def gptq(w_hat: np.ndarray, xhat: np.ndarray, *, damp: float = 0.01):
       for each input channel j in order: q_j = clamp(rne(W[j,:] / w_scale),
           +-127) (0 where w_scale is 0), e = (W[j,:] - w_scale * q_j) / U_jj,
           and every later row k takes W[k,:] -= U_jk * e.
-    w_hat [K,N] fp32, xhat [T,K] fp32.  Returns (qw [N,K] int8, w_scale [N])."""
+    damp is taken as an fp32 value (the library's argument type).
+    w_hat [K,N] fp32, xhat [T,K] fp32.  Returns (qw [N,K] int8, w_scale [N]),
+    plus the quotients W[j,n] / w_scale[n] the rounding saw [K,N] when asked."""
+    damp = float(np.float32(damp))
     W = np.asarray(w_hat, np.float32)
     K, N = W.shape
     ws = (np.abs(W).max(axis=0) / np.float32(127)).astype(np.float32)
@@ -427,12 +430,17 @@ def gptq(w_hat: np.ndarray, xhat: np.ndarray, *, damp: float = 0.01):
     d = ws.astype(np.float64)
     live = d > 0
     Q = np.zeros((K, N), np.int8)
+    quot = np.zeros((K, N)) if return_quotients else None
     for j in range(K):
         q = np.zeros(N)
+        if quot is not None:
+            quot[j, live] = W[j, live] / d[live]
         q[live] = np.clip(np.rint(W[j, live] / d[live]), -127, 127)
         Q[j] = q.astype(np.int8)
         e = (W[j] - d * q) / U[j, j]
         W[j + 1:] -= np.outer(U[j, j + 1:], e)
+    if quot is not None:
+        return np.ascontiguousarray(Q.T), ws, quot
     return np.ascontiguousarray(Q.T), ws
 
 

@@ -77,6 +77,10 @@ def lib() -> ctypes.CDLL:
         L.sq_w8a8_linear_ln.argtypes = [P, I, I64, I64, I64, P, P, F, P, P, I64, P, P, I, I64, P,
                                         ctypes.c_size_t, ctypes.POINTER(_DebugOut), P, P]
         L.sq_fold_prev_linear.argtypes = [P, I64, P, I, I64, I64, P, I64, P, P, P]
+        L.sq_gptq_workspace_bytes.argtypes = [I64, I64, I64]
+        L.sq_gptq_workspace_bytes.restype = ctypes.c_size_t
+        L.sq_quant_weight_gptq.argtypes = [P, I, I64, I64, I, P, F, P, I, I64, I64, I64, P, F, P,
+                                           P, P, P, ctypes.c_size_t, P]
         L.sq_status_string.argtypes = [I]
         L.sq_status_string.restype = ctypes.c_char_p
         L.sq_abi_version.restype = I
@@ -382,3 +386,24 @@ def sq_fold_prev_linear(s, w_prev, w_out, *, bias=None, bias_out=None, stream=No
     _check(lib().sq_fold_prev_linear(_ptr(s), K, _ptr(w_prev), _dtype(w_prev), Kp, _ld(w_prev),
                                      _ptr(w_out), _ld(w_out), _ptr(bias), _ptr(bias_out),
                                      _stream(stream)), "sq_fold_prev_linear")
+
+
+# --- GPTQ on the migrated weight ------------------------------------------------
+
+def sq_gptq_workspace_bytes(t_cal: int, k: int, n: int) -> int:
+    return int(lib().sq_gptq_workspace_bytes(t_cal, k, n))
+
+
+def sq_quant_weight_gptq(x_cal, gamma_f, w, s, wq, w_scale, workspace, *, norm: bool = False,
+                         eps: float = 1e-6, damp: float = 0.01, row_rscale=None,
+                         stream=None) -> None:
+    """wq[N, K] int8 by GPTQ rounding of diag(s) W with the Hessian of the
+    calibration x^, w_scale[N] -- see sq_quant_weight_gptq."""
+    T, K = x_cal.shape
+    N = w.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().sq_quant_weight_gptq(_ptr(x_cal), _dtype(x_cal), T, _ld(x_cal),
+                                      SQ_NORM_RMS if norm else SQ_NORM_NONE, _ptr(gamma_f), eps,
+                                      _ptr(w), _dtype(w), K, N, _ld(w), _ptr(s), damp, _ptr(wq),
+                                      _ptr(w_scale), _ptr(row_rscale), _ptr(workspace), ws_bytes,
+                                      _stream(stream)), "sq_quant_weight_gptq")

@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libsqw8a8.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["sq_w8a8.hip", "k_calib.hip", "k_weight.hip", "k_actquant.hip", "k_gemm.hip",
-           "k_gemm_decode.hip"]
+           "k_gemm_decode.hip", "k_gptq.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

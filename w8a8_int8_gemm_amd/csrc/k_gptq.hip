@@ -1,0 +1,510 @@
+// k_gptq.hip -- GPTQ error-compensating rounding of the migrated weight on
+// gfx950 ("06 -- SmoothQuant", section 10: SmoothQuant migration first, then
+// GPTQ on the migrated weights; the pages name the step, the algorithm is the
+// published GPTQ).  Everything runs in fp64, the chip's full-rate vector
+// precision for this offline step.
+//
+//   1. H = X^T X over the calibration tokens' x^ (formed exactly as the
+//      activation quantizer forms it), lower 64 x 64 tiles only.
+//   2. Dead inputs (H_jj = 0) get H_jj = 1 and a zero weight row; then
+//      H += damp * mean(diag H) * I.
+//   3. GPTQ needs U, the upper Cholesky factor of H^-1 (H^-1 = U^T U).  With J
+//      the index reversal, A = J H J = L L^T (lower Cholesky) gives
+//      H = (J L J)(J L J)^T with J L J upper, so H^-1 = (J L^-1 J)^T (J L^-1 J)
+//      and U = J L^-1 J: one blocked Cholesky and one blocked triangular
+//      inverse, and U[j][k] is read as X[K-1-j][K-1-k] from X = L^-1.
+//   4. Rows of W^ (input channels) in blocks of 64: inside a block each row
+//      is rounded with the plain quantizer's per-channel step, its error
+//      e = (w - step * q) / U_jj is pushed onto the block's later rows, and
+//      the block's errors then update every later row at once (an fp64
+//      GEMM).  Output channels are independent, so workgroups split N.
+#include "sq_common.h"
+#include "sq_internal.h"
+
+namespace sqk {
+
+namespace {
+
+constexpr int NB = 64;          // tile / block edge
+constexpr int LDP = NB + 1;     // padded LDS row (fp64)
+
+// acc[a][b] += sum_k As[ty + 16a][k] * Bs[k][tx + 16b] over a 64 x 64 x 64 product
+__device__ __forceinline__ void mm64(const double (*As)[LDP], const double (*Bs)[LDP],
+                                     double (&acc)[4][4], int tx, int ty) {
+#pragma unroll 4
+  for (int k = 0; k < NB; ++k) {
+    double a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = As[ty + 16 * i][k];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = Bs[k][tx + 16 * i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+  }
+}
+
+__device__ __forceinline__ void zero4(double (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+}
+
+// block (ti, tj), ti >= tj, of a lower-triangular tile grid from a linear index
+__device__ __forceinline__ void lower_pair(int64_t idx, int& ti, int& tj) {
+  int i = (int)((sqrt(8.0 * (double)idx + 1.0) - 1.0) * 0.5);
+  while ((int64_t)(i + 1) * (i + 2) / 2 <= idx) ++i;
+  while ((int64_t)i * (i + 1) / 2 > idx) --i;
+  ti = i;
+  tj = (int)(idx - (int64_t)i * (i + 1) / 2);
+}
+
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double s = 0.0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) s += red[w];
+  return s;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// r_t of each calibration row, in the activation quantizer's own order
+// (lane l sums chunks l, l+64, ... with fused squares, then a wave sum), so the
+// Hessian sees the quantizer's x^ bit for bit.
+// ---------------------------------------------------------------------------
+template <class In>
+__global__ __launch_bounds__(256) void k_rms_rows(const typename In::elem* __restrict__ x,
+                                                  int64_t T, int64_t K, int64_t ld, float eps,
+                                                  float* __restrict__ r) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int64_t nchunk = K >> 3;
+  double ss = 0.0;
+  for (int64_t ch = lane; ch < nchunk; ch += 64) {
+    float v[8];
+    In::load8(x + t * ld + ch * 8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double dv = (double)v[i];
+      ss = fma(dv, dv, ss);
+    }
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) r[t] = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+}
+
+// ---------------------------------------------------------------------------
+// 1. Hessian, lower tiles: H[ti*64 + i][tj*64 + j] = sum_t x^[t][.] x^[t][.]
+// x^ = fp32(fp32(x * r_t) * g_k) (norm) or fp32(x * g_k); the fp32 products
+// are exact in fp64, so only the order of the sum differs from any other
+// evaluation.
+// ---------------------------------------------------------------------------
+template <class In, bool NORM>
+__global__ __launch_bounds__(256) void k_hessian(const typename In::elem* __restrict__ x,
+                                                 int64_t T, int64_t K, int64_t ld,
+                                                 const float* __restrict__ r,
+                                                 const float* __restrict__ g,
+                                                 double* __restrict__ H) {
+  __shared__ double As[NB][LDP];   // As[i][t] = x^[t0 + t][ti*64 + i]
+  __shared__ double Bs[NB][LDP];   // Bs[t][j] = x^[t0 + t][tj*64 + j]
+  int ti, tj;
+  lower_pair(blockIdx.x, ti, tj);
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  double acc[4][4];
+  zero4(acc);
+  // loader: thread -> (row lt = tid / 4, 16 columns at 16 * (tid % 4))
+  const int lt = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 16;
+  for (int64_t t0 = 0; t0 < T; t0 += NB) {
+    const int64_t t = t0 + lt;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int64_t col0 = (int64_t)(half == 0 ? ti : tj) * NB + lc;
+      float v[16];
+      if (t < T) {
+        In::load8(x + t * ld + col0, *reinterpret_cast<float(*)[8]>(&v[0]));
+        In::load8(x + t * ld + col0 + 8, *reinterpret_cast<float(*)[8]>(&v[8]));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = 0.0f;
+      }
+      const float rt = (NORM && t < T) ? r[t] : 1.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float u = NORM ? v[e] * rt : v[e];
+        const float xh = u * (g ? g[col0 + e] : 1.0f);
+        if (half == 0) As[lc + e][lt] = (double)xh;
+        else Bs[lt][lc + e] = (double)xh;
+      }
+    }
+    __syncthreads();
+    mm64(As, Bs, acc, tx, ty);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      H[((int64_t)ti * NB + ty + 16 * a) * K + (int64_t)tj * NB + tx + 16 * b] = acc[a][b];
+}
+
+// ---------------------------------------------------------------------------
+// 2. Dead inputs and damping (one workgroup): dg[j] = (H_jj == 0 ? 1 : H_jj)
+// + damp * mean_j(that value); dead[j] = 1 where H_jj == 0.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_hess_diag(const double* __restrict__ H, int64_t K,
+                                                   float damp, double* __restrict__ dg,
+                                                   unsigned char* __restrict__ dead) {
+  __shared__ double red[4];
+  double s = 0.0;
+  for (int64_t j = threadIdx.x; j < K; j += 256) {
+    const double h = H[j * K + j];
+    s += (h == 0.0) ? 1.0 : h;
+  }
+  const double mean = block_sum(s, red) / (double)K;
+  const double add = (double)damp * mean;
+  for (int64_t j = threadIdx.x; j < K; j += 256) {
+    const double h = H[j * K + j];
+    dead[j] = (h == 0.0) ? 1 : 0;
+    dg[j] = ((h == 0.0) ? 1.0 : h) + add;
+  }
+}
+
+// A = J H J, lower tiles: A[i][j] = H[K-1-i][K-1-j] = Hlow[K-1-j][K-1-i] for
+// i > j, the fixed diagonal on i == j, 0 above it.
+__global__ __launch_bounds__(256) void k_hess_reverse(const double* __restrict__ H, int64_t K,
+                                                      const double* __restrict__ dg,
+                                                      double* __restrict__ A) {
+  int ti, tj;
+  lower_pair(blockIdx.x, ti, tj);
+  for (int e = threadIdx.x; e < NB * NB; e += 256) {
+    const int64_t i = (int64_t)ti * NB + e / NB, j = (int64_t)tj * NB + e % NB;
+    double v;
+    if (i == j) v = dg[K - 1 - i];
+    else if (i > j) v = H[(K - 1 - j) * K + (K - 1 - i)];
+    else v = 0.0;
+    A[i * K + j] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. Blocked Cholesky of A (lower, in place) and the inverse of its factor.
+// ---------------------------------------------------------------------------
+// Diagonal block p: unblocked Cholesky in LDS, then its inverse (forward
+// substitution on the identity, one column per thread) into Dinv[p].
+__global__ __launch_bounds__(256) void k_chol_panel(double* __restrict__ A, int64_t K, int p,
+                                                    double* __restrict__ Dinv) {
+  __shared__ double L[NB][LDP];
+  __shared__ double X[NB][LDP];
+  const int64_t o = (int64_t)p * NB;
+  for (int e = threadIdx.x; e < NB * NB; e += 256) {
+    const int i = e / NB, j = e % NB;
+    L[i][j] = (j <= i) ? A[(o + i) * K + o + j] : 0.0;
+  }
+  __syncthreads();
+  for (int c = 0; c < NB; ++c) {
+    if (threadIdx.x == 0) L[c][c] = sqrt(L[c][c]);
+    __syncthreads();
+    const double d = L[c][c];
+    for (int i = c + 1 + (int)threadIdx.x; i < NB; i += 256) L[i][c] = L[i][c] / d;
+    __syncthreads();
+    // trailing update of the block's lower part
+    for (int e = threadIdx.x; e < NB * NB; e += 256) {
+      const int i = e / NB, j = e % NB;
+      if (j > c && j <= i) L[i][j] = L[i][j] - L[i][c] * L[j][c];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < NB) {   // column m of L^-1
+    const int m = threadIdx.x;
+    for (int i = 0; i < NB; ++i) {
+      double s = (i == m) ? 1.0 : 0.0;
+      for (int k = m; k < i; ++k) s = s - L[i][k] * X[k][m];
+      X[i][m] = (i < m) ? 0.0 : s / L[i][i];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < NB * NB; e += 256) {
+    const int i = e / NB, j = e % NB;
+    A[(o + i) * K + o + j] = L[i][j];
+    Dinv[((int64_t)p * NB + i) * NB + j] = X[i][j];
+  }
+}
+
+// Column panel below block p: L_ip = A_ip * (L_pp^-1)^T, block i = p + 1 + blockIdx.x.
+__global__ __launch_bounds__(256) void k_chol_trsm(double* __restrict__ A, int64_t K, int p,
+                                                   const double* __restrict__ Dinv) {
+  __shared__ double As[NB][LDP];
+  __shared__ double Bs[NB][LDP];
+  const int i = p + 1 + blockIdx.x;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int64_t ro = (int64_t)i * NB, co = (int64_t)p * NB;
+  for (int e = threadIdx.x; e < NB * NB; e += 256) {
+    const int a = e / NB, b = e % NB;
+    As[a][b] = A[(ro + a) * K + co + b];
+    Bs[a][b] = Dinv[((int64_t)p * NB + b) * NB + a];   // Bs[k][c] = Dinv[c][k]
+  }
+  __syncthreads();
+  double acc[4][4];
+  zero4(acc);
+  mm64(As, Bs, acc, tx, ty);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) A[(ro + ty + 16 * a) * K + co + tx + 16 * b] = acc[a][b];
+}
+
+// Trailing update: A_ij -= L_ip L_jp^T for p < j <= i.
+__global__ __launch_bounds__(256) void k_chol_syrk(double* __restrict__ A, int64_t K, int p) {
+  __shared__ double As[NB][LDP];
+  __shared__ double Bs[NB][LDP];
+  int i, j;
+  lower_pair(blockIdx.x, i, j);
+  i += p + 1;
+  j += p + 1;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int64_t co = (int64_t)p * NB;
+  for (int e = threadIdx.x; e < NB * NB; e += 256) {
+    const int a = e / NB, b = e % NB;
+    As[a][b] = A[((int64_t)i * NB + a) * K + co + b];
+    Bs[b][a] = A[((int64_t)j * NB + a) * K + co + b];   // Bs[k][c] = L_jp[c][k]
+  }
+  __syncthreads();
+  double acc[4][4];
+  zero4(acc);
+  mm64(As, Bs, acc, tx, ty);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      double* c = A + ((int64_t)i * NB + ty + 16 * a) * K + (int64_t)j * NB + tx + 16 * b;
+      *c = *c - acc[a][b];
+    }
+}
+
+// Block row i of X = L^-1 (X_ij for j <= blockIdx.x... j = blockIdx.x):
+// X_ii = Dinv[i]; X_ij = -Dinv[i] * sum_{k=j}^{i-1} L_ik X_kj.
+__global__ __launch_bounds__(256) void k_trinv_row(const double* __restrict__ A, int64_t K, int i,
+                                                   const double* __restrict__ Dinv,
+                                                   double* __restrict__ X) {
+  __shared__ double As[NB][LDP];
+  __shared__ double Bs[NB][LDP];
+  const int j = blockIdx.x;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int64_t ro = (int64_t)i * NB, co = (int64_t)j * NB;
+  if (j == i) {
+    for (int e = threadIdx.x; e < NB * NB; e += 256)
+      X[(ro + e / NB) * K + co + e % NB] = Dinv[(ro + e / NB) * NB + e % NB];
+    return;
+  }
+  double acc[4][4];
+  zero4(acc);
+  for (int k = j; k < i; ++k) {
+    for (int e = threadIdx.x; e < NB * NB; e += 256) {
+      const int a = e / NB, b = e % NB;
+      As[a][b] = A[(ro + a) * K + (int64_t)k * NB + b];   // L_ik
+      Bs[a][b] = X[((int64_t)k * NB + a) * K + co + b];   // X_kj
+    }
+    __syncthreads();
+    mm64(As, Bs, acc, tx, ty);
+    __syncthreads();
+  }
+  // X_ij = -Dinv[i] * acc
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) Bs[ty + 16 * a][tx + 16 * b] = acc[a][b];
+  for (int e = threadIdx.x; e < NB * NB; e += 256) As[e / NB][e % NB] = Dinv[(ro + e / NB) * NB + e % NB];
+  __syncthreads();
+  double out[4][4];
+  zero4(out);
+  mm64(As, Bs, out, tx, ty);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) X[(ro + ty + 16 * a) * K + co + tx + 16 * b] = -out[a][b];
+}
+
+// ---------------------------------------------------------------------------
+// 4. The rounding loop.  W64 [K, N] fp64 holds W^ = fp32(W * s) (dead rows 0).
+// ---------------------------------------------------------------------------
+template <class In>
+__global__ __launch_bounds__(256) void k_gptq_init(const typename In::elem* __restrict__ w,
+                                                   int64_t K, int64_t N, int64_t ld,
+                                                   const float* __restrict__ s,
+                                                   const unsigned char* __restrict__ dead,
+                                                   double* __restrict__ W64) {
+  const int64_t per = N >> 3;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= K * per) return;
+  const int64_t j = c / per, n0 = (c - j * per) * 8;
+  float v[8];
+  In::load8(w + j * ld + n0, v);
+  const float sj = s ? s[j] : 1.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) W64[j * N + n0 + e] = dead[j] ? 0.0 : (double)(v[e] * sj);
+}
+
+// Block b (rows b*64 .. +63) of the rounding, for output channels
+// blockIdx.x*64 .. +63: U[j][k] = X[K-1-j][K-1-k].
+__global__ __launch_bounds__(256) void k_gptq_block(double* __restrict__ W64, int64_t K,
+                                                    int64_t N, int b,
+                                                    const double* __restrict__ X,
+                                                    const float* __restrict__ wscale,
+                                                    int8_t* __restrict__ wq,
+                                                    double* __restrict__ E) {
+  __shared__ double Wb[NB][LDP];
+  __shared__ double Ub[NB][LDP];
+  __shared__ double Es[NB][LDP];
+  __shared__ int8_t Q[NB][NB + 4];
+  const int c = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  const int64_t n = (int64_t)blockIdx.x * NB + c;
+  const bool live = n < N;
+  const int64_t r0 = (int64_t)b * NB;
+  for (int kk = rg; kk < NB; kk += 4) {
+    Wb[kk][c] = live ? W64[(r0 + kk) * N + n] : 0.0;
+    Ub[kk][c] = (c >= kk) ? X[(K - 1 - r0 - kk) * K + (K - 1 - r0 - c)] : 0.0;
+  }
+  const double d = live ? (double)wscale[n] : 0.0;
+  __syncthreads();
+  for (int jj = 0; jj < NB; ++jj) {
+    if (rg == 0) {
+      const double wv = Wb[jj][c];
+      double q = 0.0;
+      if (d > 0.0) q = fmin(fmax(rint(wv / d), -127.0), 127.0);
+      Q[jj][c] = (int8_t)q;
+      Es[jj][c] = (wv - d * q) / Ub[jj][jj];
+    }
+    __syncthreads();
+    const double e = Es[jj][c];
+    for (int kk = jj + 1 + ((rg - jj - 1) & 3); kk < NB; kk += 4) Wb[kk][c] = Wb[kk][c] - Ub[jj][kk] * e;
+    __syncthreads();
+  }
+  if (live) {
+    // codes: output channel n, input channels r0 .. r0+63 (16 per row group)
+    int8_t* dst = wq + n * K + r0 + rg * 16;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dst[e] = Q[rg * 16 + e][c];
+    for (int kk = rg; kk < NB; kk += 4) E[(int64_t)kk * N + n] = Es[kk][c];
+  }
+}
+
+// Later rows: W64[i][n] -= sum_jj U[r0 + jj][i] * E[jj][n] for i >= r0 + 64;
+// tile (blockIdx.y, blockIdx.x) of 64 x 64.
+__global__ __launch_bounds__(256) void k_gptq_update(double* __restrict__ W64, int64_t K,
+                                                     int64_t N, int b,
+                                                     const double* __restrict__ X,
+                                                     const double* __restrict__ E) {
+  __shared__ double As[NB][LDP];   // As[i][jj] = U[r0 + jj][i0 + i]
+  __shared__ double Bs[NB][LDP];   // Bs[jj][c] = E[jj][n0 + c]
+  const int64_t r0 = (int64_t)b * NB;
+  const int64_t i0 = r0 + NB + (int64_t)blockIdx.y * NB;
+  const int64_t n0 = (int64_t)blockIdx.x * NB;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  for (int e = threadIdx.x; e < NB * NB; e += 256) {
+    const int a = e / NB, q = e % NB;
+    // U[r0 + q][i0 + a] = X[K-1-r0-q][K-1-i0-a] (i0 + a > r0 + q: lower part of X)
+    As[a][q] = X[(K - 1 - r0 - q) * K + (K - 1 - i0 - a)];
+    Bs[a][q] = (n0 + q < N) ? E[(int64_t)a * N + n0 + q] : 0.0;
+  }
+  __syncthreads();
+  double acc[4][4];
+  zero4(acc);
+  mm64(As, Bs, acc, tx, ty);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t nn = n0 + tx + 16 * q;
+      if (nn < N) {
+        double* p = W64 + (i0 + ty + 16 * a) * N + nn;
+        *p = *p - acc[a][q];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+size_t gptq_workspace_bytes(int64_t T, int64_t K, int64_t N) {
+  auto r256 = [](int64_t b) { return (size_t)((b + 255) & ~int64_t(255)); };
+  return r256(K * K * 8) * 2 + r256(K * NB * 8) + r256(K * 8) + r256(K) + r256(T * 4) +
+         r256(K * N * 8) + r256((int64_t)NB * N * 8);
+}
+
+void launch_gptq(const void* x, bool xbf16, int64_t T, int64_t ldx, bool norm,
+                 const float* gamma_f, float eps, const void* w, bool wbf16, int64_t K, int64_t N,
+                 int64_t ldw, const float* s, float damp, int8_t* wq, float* wscale,
+                 float* rrow_out, void* workspace, hipStream_t st) {
+  auto r256 = [](int64_t b) { return (size_t)((b + 255) & ~int64_t(255)); };
+  char* p = static_cast<char*>(workspace);
+  double* H = reinterpret_cast<double*>(p);            p += r256(K * K * 8);   // then X = L^-1
+  double* A = reinterpret_cast<double*>(p);            p += r256(K * K * 8);
+  double* Dinv = reinterpret_cast<double*>(p);         p += r256(K * NB * 8);
+  double* dg = reinterpret_cast<double*>(p);           p += r256(K * 8);
+  unsigned char* dead = reinterpret_cast<unsigned char*>(p); p += r256(K);
+  float* rr = rrow_out ? rrow_out : reinterpret_cast<float*>(p);  p += r256(T * 4);
+  double* W64 = reinterpret_cast<double*>(p);          p += r256(K * N * 8);
+  double* E = reinterpret_cast<double*>(p);
+  const int nt = (int)(K / NB);
+  const int64_t tiles = (int64_t)nt * (nt + 1) / 2;
+
+  // the plain quantizer's per-output-channel step of W^ = W * s
+  launch_fill_f32(wscale, N, 0.0f, st);
+  launch_col_absmax(w, wbf16, K, N, ldw, s, 127.0f, wscale, st);
+
+  // 1. Hessian
+  if (norm) {
+    const dim3 g((unsigned)((T + 3) / 4));
+    if (xbf16) hipLaunchKernelGGL(k_rms_rows<Bf16In>, g, dim3(256), 0, st, (const uint16_t*)x, T, K, ldx, eps, rr);
+    else hipLaunchKernelGGL(k_rms_rows<F32In>, g, dim3(256), 0, st, (const float*)x, T, K, ldx, eps, rr);
+  }
+  const dim3 gt((unsigned)tiles);
+  if (xbf16) {
+    if (norm) hipLaunchKernelGGL((k_hessian<Bf16In, true>), gt, dim3(256), 0, st, (const uint16_t*)x, T, K, ldx, rr, gamma_f, H);
+    else hipLaunchKernelGGL((k_hessian<Bf16In, false>), gt, dim3(256), 0, st, (const uint16_t*)x, T, K, ldx, rr, gamma_f, H);
+  } else {
+    if (norm) hipLaunchKernelGGL((k_hessian<F32In, true>), gt, dim3(256), 0, st, (const float*)x, T, K, ldx, rr, gamma_f, H);
+    else hipLaunchKernelGGL((k_hessian<F32In, false>), gt, dim3(256), 0, st, (const float*)x, T, K, ldx, rr, gamma_f, H);
+  }
+  // 2. dead inputs, damping, reversal
+  hipLaunchKernelGGL(k_hess_diag, dim3(1), dim3(256), 0, st, H, K, damp, dg, dead);
+  hipLaunchKernelGGL(k_hess_reverse, gt, dim3(256), 0, st, H, K, dg, A);
+  // 3. Cholesky of A, then X = L^-1 into H's storage
+  for (int q = 0; q < nt; ++q) {
+    hipLaunchKernelGGL(k_chol_panel, dim3(1), dim3(256), 0, st, A, K, q, Dinv);
+    const int rest = nt - q - 1;
+    if (rest > 0) {
+      hipLaunchKernelGGL(k_chol_trsm, dim3((unsigned)rest), dim3(256), 0, st, A, K, q, Dinv);
+      hipLaunchKernelGGL(k_chol_syrk, dim3((unsigned)((int64_t)rest * (rest + 1) / 2)), dim3(256),
+                         0, st, A, K, q);
+    }
+  }
+  for (int i = 0; i < nt; ++i)
+    hipLaunchKernelGGL(k_trinv_row, dim3((unsigned)(i + 1)), dim3(256), 0, st, A, K, i, Dinv, H);
+  // 4. rounding
+  {
+    const int64_t chunks = K * (N >> 3);
+    const dim3 g((unsigned)((chunks + 255) / 256));
+    if (wbf16) hipLaunchKernelGGL(k_gptq_init<Bf16In>, g, dim3(256), 0, st, (const uint16_t*)w, K, N, ldw, s, dead, W64);
+    else hipLaunchKernelGGL(k_gptq_init<F32In>, g, dim3(256), 0, st, (const float*)w, K, N, ldw, s, dead, W64);
+  }
+  const unsigned nslab = (unsigned)((N + NB - 1) / NB);
+  for (int b = 0; b < nt; ++b) {
+    hipLaunchKernelGGL(k_gptq_block, dim3(nslab), dim3(256), 0, st, W64, K, N, b, H, wscale, wq, E);
+    const int rest = nt - b - 1;
+    if (rest > 0)
+      hipLaunchKernelGGL(k_gptq_update, dim3(nslab, (unsigned)rest), dim3(256), 0, st, W64, K, N,
+                         b, H, E);
+  }
+}
+
+}  // namespace sqk

@@ -50,6 +50,13 @@ void launch_quant_act_ln(const void* x, bool bf16, int64_t T, int64_t K, int64_t
 void launch_static_scale(const float* a, const float* gamma_f, int64_t K, float qmax, float* out,
                          hipStream_t st);
 
+// k_gptq.hip: GPTQ rounding of W^ = W * s with the Hessian of the calibration x^
+size_t gptq_workspace_bytes(int64_t T, int64_t K, int64_t N);
+void launch_gptq(const void* x, bool xbf16, int64_t T, int64_t ldx, bool norm,
+                 const float* gamma_f, float eps, const void* w, bool wbf16, int64_t K, int64_t N,
+                 int64_t ldw, const float* s, float damp, int8_t* wq, float* wscale,
+                 float* rrow_out, void* workspace, hipStream_t st);
+
 // k_gemm.hip / k_gemm_decode.hip; out: 0 = bf16, 1 = fp32, 2 = int32 accumulators
 void launch_gemm(const int8_t* xq, const float* xs, int64_t T, int64_t K, const int8_t* wq,
                  const float* ws, int64_t N, const float* bias, void* y, int64_t ldy, int out,

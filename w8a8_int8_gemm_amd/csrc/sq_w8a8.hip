@@ -13,6 +13,7 @@ namespace {
 constexpr int64_t kMaxK = 65536;
 constexpr int64_t kMaxRows = int64_t(1) << 24;   // tokens (T) and output channels (N) per call
 constexpr int64_t kMaxNormCalibK = 8192;
+constexpr int64_t kMaxGptqK = 16384;   // the K x K fp64 Hessian and its factor: 2 GiB each
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline bool is_fp(sq_dtype d) { return d == SQ_F32 || d == SQ_BF16; }
@@ -376,6 +377,33 @@ sq_status sq_w8a8_linear_static_fp8(const void* x, sq_dtype x_dt, int64_t t, int
   return linear_impl(x, x_dt, t, k, ldx, norm, gamma_f, eps, x_scale_static, true,
                      reinterpret_cast<const int8_t*>(wq), w_scale, n, bias, y, y_dt, ldy,
                      workspace, ws_bytes, dbg, stream);
+}
+
+// --- GPTQ on the migrated weight -----------------------------------------------
+
+size_t sq_gptq_workspace_bytes(int64_t t_cal, int64_t k, int64_t n) {
+  if (t_cal <= 0 || k <= 0 || n <= 0) return 0;
+  return sqk::gptq_workspace_bytes(t_cal, k, n);
+}
+
+sq_status sq_quant_weight_gptq(const void* x_cal, sq_dtype x_dt, int64_t t_cal, int64_t ldx,
+                               sq_norm norm, const float* gamma_f, float eps, const void* w,
+                               sq_dtype w_dt, int64_t k, int64_t n, int64_t ldw, const float* s,
+                               float damp, int8_t* wq, float* w_scale, float* row_rscale,
+                               void* workspace, size_t ws_bytes, hipStream_t stream) {
+  SQ_TRY(check_act(x_cal, x_dt, t_cal, k, ldx, norm, eps));
+  SQ_TRY(check_mat(w, w_dt, k, n, ldw));
+  if (wq == nullptr || w_scale == nullptr) return SQ_ERR_NULL;
+  if (t_cal == 0 || n == 0) return SQ_ERR_SHAPE;
+  if (k > kMaxGptqK || n % 8 != 0 || !aligned16(wq)) return SQ_ERR_UNSUPPORTED;
+  if (!(damp >= 0.0f && isfinite(damp))) return SQ_ERR_SHAPE;
+  if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0 ||
+      ws_bytes < sqk::gptq_workspace_bytes(t_cal, k, n))
+    return SQ_ERR_WORKSPACE;
+  sqk::launch_gptq(x_cal, x_dt == SQ_BF16, t_cal, ldx, norm == SQ_NORM_RMS, gamma_f, eps, w,
+                   w_dt == SQ_BF16, k, n, ldw, s, damp, wq, w_scale,
+                   norm == SQ_NORM_RMS ? row_rscale : nullptr, workspace, stream);
+  return hip_status();
 }
 
 // --- LayerNorm form and the fold into the previous linear --------------------
