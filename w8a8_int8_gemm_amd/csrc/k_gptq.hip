@@ -11,8 +11,9 @@
 //   3. GPTQ needs U, the upper Cholesky factor of H^-1 (H^-1 = U^T U).  With J
 //      the index reversal, A = J H J = L L^T (lower Cholesky) gives
 //      H = (J L J)(J L J)^T with J L J upper, so H^-1 = (J L^-1 J)^T (J L^-1 J)
-//      and U = J L^-1 J: one blocked Cholesky and one blocked triangular
-//      inverse, and U[j][k] is read as X[K-1-j][K-1-k] from X = L^-1.
+//      and U = J L^-1 J: one blocked Cholesky and one recursive triangular
+//      inverse (X21 = -X22 L21 X11 on halves, as fp64 GEMMs), and U[j][k] is
+//      read as X[K-1-j][K-1-k] from X = L^-1.
 //   4. Rows of W^ (input channels) in blocks of 64: inside a block each row
 //      is rounded with the plain quantizer's per-channel step, its error
 //      e = (w - step * q) / U_jj is pushed onto the block's later rows, and
@@ -197,45 +198,53 @@ __global__ __launch_bounds__(256) void k_hess_reverse(const double* __restrict__
 // ---------------------------------------------------------------------------
 // 3. Blocked Cholesky of A (lower, in place) and the inverse of its factor.
 // ---------------------------------------------------------------------------
-// Diagonal block p: unblocked Cholesky in LDS, then its inverse (forward
-// substitution on the identity, one column per thread) into Dinv[p].
-__global__ __launch_bounds__(256) void k_chol_panel(double* __restrict__ A, int64_t K, int p,
-                                                    double* __restrict__ Dinv) {
+// Diagonal block p, one wave: lane i holds row i of the 64 x 64 block in
+// VGPRs.  Right-looking Cholesky, column c: the pivot and the column values
+// L[j][c] reach every lane by readlane; then the factor's inverse, lane m
+// forward-substituting column m against the factor staged in LDS (every lane
+// reads the same L[i][k] at once).  Written to A (lower, zeros above) and
+// Dinv[p].
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), lane);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__global__ __launch_bounds__(64) void k_chol_panel(double* __restrict__ A, int64_t K, int p,
+                                                   double* __restrict__ Dinv) {
   __shared__ double L[NB][LDP];
-  __shared__ double X[NB][LDP];
+  const int i = threadIdx.x;
   const int64_t o = (int64_t)p * NB;
-  for (int e = threadIdx.x; e < NB * NB; e += 256) {
-    const int i = e / NB, j = e % NB;
-    L[i][j] = (j <= i) ? A[(o + i) * K + o + j] : 0.0;
-  }
-  __syncthreads();
+  double r[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) r[j] = A[(o + i) * K + o + j];   // upper part: never read
+#pragma unroll
   for (int c = 0; c < NB; ++c) {
-    if (threadIdx.x == 0) L[c][c] = sqrt(L[c][c]);
-    __syncthreads();
-    const double d = L[c][c];
-    for (int i = c + 1 + (int)threadIdx.x; i < NB; i += 256) L[i][c] = L[i][c] / d;
-    __syncthreads();
-    // trailing update of the block's lower part
-    for (int e = threadIdx.x; e < NB * NB; e += 256) {
-      const int i = e / NB, j = e % NB;
-      if (j > c && j <= i) L[i][j] = L[i][j] - L[i][c] * L[j][c];
-    }
-    __syncthreads();
+    const double d = sqrt(readlane_f64(r[c], c));
+    const double lc = (i == c) ? d : r[c] / d;
+    r[c] = lc;
+#pragma unroll
+    for (int j = c + 1; j < NB; ++j) r[j] = r[j] - lc * readlane_f64(lc, j);
   }
-  if (threadIdx.x < NB) {   // column m of L^-1
-    const int m = threadIdx.x;
-    for (int i = 0; i < NB; ++i) {
-      double s = (i == m) ? 1.0 : 0.0;
-      for (int k = m; k < i; ++k) s = s - L[i][k] * X[k][m];
-      X[i][m] = (i < m) ? 0.0 : s / L[i][i];
-    }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const double v = (j <= i) ? r[j] : 0.0;
+    L[i][j] = v;
+    A[(o + i) * K + o + j] = v;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < NB * NB; e += 256) {
-    const int i = e / NB, j = e % NB;
-    A[(o + i) * K + o + j] = L[i][j];
-    Dinv[((int64_t)p * NB + i) * NB + j] = X[i][j];
+  // column m = i of L^-1: x[k] = 0 for k < m follows from the zero right side
+  double x[NB];
+#pragma unroll
+  for (int a = 0; a < NB; ++a) {
+    double sum = (a == i) ? 1.0 : 0.0;
+#pragma unroll
+    for (int k = 0; k < a; ++k) sum = sum - L[a][k] * x[k];
+    x[a] = sum / L[a][a];
   }
+#pragma unroll
+  for (int a = 0; a < NB; ++a) Dinv[(o + a) * NB + i] = x[a];
 }
 
 // Column panel below block p: L_ip = A_ip * (L_pp^-1)^T, block i = p + 1 + blockIdx.x.
@@ -289,47 +298,48 @@ __global__ __launch_bounds__(256) void k_chol_syrk(double* __restrict__ A, int64
     }
 }
 
-// Block row i of X = L^-1 (X_ij for j <= blockIdx.x... j = blockIdx.x):
-// X_ii = Dinv[i]; X_ij = -Dinv[i] * sum_{k=j}^{i-1} L_ik X_kj.
-__global__ __launch_bounds__(256) void k_trinv_row(const double* __restrict__ A, int64_t K, int i,
-                                                   const double* __restrict__ Dinv,
-                                                   double* __restrict__ X) {
+// C = alpha * A B + beta * C on 64 x 64 tiles (M, N, Kd multiples of 64),
+// row-major with leading dimensions; tile (blockIdx.y, blockIdx.x).  Used for
+// the triangular inverse and for the deferred GPTQ updates.
+__global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t Kd, double alpha,
+                                               const double* __restrict__ A, int64_t lda,
+                                               const double* __restrict__ B, int64_t ldb,
+                                               double beta, double* __restrict__ C, int64_t ldc) {
   __shared__ double As[NB][LDP];
   __shared__ double Bs[NB][LDP];
-  const int j = blockIdx.x;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  const int64_t ro = (int64_t)i * NB, co = (int64_t)j * NB;
-  if (j == i) {
-    for (int e = threadIdx.x; e < NB * NB; e += 256)
-      X[(ro + e / NB) * K + co + e % NB] = Dinv[(ro + e / NB) * NB + e % NB];
-    return;
-  }
+  const int64_t m0 = (int64_t)blockIdx.y * NB, n0 = (int64_t)blockIdx.x * NB;
   double acc[4][4];
   zero4(acc);
-  for (int k = j; k < i; ++k) {
+  for (int64_t k0 = 0; k0 < Kd; k0 += NB) {
     for (int e = threadIdx.x; e < NB * NB; e += 256) {
       const int a = e / NB, b = e % NB;
-      As[a][b] = A[(ro + a) * K + (int64_t)k * NB + b];   // L_ik
-      Bs[a][b] = X[((int64_t)k * NB + a) * K + co + b];   // X_kj
+      As[a][b] = A[(m0 + a) * lda + k0 + b];
+      Bs[a][b] = B[(k0 + a) * ldb + n0 + b];
     }
     __syncthreads();
     mm64(As, Bs, acc, tx, ty);
     __syncthreads();
   }
-  // X_ij = -Dinv[i] * acc
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) Bs[ty + 16 * a][tx + 16 * b] = acc[a][b];
-  for (int e = threadIdx.x; e < NB * NB; e += 256) As[e / NB][e % NB] = Dinv[(ro + e / NB) * NB + e % NB];
-  __syncthreads();
-  double out[4][4];
-  zero4(out);
-  mm64(As, Bs, out, tx, ty);
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) X[(ro + ty + 16 * a) * K + co + tx + 16 * b] = -out[a][b];
+    for (int b = 0; b < 4; ++b) {
+      double* c = C + (m0 + ty + 16 * a) * ldc + n0 + tx + 16 * b;
+      const double v = alpha * acc[a][b];
+      *c = (beta == 0.0) ? v : v + beta * *c;
+    }
+}
+
+// X = L^-1 before the recursion: X_ii = Dinv[i], every other block 0 (the
+// products below read whole square ranges of X, upper blocks included);
+// block (blockIdx.y, blockIdx.x)
+__global__ __launch_bounds__(256) void k_trinv_init(int64_t K, const double* __restrict__ Dinv,
+                                                    double* __restrict__ X) {
+  const int64_t ro = (int64_t)blockIdx.y * NB, co = (int64_t)blockIdx.x * NB;
+  const bool diag = blockIdx.x == blockIdx.y;
+  for (int e = threadIdx.x; e < NB * NB; e += 256)
+    X[(ro + e / NB) * K + co + e % NB] = diag ? Dinv[(ro + e / NB) * NB + e % NB] : 0.0;
 }
 
 // ---------------------------------------------------------------------------
@@ -437,7 +447,25 @@ __global__ __launch_bounds__(256) void k_gptq_update(double* __restrict__ W64, i
 size_t gptq_workspace_bytes(int64_t T, int64_t K, int64_t N) {
   auto r256 = [](int64_t b) { return (size_t)((b + 255) & ~int64_t(255)); };
   return r256(K * K * 8) * 2 + r256(K * NB * 8) + r256(K * 8) + r256(K) + r256(T * 4) +
-         r256(K * N * 8) + r256((int64_t)NB * N * 8);
+         r256(K * N * 8) + r256((int64_t)NB * N * 8) + r256(K * K * 2);
+}
+
+// X = L^-1 on the block range [b0, b0 + nb) (diagonal blocks already in X):
+// for L = [[L11, 0], [L21, L22]], X21 = -X22 (L21 X11).
+static void trinv_rec(const double* L, double* X, double* tmp, int64_t K, int b0, int nb,
+                      hipStream_t st) {
+  if (nb <= 1) return;
+  const int h = nb / 2, h2 = nb - h;
+  trinv_rec(L, X, tmp, K, b0, h, st);
+  trinv_rec(L, X, tmp, K, b0 + h, h2, st);
+  const int64_t o1 = (int64_t)b0 * NB, o2 = (int64_t)(b0 + h) * NB;
+  const int64_t s1 = (int64_t)h * NB, s2 = (int64_t)h2 * NB;
+  // tmp [s2, s1] = L21 X11
+  hipLaunchKernelGGL(k_dgemm, dim3((unsigned)h, (unsigned)h2), dim3(256), 0, st, s2, s1, s1, 1.0,
+                     L + o2 * K + o1, K, X + o1 * K + o1, K, 0.0, tmp, s1);
+  // X21 = -X22 tmp
+  hipLaunchKernelGGL(k_dgemm, dim3((unsigned)h, (unsigned)h2), dim3(256), 0, st, s2, s1, s2, -1.0,
+                     X + o2 * K + o2, K, tmp, s1, 0.0, X + o2 * K + o1, K);
 }
 
 void launch_gptq(const void* x, bool xbf16, int64_t T, int64_t ldx, bool norm,
@@ -453,7 +481,8 @@ void launch_gptq(const void* x, bool xbf16, int64_t T, int64_t ldx, bool norm,
   unsigned char* dead = reinterpret_cast<unsigned char*>(p); p += r256(K);
   float* rr = rrow_out ? rrow_out : reinterpret_cast<float*>(p);  p += r256(T * 4);
   double* W64 = reinterpret_cast<double*>(p);          p += r256(K * N * 8);
-  double* E = reinterpret_cast<double*>(p);
+  double* E = reinterpret_cast<double*>(p);             p += r256((int64_t)NB * N * 8);
+  double* tmp = reinterpret_cast<double*>(p);
   const int nt = (int)(K / NB);
   const int64_t tiles = (int64_t)nt * (nt + 1) / 2;
 
@@ -480,7 +509,7 @@ void launch_gptq(const void* x, bool xbf16, int64_t T, int64_t ldx, bool norm,
   hipLaunchKernelGGL(k_hess_reverse, gt, dim3(256), 0, st, H, K, dg, A);
   // 3. Cholesky of A, then X = L^-1 into H's storage
   for (int q = 0; q < nt; ++q) {
-    hipLaunchKernelGGL(k_chol_panel, dim3(1), dim3(256), 0, st, A, K, q, Dinv);
+    hipLaunchKernelGGL(k_chol_panel, dim3(1), dim3(64), 0, st, A, K, q, Dinv);
     const int rest = nt - q - 1;
     if (rest > 0) {
       hipLaunchKernelGGL(k_chol_trsm, dim3((unsigned)rest), dim3(256), 0, st, A, K, q, Dinv);
@@ -488,8 +517,8 @@ void launch_gptq(const void* x, bool xbf16, int64_t T, int64_t ldx, bool norm,
                          0, st, A, K, q);
     }
   }
-  for (int i = 0; i < nt; ++i)
-    hipLaunchKernelGGL(k_trinv_row, dim3((unsigned)(i + 1)), dim3(256), 0, st, A, K, i, Dinv, H);
+  hipLaunchKernelGGL(k_trinv_init, dim3((unsigned)nt, (unsigned)nt), dim3(256), 0, st, K, Dinv, H);
+  trinv_rec(A, H, tmp, K, 0, nt, st);
   // 4. rounding
   {
     const int64_t chunks = K * (N >> 3);
