@@ -71,6 +71,9 @@ def _parse():
                     help="instead of benchmarking, run only the headline GEMM back to back for "
                          "this long (for sampling power and clocks from outside) and print the "
                          "time per launch")
+    ap.add_argument("--only", choices=("gptq", "decoder_layer"), default=None,
+                    help="instead of benchmarking, run only this extra and print its JSON "
+                         "(for profiling one part on its own)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run one plain elementwise copy kernel over "
                          "this many MiB (reads and writes that many bytes): the reference "
@@ -639,6 +642,12 @@ def main():
 
     if args.gemm_loop > 0:
         gemm_loop(sq, torch, inp, wl, d, dev, args.gemm_loop)
+        return
+    if args.only == "gptq":
+        print(json.dumps(gptq_timing(sq, torch, inp, wl, d, dev)), flush=True)
+        return
+    if args.only == "decoder_layer":
+        print(json.dumps(block_timing(sq, torch, dev)), flush=True)
         return
     nsets = max(1, args.sets)
     sets = [(d(inp.x_cal), d(inp.x), d(inp.w)) for _ in range(nsets)]

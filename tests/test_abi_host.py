@@ -214,6 +214,32 @@ def test_layernorm_and_fold_prev_validation(L):
     assert fp(A16, 64, A16, sq.SQ_I8, 8, 64, A16, 64, None, None, None) == sq.SQ_ERR_DTYPE
 
 
+def test_gptq_validation(L):
+    g = L.sq_quant_weight_gptq
+    ws = L.sq_gptq_workspace_bytes(8, 64, 64)
+    assert ws > 64 * 64 * 8 * 2
+    assert L.sq_gptq_workspace_bytes(0, 64, 64) == 0
+    args = [A16, sq.SQ_BF16, 8, 64, 0, None, 1e-6, A16, sq.SQ_BF16, 64, 64, 64, None, 0.01, A16,
+            A16, None, A16, ws, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return g(*a)
+
+    assert call(a14=None) == sq.SQ_ERR_NULL                   # wq
+    assert call(a15=None) == sq.SQ_ERR_NULL                   # w_scale
+    assert call(a7=None) == sq.SQ_ERR_NULL                    # w
+    assert call(a2=0) == sq.SQ_ERR_SHAPE                      # no calibration tokens
+    assert call(a13=-1.0) == sq.SQ_ERR_SHAPE                  # damp
+    assert call(a10=12, a11=16) == sq.SQ_ERR_UNSUPPORTED      # n % 8
+    assert call(a9=16384 + 64, a3=16448, a11=64) == sq.SQ_ERR_UNSUPPORTED   # k too large
+    assert call(a17=None) == sq.SQ_ERR_WORKSPACE
+    assert call(a18=ws - 1) == sq.SQ_ERR_WORKSPACE
+    assert call(a17=MIS) == sq.SQ_ERR_WORKSPACE
+
+
 def test_row_limits(L):
     big = (1 << 24) + 1
     assert L.sq_quant_act(A16, sq.SQ_BF16, big, 64, 64, 0, None, 1e-6, A16, A16, None,
