@@ -57,7 +57,8 @@ def test_quant_act_ln(T, K, dt):
     np.testing.assert_array_equal(to_np(xq), q_ref)
 
 
-@pytest.mark.parametrize("K,dt", [(512, "bf16"), (4096, "bf16"), (1344, "f32"), (8192, "bf16")])
+@pytest.mark.parametrize("K,dt", [(512, "bf16"), (4096, "bf16"), (1344, "f32"), (8192, "bf16"),
+                                  (4096, "f32"), (8192, "f32")])
 def test_calibrate_and_fold_ln(K, dt):
     wl, inp = _ln_inputs(8, K, 96, 300, dt)
     say(f"ln calibrate K={K} {dt}")
