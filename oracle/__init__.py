@@ -398,7 +398,8 @@ def smoothed_act(x: np.ndarray, gamma_f=None, *, norm: bool = False,
     return out
 
 
-def gptq(w_hat: np.ndarray, xhat: np.ndarray, *, damp: float = 0.01, return_quotients=False):
+def gptq(w_hat: np.ndarray, xhat: np.ndarray, *, damp: float = 0.01, return_quotients=False,
+         columns: Optional[np.ndarray] = None):
     """GPTQ error-compensating rounding of the migrated weight ("06 --
     SmoothQuant", section 10: SmoothQuant migration first, then GPTQ on the
     migrated weights).  The pages name the step only; this follows the
@@ -414,9 +415,13 @@ def gptq(w_hat: np.ndarray, xhat: np.ndarray, *, damp: float = 0.01, return_quot
           and every later row k takes W[k,:] -= U_jk * e.
     damp is taken as an fp32 value (the library's argument type).
     w_hat [K,N] fp32, xhat [T,K] fp32.  Returns (qw [N,K] int8, w_scale [N]),
-    plus the quotients W[j,n] / w_scale[n] the rounding saw [K,N] when asked."""
+    plus the quotients W[j,n] / w_scale[n] the rounding saw [K,N] when asked.
+    Output channels never interact, so ``columns`` (indices) computes only
+    those channels; the results are then [len(columns), ...] in that order."""
     damp = float(np.float32(damp))
     W = np.asarray(w_hat, np.float32)
+    if columns is not None:
+        W = np.ascontiguousarray(W[:, np.asarray(columns)])
     K, N = W.shape
     ws = (np.abs(W).max(axis=0) / np.float32(127)).astype(np.float32)
     X = np.asarray(xhat, np.float32).astype(np.float64)

@@ -835,3 +835,16 @@ def test_gptq_dead_inputs_and_zero_columns():
     w[:, 3] = 0.0                                   # an output channel with no weight
     q, ws = oracle.gptq(w, x)
     assert not q[:, 5].any() and not q[3].any() and ws[3] == 0
+
+
+def test_gptq_output_channels_are_independent():
+    # the rounding of one output channel never reads another's weights: the
+    # same codes come out of the full weight and of any subset of its columns
+    rng = np.random.default_rng(65)
+    x = (rng.standard_normal((120, 48)) @ rng.standard_normal((48, 48))).astype(np.float32)
+    w = (rng.standard_normal((48, 30)) * 0.05).astype(np.float32)
+    q, ws = oracle.gptq(w, x)
+    cols = np.array([29, 0, 11, 12])
+    qc, wc = oracle.gptq(w, x, columns=cols)
+    np.testing.assert_array_equal(qc, q[cols])
+    np.testing.assert_array_equal(wc, ws[cols])
