@@ -216,6 +216,29 @@ def alpha_sweep(sq, torch, inp, wl, x_cal, x, w, bias, dev, sample=256):
     return res
 
 
+def vendor_int8_gemm(torch, xq, wq, iters=20):
+    """Reference point only: the vendor library's INT8 GEMM (torch._int_mm,
+    hipBLASLt on this stack) on the same codes, int32 output without the
+    epilogue, event-timed."""
+    wt = wq.t()
+    try:
+        torch._int_mm(xq, wt)
+    except Exception as e:  # noqa: BLE001 -- a missing backend is reported, not fatal
+        return {"error": str(e)[:200]}
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        torch._int_mm(xq, wt)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    T, K = xq.shape
+    N = wq.shape[0]
+    return {"op": "torch._int_mm (hipBLASLt), int32 out, same shape", "us": us,
+            "tops": 2.0 * T * K * N / (us * 1e-6) / 1e12}
+
+
 def fp8_timing(sq, torch, sets, wl, s, gp, bias, dev, iters=20):
     """Event times of the FP8 E4M3 weight and activation quantizers and the
     FP8 GEMM on the headline shape (rotating input sets), the GEMM against
@@ -750,6 +773,7 @@ def main():
                                                                  dev)
         out["decode_gemm"] = decode_gemm(sq, torch, dev)
         out["fp8"] = fp8_timing(sq, torch, sets, wl, s, gp, bias, dev)
+        out["vendor_int8_gemm"] = vendor_int8_gemm(torch, xq, wq)
         out["decoder_layer"] = block_timing(sq, torch, dev)
         out["decode_calibration"] = decode_calibration(sq, torch, dev)
         out["configs"] = {n: config_step(sq, torch, dev, n) for n in ("rmsnorm_qkv", "gate_up")}
