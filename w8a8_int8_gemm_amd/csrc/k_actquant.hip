@@ -31,8 +31,6 @@
 
 namespace sqk {
 
-constexpr float kTieBand = 0.5f - 0x1p-15f;
-
 // codes of 8 values of one token by the reciprocal; `d` > 0, `rc` = fp32(1/d)
 // finite.  `near_tie` is set when some quotient is within 2^-15 of a
 // half-integer: those 8 codes must then be recomputed with quant8_div.

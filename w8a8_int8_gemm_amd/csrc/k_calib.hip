@@ -288,9 +288,12 @@ __global__ __launch_bounds__(256) void k_ln_act_absmax(const typename In::elem* 
 }
 
 // ---------------------------------------------------------------------------
-// Weight row absmax and smoothing factor.  One wave per input channel j
-// (row j of the [K, N] weight).  s_j = fp32(a_j^alpha / w_j^(1-alpha)) in
-// fp64, floored at 1e-5; s_j = 1 for an all-zero row.
+// Weight row absmax and smoothing factor.  A workgroup of 4 waves takes 16
+// input channels (rows j of the [K, N] weight); each wave streams 4 rows at
+// once, U 16-byte loads per row in flight.  s_j = fp32(a_j^alpha /
+// w_j^(1-alpha)) in fp64, floored at 1e-5; s_j = 1 for an all-zero row.  The
+// fp64 powers run one lane per row, 16 rows at a time, after the maxima meet
+// in LDS: a serial power per row would hold a whole wave for each row.
 // ---------------------------------------------------------------------------
 template <class In, int U>
 __global__ __launch_bounds__(256) void k_wrow_absmax_s(const typename In::elem* __restrict__ w,
@@ -298,37 +301,51 @@ __global__ __launch_bounds__(256) void k_wrow_absmax_s(const typename In::elem* 
                                                        const float* __restrict__ a, float alpha,
                                                        float* __restrict__ wmax,
                                                        float* __restrict__ s) {
+  __shared__ float rmax[16];
   const int lane = threadIdx.x & 63;
-  const int64_t j = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (j >= K) return;
-  const typename In::elem* row = w + j * ld;
-  float mx = 0.0f;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t j0 = (int64_t)blockIdx.x * 16 + wave * 4;   // K % 16 == 0: all 4 rows exist
+  float mx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   int64_t c = (int64_t)lane * 8;
   for (; c + (U - 1) * 512 < N; c += U * 512) {
-    typename In::Raw raw[U];
+    typename In::Raw raw[4][U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) raw[u] = In::raw8(row + c + u * 512);
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float v[8];
-      In::widen(raw[u], v);
+      for (int u = 0; u < U; ++u) raw[q][u] = In::raw8(w + (j0 + q) * ld + c + u * 512);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(v[i]));
-    }
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float v[8];
+        In::widen(raw[q][u], v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx[q] = fmaxf(mx[q], fabsf(v[i]));
+      }
   }
   for (; c < N; c += 512) {
-    float v[8];
-    In::load8(row + c, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(v[i]));
+    for (int q = 0; q < 4; ++q) {
+      float v[8];
+      In::load8(w + (j0 + q) * ld + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx[q] = fmaxf(mx[q], fabsf(v[i]));
+    }
   }
-  mx = wave_max(mx);
-  if (lane == 0) {
-    wmax[j] = mx;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) mx[q] = wave_max(mx[q]);
+  if (lane == 0)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rmax[wave * 4 + q] = mx[q];
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const int64_t j = (int64_t)blockIdx.x * 16 + threadIdx.x;
+    const float m = rmax[threadIdx.x];
+    wmax[j] = m;
     float sj = 1.0f;
-    if (mx != 0.0f) {
+    if (m != 0.0f) {
       const double al = (double)alpha;
-      const double q = pow((double)a[j], al) / pow((double)mx, 1.0 - al);
+      const double q = pow((double)a[j], al) / pow((double)m, 1.0 - al);
       const float f = (float)q;
       sj = f < 1e-5f ? 1e-5f : f;
     }
@@ -442,7 +459,7 @@ void launch_ln_act_absmax(const void* h, bool bf16, int64_t rows, int64_t K, int
 void launch_wrow_absmax_s(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
                           const float* a, float alpha, float* wmax, float* s, hipStream_t st) {
   if (K <= 0) return;
-  const dim3 grid((unsigned)((K + 3) / 4));
+  const dim3 grid((unsigned)(K / 16));   // K % 64 == 0
   if (bf16)
     hipLaunchKernelGGL((k_wrow_absmax_s<Bf16In, 8>), grid, dim3(256), 0, st, (const uint16_t*)w,
                        K, N, ld, a, alpha, wmax, s);

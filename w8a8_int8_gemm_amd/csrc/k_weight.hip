@@ -180,6 +180,185 @@ __global__ __launch_bounds__(256) void k_quant_weight_t(const typename In::elem*
 }
 
 // ---------------------------------------------------------------------------
+// One-launch quantization of a bf16 weight with K <= 4096.  A workgroup of NT
+// threads owns a strip of 16 output channels (columns n0 .. n0+15 of the
+// [K, N] weight) and holds the whole strip in registers as W^ = W * s: thread
+// t = 2*rt + h has the 8 columns n0 + 8h .. +7 of the rows 4*(rt + RT*m) + r
+// (RT = NT/2 row threads, m < M, r < 4), all loads in flight at once.  The
+// column maxima of |W^| are reduced across the workgroup and written as the
+// steps directly: the strip is the only writer of its columns, so there is
+// no fill and no atomic.  The codes are packed four rows to a dword into an
+// LDS tile [16][2048 bytes] and written out K-contiguous, 2048 values of k at
+// a time.  Strips go to the XCDs in contiguous runs, so the four strips that
+// share the 128-byte lines of a row share one L2.
+//
+// INT8 rounding by the reciprocal of the step (kTieBand): the bound there
+// holds since |W^ / Delta| <= 127 / (1 - 2^-24) < 128 whenever 1/Delta is
+// finite (Delta > 2^-128, so its own rounding error is below 2^-22 of it).
+// y + 1.5 * 2^23 rounds y to an integer, ties to even, and leaves that integer
+// in the low bits of the sum: its low byte is the code, and subtracting the
+// constant back gives rint(y) exactly for the tie check.  |y| < 127.5, so no
+// clamp is needed on this path.  FP8 takes the IEEE quotient and the
+// hardware's nearest-E4M3 conversion, as k_quant_weight_t does.
+// ---------------------------------------------------------------------------
+template <int NT, int M, bool kRowScale, bool F8>
+__global__ __launch_bounds__(NT) void k_quant_weight_strip(const uint16_t* __restrict__ w,
+                                                           int64_t K, int64_t N, int64_t ld,
+                                                           const float* __restrict__ s,
+                                                           float qdiv, float* __restrict__ wscale,
+                                                           int8_t* __restrict__ wq, int nstrips) {
+  constexpr int RT = NT / 2;       // row threads; 4*RT rows per m
+  constexpr int NW = NT / kWave;
+  constexpr int TW = 512;          // tile width in dwords: 2048 k
+  constexpr int MPP = TW / RT;     // m groups per tile
+  constexpr int LDT = TW + 4;      // padded tile row: the two 8-column halves on other banks
+  static_assert(MPP >= 1 && TW % RT == 0, "tile covers whole m groups");
+  __shared__ uint32_t tile[16 * LDT];
+  __shared__ float red[NW][16];
+  __shared__ float dsh[16];
+  const int t = threadIdx.x;
+  const int h = t & 1, rt = t >> 1;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int b = blockIdx.x;
+  const int strip = (nstrips & 7) == 0 ? (b & 7) * (nstrips >> 3) + (b >> 3) : b;
+  const int64_t n0 = (int64_t)strip * 16;
+  const int64_t nb = n0 + 8 * h;
+  const bool ncol = nb < N;   // N % 8 == 0: a thread's 8 columns are all valid or none
+  const int64_t kq = K >> 2;  // groups of 4 rows (K % 64 == 0)
+
+  // The whole strip.  Rows past K read row K-1 again (a duplicate cannot
+  // change a maximum) and columns past N read column 0 (those maxima belong
+  // to no column); neither is ever written out.
+  float wh[M][4][8];
+  {
+    Bf16In::Raw raw[M][4];
+    float sk[M][4];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t k = min(4 * ((int64_t)rt + RT * m) + r, K - 1);
+        raw[m][r] = Bf16In::raw8(w + k * ld + (ncol ? nb : 0));
+        sk[m][r] = kRowScale ? s[k] : 1.0f;
+      }
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v[8];
+        Bf16In::widen(raw[m][r], v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wh[m][r][i] = kRowScale ? v[i] * sk[m][r] : v[i];
+      }
+  }
+  float mx[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mx[i] = 0.0f;
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(wh[m][r][i]));
+  // lanes of equal h first, then the waves through LDS
+#pragma unroll
+  for (int off = 2; off < kWave; off <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], off, kWave));
+  if (lane < 2)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[wave][lane * 8 + i] = mx[i];
+  __syncthreads();
+  if (t < 16) {
+    float v = red[0][t];
+#pragma unroll
+    for (int j = 1; j < NW; ++j) v = fmaxf(v, red[j][t]);
+    const float d = v / qdiv;
+    if (n0 + t < N) wscale[n0 + t] = d;
+    dsh[t] = d;
+  }
+  __syncthreads();
+  float d[8], rc[8];
+  bool slow = false;   // a zero step (all-zero column) or one whose reciprocal overflows
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    d[i] = dsh[h * 8 + i];
+    rc[i] = 1.0f / d[i];
+    slow |= !(rc[i] < INFINITY);
+  }
+
+#pragma unroll
+  for (int p = 0; p < (M + MPP - 1) / MPP; ++p) {
+    if (p > 0) __syncthreads();   // the previous tile has been written out
+#pragma unroll
+    for (int mm = 0; mm < MPP; ++mm) {
+      const int m = MPP * p + mm;
+      if (m >= M) break;
+      const int64_t g = (int64_t)rt + RT * m;
+      if (!ncol || g >= kq) continue;
+      uint32_t pk[8];
+      if (F8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float q[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) q[r] = d[i] != 0.0f ? wh[m][r][i] / d[i] : 0.0f;
+          int x = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+          x = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], x, true);
+          pk[i] = (uint32_t)x;
+        }
+      } else {
+        constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
+        float dm = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t tb[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float y = wh[m][r][i] * rc[i];
+            const float tq = y + kMagic;
+            dm = fmaxf(dm, fabsf(y - (tq - kMagic)));
+            tb[r] = __float_as_uint(tq);
+          }
+          // low bytes of tb[0..3] -> one dword, tb[0] in the lowest byte
+          const uint32_t lo = __builtin_amdgcn_perm(tb[1], tb[0], 0x0c0c0400u);
+          const uint32_t hi = __builtin_amdgcn_perm(tb[3], tb[2], 0x04000c0cu);
+          pk[i] = lo | hi;
+        }
+        if (slow || !(dm <= kTieBand)) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            pk[i] = 0u;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float q = d[i] != 0.0f ? rintf(wh[m][r][i] / d[i]) : 0.0f;
+              pk[i] |= code_byte(fminf(fmaxf(q, -127.0f), 127.0f)) << (8 * r);
+            }
+          }
+        }
+      }
+      const int col = (int)(g - TW * p);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tile[(h * 8 + i) * LDT + col] = pk[i];
+    }
+    __syncthreads();
+    // this tile: 16 rows x kspan bytes, 16 bytes per thread per pass
+    const int64_t k0 = (int64_t)4 * TW * p;
+    const int64_t kspan = min(K - k0, (int64_t)4 * TW);
+    const int segs = (int)(kspan >> 4);
+    for (int q = t; q < 16 * segs; q += NT) {
+      const int n = q / segs;
+      const int sg = q - n * segs;
+      if (n0 + n < N) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&tile[n * LDT + 4 * sg]);
+        *reinterpret_cast<u32x4*>(wq + (n0 + n) * K + k0 + 16 * sg) = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 
@@ -245,6 +424,46 @@ static void quant_weight_f(const void* w, bool bf16, int64_t K, int64_t N, int64
 void launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
                            const float* s, const float* wscale, int8_t* wq, hipStream_t st) {
   quant_weight_f<false>(w, bf16, K, N, ld, s, wscale, wq, st);
+}
+
+bool quant_weight_strip_ok(bool bf16, int64_t K, int64_t N) {
+  return bf16 && K > 0 && K <= 4096 && K % 64 == 0 && N > 0 && N % 8 == 0 &&
+         (N + 15) / 16 <= (int64_t)INT32_MAX;
+}
+
+// NT threads per strip: 1024 (4 waves per SIMD, to hide the quantization's
+// dependency chains) once K > 1024, else 512
+template <int NT, int M, bool F8>
+static void strip_m(const uint16_t* w, int64_t K, int64_t N, int64_t ld, const float* s,
+                    float qdiv, float* wscale, int8_t* wq, hipStream_t st) {
+  const int nstrips = (int)((N + 15) / 16);
+  if (s)
+    hipLaunchKernelGGL((k_quant_weight_strip<NT, M, true, F8>), dim3((unsigned)nstrips), dim3(NT),
+                       0, st, w, K, N, ld, s, qdiv, wscale, wq, nstrips);
+  else
+    hipLaunchKernelGGL((k_quant_weight_strip<NT, M, false, F8>), dim3((unsigned)nstrips), dim3(NT),
+                       0, st, w, K, N, ld, s, qdiv, wscale, wq, nstrips);
+}
+
+template <bool F8>
+static void strip_f(const void* w, int64_t K, int64_t N, int64_t ld, const float* s,
+                    float* wscale, int8_t* wq, hipStream_t st) {
+  const float qdiv = F8 ? 448.0f : 127.0f;
+  const uint16_t* wb = (const uint16_t*)w;
+  const int64_t groups = K >> 2;   // groups of 4 rows
+  if (groups <= 256) strip_m<512, 1, F8>(wb, K, N, ld, s, qdiv, wscale, wq, st);
+  else if (groups <= 512) strip_m<1024, 1, F8>(wb, K, N, ld, s, qdiv, wscale, wq, st);
+  else strip_m<1024, 2, F8>(wb, K, N, ld, s, qdiv, wscale, wq, st);
+}
+
+void launch_quant_weight_strip(const void* w, int64_t K, int64_t N, int64_t ld, const float* s,
+                               float* wscale, int8_t* wq, hipStream_t st) {
+  strip_f<false>(w, K, N, ld, s, wscale, wq, st);
+}
+
+void launch_quant_weight_strip_fp8(const void* w, int64_t K, int64_t N, int64_t ld,
+                                   const float* s, float* wscale, uint8_t* wq, hipStream_t st) {
+  strip_f<true>(w, K, N, ld, s, wscale, reinterpret_cast<int8_t*>(wq), st);
 }
 
 void launch_quant_weight_t_fp8(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,

@@ -133,6 +133,14 @@ __device__ __forceinline__ void atomic_max_nonneg(float* addr, float v) {
   atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
 }
 
+// Rounding by the reciprocal.  For a step d > 0 with rc = fp32(1/d) finite and
+// a quotient below 128 in magnitude, y = fp32(v * rc) lies within 2.3e-5 of
+// the correctly rounded quotient fp32(v / d): when y is farther than 2^-15
+// from every half-integer, both round to the same integer.  A distance
+// |y - rint(y)| above kTieBand marks the values that must be redone with the
+// IEEE division.
+constexpr float kTieBand = 0.5f - 0x1p-15f;
+
 // fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   __bf16 a = (__bf16)lo;

@@ -27,6 +27,12 @@ void launch_fold_w(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, c
 void launch_fold_beta(const float* s, const float* beta, float* bout, int64_t K, hipStream_t st);
 void launch_fold_prev(const void* w, bool bf16, int64_t Kp, int64_t K, int64_t ld, const float* s,
                       float* wout, int64_t ldo, hipStream_t st);
+// one launch: steps and codes of a bf16 weight with K <= 4096 (quant_weight_strip_ok)
+bool quant_weight_strip_ok(bool bf16, int64_t K, int64_t N);
+void launch_quant_weight_strip(const void* w, int64_t K, int64_t N, int64_t ld, const float* s,
+                               float* wscale, int8_t* wq, hipStream_t st);
+void launch_quant_weight_strip_fp8(const void* w, int64_t K, int64_t N, int64_t ld,
+                                   const float* s, float* wscale, uint8_t* wq, hipStream_t st);
 void launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
                            const float* s, const float* wscale, int8_t* wq, hipStream_t st);
 void launch_quant_weight_t_fp8(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,

@@ -156,6 +156,10 @@ sq_status sq_quant_weight(const void* w, sq_dtype w_dt, int64_t k, int64_t n, in
   if (wq == nullptr || w_scale == nullptr) return SQ_ERR_NULL;
   if (n % 8 != 0 || !aligned16(wq)) return SQ_ERR_UNSUPPORTED;
   if (n == 0) return SQ_OK;
+  if (sqk::quant_weight_strip_ok(w_dt == SQ_BF16, k, n)) {
+    sqk::launch_quant_weight_strip(w, k, n, ldw, s, w_scale, wq, stream);
+    return hip_status();
+  }
   sqk::launch_fill_f32(w_scale, n, 0.0f, stream);
   sqk::launch_col_absmax(w, w_dt == SQ_BF16, k, n, ldw, s, 127.0f, w_scale, stream);
   sqk::launch_quant_weight_t(w, w_dt == SQ_BF16, k, n, ldw, s, w_scale, wq, stream);
@@ -169,6 +173,10 @@ sq_status sq_quant_weight_fp8(const void* w, sq_dtype w_dt, int64_t k, int64_t n
   if (wq == nullptr || w_scale == nullptr) return SQ_ERR_NULL;
   if (n % 8 != 0 || !aligned16(wq)) return SQ_ERR_UNSUPPORTED;
   if (n == 0) return SQ_OK;
+  if (sqk::quant_weight_strip_ok(w_dt == SQ_BF16, k, n)) {
+    sqk::launch_quant_weight_strip_fp8(w, k, n, ldw, s, w_scale, wq, stream);
+    return hip_status();
+  }
   sqk::launch_fill_f32(w_scale, n, 0.0f, stream);
   sqk::launch_col_absmax(w, w_dt == SQ_BF16, k, n, ldw, s, 448.0f, w_scale, stream);
   sqk::launch_quant_weight_t_fp8(w, w_dt == SQ_BF16, k, n, ldw, s, w_scale, wq, stream);
