@@ -491,7 +491,7 @@ static void gemm_tile(const int8_t* xq, const float* xs, int T, int K, const int
 }
 
 // compute units of the current device (looked up once per device)
-static int cu_count() {
+int cu_count() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

@@ -6,10 +6,10 @@
 //  * v_mfma_i32_16x16x64_i8 with the weight rows as the A operand (16 output
 //    channels) and up to 16 tokens as the B operand; a lane's 4 accumulators
 //    are 4 consecutive output channels of one token.
-//  * Workgroup = 8 waves over 16*NB output channels; the K steps are split
-//    over the 8 waves and each wave streams its slice of the weight rows
-//    straight into VGPRs (no LDS staging: nothing is reused), U steps in
-//    flight.  The 8 partial int32 sums are added through LDS -- integer adds,
+//  * Workgroup = 8 waves over 16*NB output channels (NB = 1 or 2, chosen per
+//    shape); the K steps are split over the 8 waves and each wave streams its
+//    slice of the weight rows straight into VGPRs (no LDS staging: nothing is
+//    reused), U steps in flight.  The 8 partial int32 sums are added through LDS -- integer adds,
 //    so the result is exact in any order.
 #include "sq_common.h"
 #include "sq_internal.h"
@@ -148,11 +148,10 @@ __global__ __launch_bounds__(512) void k_gemm_decode(const int8_t* __restrict__ 
   }
 }
 
-template <int TB>
+template <int TB, int NB, int U>
 static void decode_tb(const int8_t* xq, const float* xs, int T, int K, const int8_t* wq,
                       const float* ws, int N, const float* bias, void* y, int ldy, int out,
                       hipStream_t st) {
-  constexpr int NB = 2, U = 4;
   const dim3 grid((unsigned)((N + 16 * NB - 1) / (16 * NB))), block(512);
   if (out == 0)
     hipLaunchKernelGGL((k_gemm_decode<TB, NB, U, D_OUT_BF16>), grid, block, 0, st, xq, xs, T, K, wq,
@@ -165,14 +164,28 @@ static void decode_tb(const int8_t* xq, const float* xs, int T, int K, const int
                        ws, N, bias, y, ldy);
 }
 
+// Channels per workgroup: 32 (NB = 2) share each token load between two
+// channel blocks, which pays with more than 8 tokens when N / 32 workgroups
+// still cover every compute unit; otherwise 16 (NB = 1, 8 k-steps in flight)
+// keep twice as many workgroups streaming.  Measured at 16 tokens: K = N =
+// 8192 17.5 us (NB = 2) vs 19.6 us; N = 4096: K = 4096 6.4 us vs 8.0 us,
+// K = 14336 18.0 us vs 24.7 us; one token, K = N = 8192: 15.1 us vs 17.5 us.
 void launch_gemm_decode(const int8_t* xq, const float* xs, int64_t T, int64_t K, const int8_t* wq,
                         const float* ws, int64_t N, const float* bias, void* y, int64_t ldy,
                         int out, hipStream_t st) {
   const int it = (int)T, ik = (int)K, in = (int)N, il = (int)ldy;
-  if (T <= 16) decode_tb<1>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
-  else if (T <= 32) decode_tb<2>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
-  else if (T <= 48) decode_tb<3>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
-  else decode_tb<4>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+  if (T <= 16) {
+    if (T > 8 && (N + 31) / 32 >= cu_count())
+      decode_tb<1, 2, 4>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+    else
+      decode_tb<1, 1, 8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+  } else if (T <= 32) {
+    decode_tb<2, 2, 4>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+  } else if (T <= 48) {
+    decode_tb<3, 2, 4>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+  } else {
+    decode_tb<4, 2, 4>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+  }
 }
 
 }  // namespace sqk

@@ -63,6 +63,9 @@ void launch_gptq(const void* x, bool xbf16, int64_t T, int64_t ldx, bool norm,
                  int64_t ldw, const float* s, float damp, int8_t* wq, float* wscale,
                  float* rrow_out, void* workspace, hipStream_t st);
 
+// compute units of the current device (k_gemm.hip)
+int cu_count();
+
 // k_gemm.hip / k_gemm_decode.hip; out: 0 = bf16, 1 = fp32, 2 = int32 accumulators
 void launch_gemm(const int8_t* xq, const float* xs, int64_t T, int64_t K, const int8_t* wq,
                  const float* ws, int64_t N, const float* bias, void* y, int64_t ldy, int out,
