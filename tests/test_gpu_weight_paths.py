@@ -1,10 +1,13 @@
 """GPU parity of the two weight-quantization paths behind sq_quant_weight and
 sq_quant_weight_fp8, bit for bit against the oracle's fold and quantization:
 
-  * the one-launch strip kernel (bf16 weight, K <= 4096): one, two and four
-    register groups of rows, half-empty last strips, strip counts that are and
-    are not a multiple of the XCD count;
-  * the three-launch path (fp32 weights, K > 4096).
+  * the one-launch strip kernel (bf16 weight; every K <= 2048, and K <= 4096
+    when the strips fill at most two rounds of the compute units, the last
+    at least 90%): 512- and 1024-thread strips with one or two register
+    groups of rows, half-empty last strips, a partial second half of K,
+    strip counts that are and are not a multiple of the XCD count;
+  * the three-launch path (fp32 weights, K > 4096, and K in (2048, 4096]
+    with too few or too many strips).
 
 Also the cases the strip kernel's rounding by the reciprocal must hand to the
 IEEE division: quotients on and within a few ulps of half-integers, an
@@ -26,9 +29,10 @@ from _gpu_util import DEV, f32, say, to_dev, to_np  # noqa: E402
 
 F32 = np.float32
 
-# (K, N): strip path for bf16 with K <= 4096, three-launch path beyond
-SHAPES = [(4096, 4096), (4096, 264), (3072, 24), (2048, 1032), (1088, 72), (1024, 128),
-          (704, 520), (64, 8), (8192, 136)]
+# (K, N) on a 256-CU part: strip kernel for (4096, 4096), (4096, 8192),
+# (3072, 3688) and every K <= 2048; three-launch path for the rest
+SHAPES = [(4096, 4096), (4096, 8192), (3072, 3688), (4096, 264), (3072, 24), (2048, 1032),
+          (1088, 72), (1024, 128), (704, 520), (64, 8), (8192, 136)]
 
 
 def _weight(K, N, seed):
@@ -65,7 +69,8 @@ def test_quant_weight_bf16_paths(K, N):
     np.testing.assert_array_equal(qw2, qw_ref2)
 
 
-@pytest.mark.parametrize("K,N", [(4096, 264), (1088, 72), (704, 520), (8192, 136)])
+@pytest.mark.parametrize("K,N", [(4096, 4096), (3072, 3688), (4096, 264), (1088, 72), (704, 520),
+                                 (8192, 136)])
 def test_quant_weight_fp8_bf16_paths(K, N):
     w, s = _weight(K, N, K * 17 + N)
     say(f"quant weight fp8 bf16 K={K} N={N}")

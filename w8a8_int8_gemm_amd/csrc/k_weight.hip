@@ -426,9 +426,22 @@ void launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, int64
   quant_weight_f<false>(w, bf16, K, N, ld, s, wscale, wq, st);
 }
 
+// The strip kernel takes a whole compute unit per workgroup once K > 2048, so
+// its rounds of cu_count() strips run one after another with no overlap of
+// one strip's loads and another's arithmetic: about 20 us per round at K =
+// 4096, where the three-launch path streams 32 MiB in about 18 us once its
+// fixed costs are paid.  It wins by skipping those costs only with at most two
+// rounds, the last nearly full (measured at K = 4096: N = 4096 20.1 vs 28.8
+// us, 8192 34.5 vs 39.1; N = 1024, 2048, 6144, 14336, 28672 lose).  With
+// K <= 2048 it won at every shape measured (N = 4096: 8.6 vs 13.4 us at
+// K = 1024, 12.1 vs 17.0 at K = 2048).
 bool quant_weight_strip_ok(bool bf16, int64_t K, int64_t N) {
-  return bf16 && K > 0 && K <= 4096 && K % 64 == 0 && N > 0 && N % 8 == 0 &&
-         (N + 15) / 16 <= (int64_t)INT32_MAX;
+  if (!(bf16 && K > 0 && K <= 4096 && K % 64 == 0 && N > 0 && N % 8 == 0)) return false;
+  const int64_t strips = (N + 15) / 16;
+  if (K <= 2048) return strips <= (int64_t)INT32_MAX;
+  const int64_t cu = cu_count();
+  const int64_t rounds = (strips + cu - 1) / cu;
+  return rounds <= 2 && 10 * strips >= 9 * rounds * cu;
 }
 
 // NT threads per strip: 1024 (4 waves per SIMD, to hide the quantization's
