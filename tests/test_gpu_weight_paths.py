@@ -94,13 +94,15 @@ def test_quant_weight_fp32_path():
     np.testing.assert_array_equal(qw, qw_ref)
 
 
-def test_quant_weight_strip_near_ties_and_degenerate_steps():
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_quant_weight_near_ties_and_degenerate_steps(dt):
     """Columns whose step is 3 or 1.5 exactly (row 0 sets the maximum: W = 1
     or 0.5 times s_0 = 381), with every other W^ = +-s_j and s_j within three
     ulps of (m + 1/2) * 3: the quotients sit on or next to half-integers, where
     rounding by fp32(1/3) and by the correctly rounded quotient can part.
     Plus an all-zero column and a column whose step is so small that its
-    reciprocal overflows."""
+    reciprocal overflows.  The same values as a bf16 weight (the strip kernel
+    at this size) and as an fp32 one (the three-launch path)."""
     K, N = 1024, 64
     rng = np.random.default_rng(11)
     m = rng.integers(0, 127, K).astype(np.float64)
@@ -128,8 +130,8 @@ def test_quant_weight_strip_near_ties_and_degenerate_steps():
     quot = (what / np.where(ws_ref == 0, 1, ws_ref)[None, :]).astype(F32)
     near = np.abs(np.abs(quot - np.rint(quot)) - 0.5) < 2.0 ** -15
     assert near.sum() > K * N // 4
-    say("quant weight strip near ties")
-    qw, ws = _quant(to_dev(wb), to_dev(s), K, N)
+    say(f"quant weight near ties {dt}")
+    qw, ws = _quant(to_dev(wb if dt == "bf16" else w), to_dev(s), K, N)
     np.testing.assert_array_equal(ws, ws_ref)
     np.testing.assert_array_equal(qw, qw_ref)
     assert (qw[5] == 0).all()

@@ -12,9 +12,10 @@
 //  * k_fold_prev: W_prev'[i, j] = W_prev[i, j] / s_j -- 1/s folded into the
 //    output columns of the linear whose output is this linear's input ("06 --
 //    SmoothQuant", section 7), with its bias b'_j = b_j / s_j.
-//  * k_quant_weight_t: codes = round-half-even(W^ / Delta_n) (INT8, or the
-//    nearest E4M3 value for FP8), written transposed to the [N, K]
-//    K-contiguous layout the GEMM streams.
+//  * k_quant_weight_t: codes = round-half-even(W^ / Delta_n) (INT8, rounded
+//    by the reciprocal of the step with the IEEE division for near-ties, as
+//    k_quant_weight_strip; or the nearest E4M3 value for FP8), written
+//    transposed to the [N, K] K-contiguous layout the GEMM streams.
 // The per-output-channel step between fold and quant is k_col_absmax with the
 // row scale s and the divisor 127 (the symmetric 8-bit step, "Taming the
 // Outliers", The Problem) or 448 (FP8 E4M3), in k_calib.hip, so W^ is never
@@ -128,33 +129,65 @@ __global__ __launch_bounds__(256) void k_quant_weight_t(const typename In::elem*
     sk[r] = kRowScale ? s[k] : 1.0f;
   }
   uint32_t packed[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) packed[i] = 0u;
-  // quotients W^ / Delta_n (0 where Delta_n == 0, rows past K and columns past N)
-  float qt[4][8];
+  // W^ (0 for rows past K and columns past N, whose codes are then 0)
+  float wh[4][8];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t k = k0 + ty * 4 + r;
     float v[8];
     In::widen(raw[r], v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float wh = kRowScale ? v[i] * sk[r] : v[i];
-      qt[r][i] = (d[i] != 0.0f && ncol && k < K) ? wh / d[i] : 0.0f;
-    }
+    for (int i = 0; i < 8; ++i)
+      wh[r][i] = (ncol && k < K) ? (kRowScale ? v[i] * sk[r] : v[i]) : 0.0f;
   }
+  if (F8) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (F8) {
-      // nearest E4M3, ties to even; |quotient| <= 448 up to one rounding
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(qt[0][i], qt[1][i], 0, false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(qt[2][i], qt[3][i], w, true);
+    for (int i = 0; i < 8; ++i) {
+      // the IEEE quotient, then the nearest E4M3, ties to even; |quotient|
+      // <= 448 up to one rounding
+      float q[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) q[r] = d[i] != 0.0f ? wh[r][i] / d[i] : 0.0f;
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
       packed[i] = (uint32_t)w;
-    } else {
+    }
+  } else {
+    // rounding by the reciprocal, as k_quant_weight_strip: y + 1.5 * 2^23
+    // rounds y to an integer (ties to even) with the code in its low byte;
+    // near-ties, zero steps and overflowing reciprocals take the division
+    constexpr float kMagic = 12582912.0f;
+    float rc[8];
+    bool slow = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      rc[i] = 1.0f / d[i];
+      slow |= !(rc[i] < INFINITY);
+    }
+    float dm = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t tb[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float q = fminf(fmaxf(rintf(qt[r][i]), -127.0f), 127.0f);
-        packed[i] |= code_byte(q) << (8 * r);
+        const float y = wh[r][i] * rc[i];
+        const float tq = y + kMagic;
+        dm = fmaxf(dm, fabsf(y - (tq - kMagic)));
+        tb[r] = __float_as_uint(tq);
+      }
+      const uint32_t lo = __builtin_amdgcn_perm(tb[1], tb[0], 0x0c0c0400u);
+      const uint32_t hi = __builtin_amdgcn_perm(tb[3], tb[2], 0x04000c0cu);
+      packed[i] = lo | hi;
+    }
+    if (slow || !(dm <= kTieBand)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        packed[i] = 0u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float q = d[i] != 0.0f ? rintf(wh[r][i] / d[i]) : 0.0f;
+          packed[i] |= code_byte(fminf(fmaxf(q, -127.0f), 127.0f)) << (8 * r);
+        }
       }
     }
   }
