@@ -7,7 +7,7 @@ does, and this package never imports the product.
 The arithmetic lives in ``sq_oracle.c`` (plain C loops, fp32 where the pages'
 own code quantizes in fp32, fp64 for the RMSNorm mean and the smoothing
 factor's powers).  This file is argument marshalling for it, plus the fp64
-whole-layer reference and error metric used to judge quantization error
+whole-layer reference and error metric used to measure quantization error
 ("SmoothQuant and W8A8", One layer, measured: ||XW - Q(X)Q(W)|| / ||XW||) and
 the fake-quant cross-path of the pages' PyTorch class ("Taming the Outliers",
 Implementation in PyTorch).
