@@ -129,10 +129,15 @@ class HipTimer:
 
 
 def _kernel_hash() -> str:
+    """Hash of the GEMM's device code: k_gemm.hip up to its host-launcher
+    section, and the device helpers of sq_common.h."""
     h = hashlib.sha256()
     for f in ("k_gemm.hip", "sq_common.h"):
         with open(os.path.join(ROOT, "w8a8_int8_gemm_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+            text = fh.read()
+        if f == "k_gemm.hip":
+            text = text.split(b"// host launcher", 1)[0]
+        h.update(text)
     return h.hexdigest()[:16]
 
 
