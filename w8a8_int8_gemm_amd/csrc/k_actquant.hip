@@ -146,7 +146,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV, Q
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int ch = j * 64 + lane;
-    raw[j] = In::raw8(row + (ch < nchunk ? ch : 0) * 8);
+    raw[j] = In::raw8_nt(row + (ch < nchunk ? ch : 0) * 8);   // read once
   }
   float rt = 1.0f;
   if (NORM) {
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_quant_act_ln(
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int ch = j * 64 + lane;
-    raw[j] = In::raw8(row + (ch < nchunk ? ch : 0) * 8);
+    raw[j] = In::raw8_nt(row + (ch < nchunk ? ch : 0) * 8);   // read once
   }
   double s1 = 0.0;
 #pragma unroll

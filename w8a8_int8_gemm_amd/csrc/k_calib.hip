@@ -59,7 +59,10 @@ __global__ __launch_bounds__(256) void k_col_absmax(const typename In::elem* __r
       float sc[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        raw[u] = In::raw8(base + (r + u * step) * ld);
+        // the calibration set is read once (non-temporal); a weight with its
+        // row scale is read again by the quantizer that follows
+        raw[u] = kRowScale ? In::raw8(base + (r + u * step) * ld)
+                           : In::raw8_nt(base + (r + u * step) * ld);
         sc[u] = kRowScale ? rs[r + u * step] : 1.0f;
       }
 #pragma unroll

@@ -397,7 +397,10 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
       const int n = n0 + wn * WTN + cc * 8;
       uint16_t* dst = reinterpret_cast<uint16_t*>(yout) + (int64_t)t * ldy + n;
       if (full_tile || (t < T && n + 8 <= N)) {
-        *reinterpret_cast<u32x4*>(dst) = v;
+        // non-temporal: the output is not read again here, and it then leaves
+        // no dirty lines in the caches to be written back under the next
+        // kernels' streams
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
       } else if (t < T) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)

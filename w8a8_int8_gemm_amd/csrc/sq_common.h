@@ -58,6 +58,14 @@ struct Bf16In {
     r.v = *reinterpret_cast<const u32x4*>(p);
     return r;
   }
+  // non-temporal: for data streamed once (the activations into the
+  // quantizer, the calibration set), so that it does not push out of the
+  // caches what the next kernels read again
+  __device__ __forceinline__ static Raw raw8_nt(const uint16_t* p) {
+    Raw r;
+    r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return r;
+  }
   __device__ __forceinline__ static Raw raw8_cached(const uint16_t* p) {
     Raw r;
     r.v = *reinterpret_cast<const u32x4*>(p);
@@ -92,6 +100,12 @@ struct F32In {
     Raw r;
     r.a = *reinterpret_cast<const f32x4*>(p);
     r.b = *reinterpret_cast<const f32x4*>(p + 4);
+    return r;
+  }
+  __device__ __forceinline__ static Raw raw8_nt(const float* p) {
+    Raw r;
+    r.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    r.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
     return r;
   }
   __device__ __forceinline__ static Raw raw8_cached(const float* p) {
