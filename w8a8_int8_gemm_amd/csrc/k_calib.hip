@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void k_rms_act_absmax(const typename In::elem*
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int64_t ch = (int64_t)j * 64 + lane;
-      dst[j] = In::raw8(row + (ch < nchunk ? ch : 0) * 8);
+      dst[j] = In::raw8_nt(row + (ch < nchunk ? ch : 0) * 8);   // read once
     }
   };
   if (kPrefetch && r < rows) load_row(r, nxt);
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void k_ln_act_absmax(const typename In::elem* 
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int64_t ch = (int64_t)j * 64 + lane;
-      raw[j] = In::raw8(row + (ch < nchunk ? ch : 0) * 8);
+      raw[j] = In::raw8_nt(row + (ch < nchunk ? ch : 0) * 8);   // read once
     }
     double s1 = 0.0;
 #pragma unroll
