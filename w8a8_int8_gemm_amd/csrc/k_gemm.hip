@@ -493,18 +493,19 @@ static void gemm_tile(const int8_t* xq, const float* xs, int T, int K, const int
                        xs, T, K, wq, ws, N, bias, y, ldy, group_t);
 }
 
-// compute units of the current device (looked up once per device)
+// compute units of the current device (looked up once per device; threads
+// that race on the first lookup store the same value)
 int cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <bool F8>
