@@ -16,9 +16,13 @@
 //    by the reciprocal of the step with the IEEE division for near-ties, as
 //    k_quant_weight_strip; or the nearest E4M3 value for FP8), written
 //    transposed to the [N, K] K-contiguous layout the GEMM streams.
-// The per-output-channel step between fold and quant is k_col_absmax with the
-// row scale s and the divisor 127 (the symmetric 8-bit step, "Taming the
-// Outliers", The Problem) or 448 (FP8 E4M3), in k_calib.hip, so W^ is never
+//  * k_quant_weight_strip: the per-output-channel step and the codes of a
+//    bf16 weight with K <= 4096 in one launch, one workgroup per 16 output
+//    channels (where it beats the path below: quant_weight_strip_ok).
+// Otherwise the per-output-channel step between fold and quant is
+// k_col_absmax with the row scale s and the divisor 127 (the symmetric 8-bit
+// step, "Taming the Outliers", The Problem) or 448 (FP8 E4M3), in
+// k_calib.hip, followed by k_quant_weight_t; either way W^ is never
 // materialised.
 #include "sq_common.h"
 #include "sq_internal.h"
