@@ -28,30 +28,56 @@ namespace {
 
 constexpr int NB = 64;          // tile / block edge
 constexpr int LDP = NB + 1;     // padded LDS row (fp64)
+constexpr int kLazy = 4;        // blocks per lazy batch of the GPTQ updates
 
-// acc[a][b] += sum_k As[ty + 16a][k] * Bs[k][tx + 16b] over a 64 x 64 x 64 product
-__device__ __forceinline__ void mm64(const double (*As)[LDP], const double (*Bs)[LDP],
-                                     double (&acc)[4][4], int tx, int ty) {
-#pragma unroll 4
-  for (int k = 0; k < NB; ++k) {
-    double a[4], b[4];
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+// 64 x 64 product tile, acc += As * Bs over 64 k, on the fp64 matrix
+// instruction v_mfma_f64_16x16x4f64 (workgroup of 4 waves).  Wave w owns the
+// 32 x 32 quarter at rows 32 * (w / 2), columns 32 * (w % 2): 2 x 2 blocks of
+// 16 x 16.  Operand lanes: A row lane % 16 and k lane / 16, B column lane % 16
+// and k lane / 16; result value v of lane l is row 4v + l / 16, column l % 16
+// of its block (layouts read off the instruction by a probe).  Every output
+// element sums its 64 products in the same k order, so a tile and its
+// transpose give bit-identical sums.
+struct Tile64 {
+  v4d acc[2][2];
+
+  __device__ __forceinline__ void zero() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = As[ty + 16 * i][k];
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = Bs[k][tx + 16 * i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+      for (int j = 0; j < 2; ++j) acc[i][j] = v4d{0.0, 0.0, 0.0, 0.0};
   }
-}
 
-__device__ __forceinline__ void zero4(double (&acc)[4][4]) {
+  __device__ __forceinline__ void mma(const double (*As)[LDP], const double (*Bs)[LDP]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r0 = (wave >> 1) * 32, c0 = (wave & 1) * 32;
+    const int li = lane & 15, lk = lane >> 4;
+#pragma unroll 4
+    for (int k = 0; k < NB; k += 4) {
+      const double a0 = As[r0 + li][k + lk], a1 = As[r0 + 16 + li][k + lk];
+      const double b0 = Bs[k + lk][c0 + li], b1 = Bs[k + lk][c0 + 16 + li];
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+    }
+  }
+
+  // f(row, column, value) for this lane's 16 elements of the 64 x 64 tile
+  template <class F>
+  __device__ __forceinline__ void each(F&& f) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r0 = (wave >> 1) * 32 + (lane >> 4), c0 = (wave & 1) * 32 + (lane & 15);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-}
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) f(r0 + 16 * i + 4 * v, c0 + 16 * j, acc[i][j][v]);
+  }
+};
 
 // block (ti, tj), ti >= tj, of a lower-triangular tile grid from a linear index
 __device__ __forceinline__ void lower_pair(int64_t idx, int& ti, int& tj) {
@@ -118,9 +144,8 @@ __global__ __launch_bounds__(256) void k_hessian(const typename In::elem* __rest
   __shared__ double Bs[NB][LDP];   // Bs[t][j] = x^[t0 + t][tj*64 + j]
   int ti, tj;
   lower_pair(blockIdx.x, ti, tj);
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  double acc[4][4];
-  zero4(acc);
+  Tile64 acc;
+  acc.zero();
   // loader: thread -> (row lt = tid / 4, 16 columns at 16 * (tid % 4))
   const int lt = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 16;
   for (int64_t t0 = 0; t0 < T; t0 += NB) {
@@ -146,14 +171,10 @@ __global__ __launch_bounds__(256) void k_hessian(const typename In::elem* __rest
       }
     }
     __syncthreads();
-    mm64(As, Bs, acc, tx, ty);
+    acc.mma(As, Bs);
     __syncthreads();
   }
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      H[((int64_t)ti * NB + ty + 16 * a) * K + (int64_t)tj * NB + tx + 16 * b] = acc[a][b];
+  acc.each([&](int r, int c, double v) { H[((int64_t)ti * NB + r) * K + (int64_t)tj * NB + c] = v; });
 }
 
 // ---------------------------------------------------------------------------
@@ -253,7 +274,6 @@ __global__ __launch_bounds__(256) void k_chol_trsm(double* __restrict__ A, int64
   __shared__ double As[NB][LDP];
   __shared__ double Bs[NB][LDP];
   const int i = p + 1 + blockIdx.x;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int64_t ro = (int64_t)i * NB, co = (int64_t)p * NB;
   for (int e = threadIdx.x; e < NB * NB; e += 256) {
     const int a = e / NB, b = e % NB;
@@ -261,13 +281,10 @@ __global__ __launch_bounds__(256) void k_chol_trsm(double* __restrict__ A, int64
     Bs[a][b] = Dinv[((int64_t)p * NB + b) * NB + a];   // Bs[k][c] = Dinv[c][k]
   }
   __syncthreads();
-  double acc[4][4];
-  zero4(acc);
-  mm64(As, Bs, acc, tx, ty);
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) A[(ro + ty + 16 * a) * K + co + tx + 16 * b] = acc[a][b];
+  Tile64 acc;
+  acc.zero();
+  acc.mma(As, Bs);
+  acc.each([&](int r, int c, double v) { A[(ro + r) * K + co + c] = v; });
 }
 
 // Trailing update: A_ij -= L_ip L_jp^T for p < j <= i.
@@ -278,7 +295,6 @@ __global__ __launch_bounds__(256) void k_chol_syrk(double* __restrict__ A, int64
   lower_pair(blockIdx.x, i, j);
   i += p + 1;
   j += p + 1;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int64_t co = (int64_t)p * NB;
   for (int e = threadIdx.x; e < NB * NB; e += 256) {
     const int a = e / NB, b = e % NB;
@@ -286,16 +302,13 @@ __global__ __launch_bounds__(256) void k_chol_syrk(double* __restrict__ A, int64
     Bs[b][a] = A[((int64_t)j * NB + a) * K + co + b];   // Bs[k][c] = L_jp[c][k]
   }
   __syncthreads();
-  double acc[4][4];
-  zero4(acc);
-  mm64(As, Bs, acc, tx, ty);
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      double* c = A + ((int64_t)i * NB + ty + 16 * a) * K + (int64_t)j * NB + tx + 16 * b;
-      *c = *c - acc[a][b];
-    }
+  Tile64 acc;
+  acc.zero();
+  acc.mma(As, Bs);
+  acc.each([&](int r, int c, double v) {
+    double* q = A + ((int64_t)i * NB + r) * K + (int64_t)j * NB + c;
+    *q = *q - v;
+  });
 }
 
 // C = alpha * A B + beta * C on 64 x 64 tiles (M, N, Kd multiples of 64),
@@ -307,10 +320,9 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t Kd,
                                                double beta, double* __restrict__ C, int64_t ldc) {
   __shared__ double As[NB][LDP];
   __shared__ double Bs[NB][LDP];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int64_t m0 = (int64_t)blockIdx.y * NB, n0 = (int64_t)blockIdx.x * NB;
-  double acc[4][4];
-  zero4(acc);
+  Tile64 acc;
+  acc.zero();
   for (int64_t k0 = 0; k0 < Kd; k0 += NB) {
     for (int e = threadIdx.x; e < NB * NB; e += 256) {
       const int a = e / NB, b = e % NB;
@@ -318,17 +330,14 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t Kd,
       Bs[a][b] = B[(k0 + a) * ldb + n0 + b];
     }
     __syncthreads();
-    mm64(As, Bs, acc, tx, ty);
+    acc.mma(As, Bs);
     __syncthreads();
   }
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      double* c = C + (m0 + ty + 16 * a) * ldc + n0 + tx + 16 * b;
-      const double v = alpha * acc[a][b];
-      *c = (beta == 0.0) ? v : v + beta * *c;
-    }
+  acc.each([&](int r, int c, double x) {
+    double* q = C + (m0 + r) * ldc + n0 + c;
+    const double v = alpha * x;
+    *q = (beta == 0.0) ? v : v + beta * *q;
+  });
 }
 
 // X = L^-1 before the recursion: X_ii = Dinv[i], every other block 0 (the
@@ -406,38 +415,44 @@ __global__ __launch_bounds__(256) void k_gptq_block(double* __restrict__ W64, in
   }
 }
 
-// Later rows: W64[i][n] -= sum_jj U[r0 + jj][i] * E[jj][n] for i >= r0 + 64;
-// tile (blockIdx.y, blockIdx.x) of 64 x 64.
+// Later rows: W64[i][n] -= sum_jj U[r0 + jj][i] * E[jj][n], jj < depth (a
+// multiple of 64: the error rows of one block, or of a whole lazy batch), for
+// the rows i = i_first + 64 * blockIdx.y + (0 .. 63), all past r0 + depth;
+// columns n0 = 64 * blockIdx.x.
 __global__ __launch_bounds__(256) void k_gptq_update(double* __restrict__ W64, int64_t K,
-                                                     int64_t N, int b,
+                                                     int64_t N, int64_t r0, int depth,
+                                                     int64_t i_first,
                                                      const double* __restrict__ X,
                                                      const double* __restrict__ E) {
-  __shared__ double As[NB][LDP];   // As[i][jj] = U[r0 + jj][i0 + i]
-  __shared__ double Bs[NB][LDP];   // Bs[jj][c] = E[jj][n0 + c]
-  const int64_t r0 = (int64_t)b * NB;
-  const int64_t i0 = r0 + NB + (int64_t)blockIdx.y * NB;
+  __shared__ double As[NB][LDP];   // As[i][jj] = U[r0 + 64c + jj][i0 + i]
+  __shared__ double Bs[NB][LDP];   // Bs[jj][col] = E[64c + jj][n0 + col]
+  const int64_t i0 = i_first + (int64_t)blockIdx.y * NB;
   const int64_t n0 = (int64_t)blockIdx.x * NB;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  for (int e = threadIdx.x; e < NB * NB; e += 256) {
-    const int a = e / NB, q = e % NB;
-    // U[r0 + q][i0 + a] = X[K-1-r0-q][K-1-i0-a] (i0 + a > r0 + q: lower part of X)
-    As[a][q] = X[(K - 1 - r0 - q) * K + (K - 1 - i0 - a)];
-    Bs[a][q] = (n0 + q < N) ? E[(int64_t)a * N + n0 + q] : 0.0;
-  }
-  __syncthreads();
-  double acc[4][4];
-  zero4(acc);
-  mm64(As, Bs, acc, tx, ty);
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t nn = n0 + tx + 16 * q;
-      if (nn < N) {
-        double* p = W64 + (i0 + ty + 16 * a) * N + nn;
-        *p = *p - acc[a][q];
-      }
+  Tile64 acc;
+  acc.zero();
+  for (int c = 0; c < depth / NB; ++c) {
+    const int64_t j0 = r0 + (int64_t)c * NB;
+    if (c > 0) __syncthreads();
+    for (int e = threadIdx.x; e < NB * NB; e += 256) {
+      // U[j0 + q][i0 + a] = X[K-1-j0-q][K-1-i0-a] (i0 + a > j0 + q: lower part
+      // of X); consecutive threads take consecutive a, i.e. one row of X
+      const int q = e / NB, a = e % NB;
+      As[a][q] = X[(K - 1 - j0 - q) * K + (K - 1 - i0 - a)];
     }
+    for (int e = threadIdx.x; e < NB * NB; e += 256) {
+      const int a = e / NB, q = e % NB;
+      Bs[a][q] = (n0 + q < N) ? E[((int64_t)c * NB + a) * N + n0 + q] : 0.0;
+    }
+    __syncthreads();
+    acc.mma(As, Bs);
+  }
+  acc.each([&](int r, int c, double v) {
+    const int64_t nn = n0 + c;
+    if (nn < N) {
+      double* q = W64 + (i0 + r) * N + nn;
+      *q = *q - v;
+    }
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -447,7 +462,7 @@ __global__ __launch_bounds__(256) void k_gptq_update(double* __restrict__ W64, i
 size_t gptq_workspace_bytes(int64_t T, int64_t K, int64_t N) {
   auto r256 = [](int64_t b) { return (size_t)((b + 255) & ~int64_t(255)); };
   return r256(K * K * 8) * 2 + r256(K * NB * 8) + r256(K * 8) + r256(K) + r256(T * 4) +
-         r256(K * N * 8) + r256((int64_t)NB * N * 8) + r256(K * K * 2);
+         r256(K * N * 8) + r256((int64_t)kLazy * NB * N * 8) + r256(K * K * 2);
 }
 
 // X = L^-1 on the block range [b0, b0 + nb) (diagonal blocks already in X):
@@ -481,7 +496,7 @@ void launch_gptq(const void* x, bool xbf16, int64_t T, int64_t ldx, bool norm,
   unsigned char* dead = reinterpret_cast<unsigned char*>(p); p += r256(K);
   float* rr = rrow_out ? rrow_out : reinterpret_cast<float*>(p);  p += r256(T * 4);
   double* W64 = reinterpret_cast<double*>(p);          p += r256(K * N * 8);
-  double* E = reinterpret_cast<double*>(p);             p += r256((int64_t)NB * N * 8);
+  double* E = reinterpret_cast<double*>(p);             p += r256((int64_t)kLazy * NB * N * 8);
   double* tmp = reinterpret_cast<double*>(p);
   const int nt = (int)(K / NB);
   const int64_t tiles = (int64_t)nt * (nt + 1) / 2;
@@ -526,13 +541,27 @@ void launch_gptq(const void* x, bool xbf16, int64_t T, int64_t ldx, bool norm,
     if (wbf16) hipLaunchKernelGGL(k_gptq_init<Bf16In>, g, dim3(256), 0, st, (const uint16_t*)w, K, N, ldw, s, dead, W64);
     else hipLaunchKernelGGL(k_gptq_init<F32In>, g, dim3(256), 0, st, (const float*)w, K, N, ldw, s, dead, W64);
   }
+  // Lazy batches of kLazy blocks: a block's errors update the rest of its
+  // batch at once, and the rows past the batch once per batch with all of its
+  // error rows, so the fp64 weight below is read and written K / (64 kLazy)
+  // times instead of K / 64.  The same terms reach every row; only the order
+  // of their sum changes.
   const unsigned nslab = (unsigned)((N + NB - 1) / NB);
-  for (int b = 0; b < nt; ++b) {
-    hipLaunchKernelGGL(k_gptq_block, dim3(nslab), dim3(256), 0, st, W64, K, N, b, H, wscale, wq, E);
-    const int rest = nt - b - 1;
+  for (int s0 = 0; s0 < nt; s0 += kLazy) {
+    const int s1 = min(nt, s0 + kLazy);
+    for (int b = s0; b < s1; ++b) {
+      double* Eb = E + (int64_t)(b - s0) * NB * N;
+      hipLaunchKernelGGL(k_gptq_block, dim3(nslab), dim3(256), 0, st, W64, K, N, b, H, wscale, wq,
+                         Eb);
+      const int rest_in = s1 - b - 1;
+      if (rest_in > 0)
+        hipLaunchKernelGGL(k_gptq_update, dim3(nslab, (unsigned)rest_in), dim3(256), 0, st, W64,
+                           K, N, (int64_t)b * NB, NB, (int64_t)(b + 1) * NB, H, Eb);
+    }
+    const int rest = nt - s1;
     if (rest > 0)
       hipLaunchKernelGGL(k_gptq_update, dim3(nslab, (unsigned)rest), dim3(256), 0, st, W64, K, N,
-                         b, H, E);
+                         (int64_t)s0 * NB, (s1 - s0) * NB, (int64_t)s1 * NB, H, E);
   }
 }
 
