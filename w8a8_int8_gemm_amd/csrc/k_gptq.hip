@@ -146,31 +146,48 @@ __global__ __launch_bounds__(256) void k_hessian(const typename In::elem* __rest
   lower_pair(blockIdx.x, ti, tj);
   Tile64 acc;
   acc.zero();
-  // loader: thread -> (row lt = tid / 4, 16 columns at 16 * (tid % 4))
+  // loader: thread -> (row lt = tid / 4, 16 columns at 16 * (tid % 4)) of
+  // each 64-token chunk, for the ti panel (half 0) and the tj panel (half 1).
+  // The next chunk's raw values are loaded while this chunk's products run.
   const int lt = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 16;
+  int64_t col0[2];
+  col0[0] = (int64_t)ti * NB + lc;
+  col0[1] = (int64_t)tj * NB + lc;
+  float gv[2][16];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) gv[h][e] = g ? g[col0[h] + e] : 1.0f;
+  typename In::Raw raw[2][2];
+  float rt = 1.0f;
+  auto load = [&](int64_t t0) {
+    const int64_t t = min(t0 + lt, T - 1);   // rows past T: zeroed at the store
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      raw[h][0] = In::raw8(x + t * ld + col0[h]);
+      raw[h][1] = In::raw8(x + t * ld + col0[h] + 8);
+    }
+    if (NORM) rt = r[t];
+  };
+  load(0);
   for (int64_t t0 = 0; t0 < T; t0 += NB) {
-    const int64_t t = t0 + lt;
+    const bool live = t0 + lt < T;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int64_t col0 = (int64_t)(half == 0 ? ti : tj) * NB + lc;
+    for (int h = 0; h < 2; ++h) {
       float v[16];
-      if (t < T) {
-        In::load8(x + t * ld + col0, *reinterpret_cast<float(*)[8]>(&v[0]));
-        In::load8(x + t * ld + col0 + 8, *reinterpret_cast<float(*)[8]>(&v[8]));
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) v[e] = 0.0f;
-      }
-      const float rt = (NORM && t < T) ? r[t] : 1.0f;
+      In::widen(raw[h][0], *reinterpret_cast<float(*)[8]>(&v[0]));
+      In::widen(raw[h][1], *reinterpret_cast<float(*)[8]>(&v[8]));
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float u = NORM ? v[e] * rt : v[e];
-        const float xh = u * (g ? g[col0 + e] : 1.0f);
-        if (half == 0) As[lc + e][lt] = (double)xh;
-        else Bs[lt][lc + e] = (double)xh;
+        const double xh = live ? (double)(u * gv[h][e]) : 0.0;
+        if (h == 0) As[lc + e][lt] = xh;
+        else Bs[lt][lc + e] = xh;
       }
     }
     __syncthreads();
+    if (t0 + NB < T) load(t0 + NB);
+    asm volatile("" ::: "memory");   // keep those loads ahead of the products
     acc.mma(As, Bs);
     __syncthreads();
   }
@@ -323,13 +340,28 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t Kd,
   const int64_t m0 = (int64_t)blockIdx.y * NB, n0 = (int64_t)blockIdx.x * NB;
   Tile64 acc;
   acc.zero();
+  // element e = threadIdx.x + 256 i (i < 16) of each 64 x 64 operand chunk;
+  // the next chunk is loaded while this one's products run
+  double pa[16], pb[16];
+  auto load = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = threadIdx.x + 256 * i, a = e / NB, b = e % NB;
+      pa[i] = A[(m0 + a) * lda + k0 + b];
+      pb[i] = B[(k0 + a) * ldb + n0 + b];
+    }
+  };
+  load(0);
   for (int64_t k0 = 0; k0 < Kd; k0 += NB) {
-    for (int e = threadIdx.x; e < NB * NB; e += 256) {
-      const int a = e / NB, b = e % NB;
-      As[a][b] = A[(m0 + a) * lda + k0 + b];
-      Bs[a][b] = B[(k0 + a) * ldb + n0 + b];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = threadIdx.x + 256 * i, a = e / NB, b = e % NB;
+      As[a][b] = pa[i];
+      Bs[a][b] = pb[i];
     }
     __syncthreads();
+    if (k0 + NB < Kd) load(k0 + NB);
+    asm volatile("" ::: "memory");   // keep those loads ahead of the products
     acc.mma(As, Bs);
     __syncthreads();
   }
@@ -430,21 +462,33 @@ __global__ __launch_bounds__(256) void k_gptq_update(double* __restrict__ W64, i
   const int64_t n0 = (int64_t)blockIdx.x * NB;
   Tile64 acc;
   acc.zero();
-  for (int c = 0; c < depth / NB; ++c) {
+  // element e = threadIdx.x + 256 i (i < 16) of each chunk's operands: U[j0 +
+  // q][i0 + a] = X[K-1-j0-q][K-1-i0-a] (i0 + a > j0 + q: lower part of X),
+  // consecutive threads on consecutive a (one row of X), and E[j0 - r0 + a][n0
+  // + q].  The next chunk is loaded while this one's products run.
+  double pu[16], pe[16];
+  auto load = [&](int c) {
     const int64_t j0 = r0 + (int64_t)c * NB;
-    if (c > 0) __syncthreads();
-    for (int e = threadIdx.x; e < NB * NB; e += 256) {
-      // U[j0 + q][i0 + a] = X[K-1-j0-q][K-1-i0-a] (i0 + a > j0 + q: lower part
-      // of X); consecutive threads take consecutive a, i.e. one row of X
-      const int q = e / NB, a = e % NB;
-      As[a][q] = X[(K - 1 - j0 - q) * K + (K - 1 - i0 - a)];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      pu[i] = X[(K - 1 - j0 - e / NB) * K + (K - 1 - i0 - e % NB)];
+      pe[i] = (n0 + e % NB < N) ? E[((int64_t)c * NB + e / NB) * N + n0 + e % NB] : 0.0;
     }
-    for (int e = threadIdx.x; e < NB * NB; e += 256) {
-      const int a = e / NB, q = e % NB;
-      Bs[a][q] = (n0 + q < N) ? E[((int64_t)c * NB + a) * N + n0 + q] : 0.0;
+  };
+  load(0);
+  for (int c = 0; c < depth / NB; ++c) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      As[e % NB][e / NB] = pu[i];
+      Bs[e / NB][e % NB] = pe[i];
     }
     __syncthreads();
+    if (c + 1 < depth / NB) load(c + 1);
+    asm volatile("" ::: "memory");   // keep those loads ahead of the products
     acc.mma(As, Bs);
+    __syncthreads();
   }
   acc.each([&](int r, int c, double v) {
     const int64_t nn = n0 + c;
