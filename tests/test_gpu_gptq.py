@@ -113,3 +113,34 @@ def test_gptq_dead_input_and_empty_output_channel():
     np.testing.assert_array_equal(to_np(wsc), ws_ref)
     _check_codes(to_np(wq), q_ref, quot)
     assert not to_np(wq)[:, 9].any() and not to_np(wq)[17].any()
+
+
+def test_gptq_first_row_ties():
+    """Row 0 is rounded before any update reaches it, so its quotients are the
+    plain W / w_scale.  With every column's maximum 127/128 (step 2^-7 exactly)
+    and W[0, n] = (m + 1/2) / 128, one fp32 ulp above or one below, the
+    quotients sit exactly on half-integers (ties to even) or next to them:
+    the rounding kernel's near-tie rule must give the oracle's codes there,
+    with no allowance."""
+    say("gptq first-row ties")
+    rng = np.random.default_rng(71)
+    Tc, K, N = 200, 128, 192
+    x = rng.standard_normal((Tc, K)).astype(np.float32)
+    w = rng.uniform(-0.9, 0.9, (K, N)).astype(np.float32)
+    w[K - 1] = np.where(rng.random(N) < 0.5, 127.0, -127.0) / 128.0
+    m = rng.integers(-127, 127, N).astype(np.float32)
+    w0 = ((m + np.float32(0.5)) / np.float32(128)).astype(np.float32)
+    w0[N // 3:2 * N // 3] = np.nextafter(w0[N // 3:2 * N // 3], np.float32(np.inf))
+    w0[2 * N // 3:] = np.nextafter(w0[2 * N // 3:], np.float32(-np.inf))
+    w[0] = w0
+    wq, wsc = torch.empty((N, K), dtype=torch.int8, device=DEV), f32(N)
+    work = torch.empty(sq.sq_gptq_workspace_bytes(Tc, K, N), dtype=torch.uint8, device=DEV)
+    sq.sq_quant_weight_gptq(to_dev(x), None, to_dev(w), None, wq, wsc, work)
+    torch.cuda.synchronize()
+    q_ref, ws_ref, quot = oracle.gptq(w, oracle.smoothed_act(x), return_quotients=True)
+    assert (ws_ref == np.float32(2.0 ** -7)).all()
+    assert (np.abs(quot[0, :N // 3] - np.floor(quot[0, :N // 3])) == 0.5).all()
+    q = to_np(wq)
+    np.testing.assert_array_equal(to_np(wsc), ws_ref)
+    np.testing.assert_array_equal(q[:, 0], q_ref[:, 0])
+    _check_codes(q, q_ref, quot)

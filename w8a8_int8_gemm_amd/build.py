@@ -30,9 +30,15 @@ CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract
           "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
 
+# per-source additions: the GPTQ row and column steps unroll 64 x 64 updates
+# fully (their values live in registers, indexed by the loop counters), past
+# clang's default cost limit for an unroll pragma
+EXTRA = {"k_gptq.hip": ["-mllvm", "-pragma-unroll-threshold=200000"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

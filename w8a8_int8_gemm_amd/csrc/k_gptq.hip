@@ -236,12 +236,6 @@ __global__ __launch_bounds__(256) void k_hess_reverse(const double* __restrict__
 // ---------------------------------------------------------------------------
 // 3. Blocked Cholesky of A (lower, in place) and the inverse of its factor.
 // ---------------------------------------------------------------------------
-// Diagonal block p, one wave: lane i holds row i of the 64 x 64 block in
-// VGPRs.  Right-looking Cholesky, column c: the pivot and the column values
-// L[j][c] reach every lane by readlane; then the factor's inverse, lane m
-// forward-substituting column m against the factor staged in LDS (every lane
-// reads the same L[i][k] at once).  Written to A (lower, zeros above) and
-// Dinv[p].
 __device__ __forceinline__ double readlane_f64(double v, int lane) {
   const uint64_t b = __builtin_bit_cast(uint64_t, v);
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, lane);
@@ -249,38 +243,130 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
+// 1 / sqrt(x): the hardware estimate and two Newton steps
+__device__ __forceinline__ double rsqrt_nr(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) y = fma(0.5 * y, fma(-x * y, y, 1.0), y);
+  return y;
+}
+
+// The update stream of a 64 x 64 triangle in chunks: row jj (0 .. 62) takes
+// the groups g = (jj + 1) / 8 .. 7 of its entries 8g .. 8g + 7 (the entries
+// past the diagonal, rounded out to whole groups).
+struct UChunks {
+  int row[NB * 8], grp[NB * 8], n;
+};
+constexpr UChunks make_uchunks() {
+  UChunks L{};
+  int n = 0;
+  for (int jj = 0; jj + 1 < NB; ++jj)
+    for (int g = (jj + 1) / 8; g < NB / 8; ++g) {
+      L.row[n] = jj;
+      L.grp[n] = g;
+      ++n;
+    }
+  L.n = n;
+  return L;
+}
+constexpr UChunks kUChunks = make_uchunks();
+constexpr int kRing = 4;   // chunks in flight (4 LDS reads each; lgkmcnt counts to 15)
+
+// An empty asm that takes v[0 .. 7] as read-write VGPR operands, with a
+// memory clobber: the products that update them, and the loads issued before
+// it, stay before it.  Without such pins the scheduler hoists whole triangles
+// of LDS loads, or sinks the row-by-row products to first use, and either way
+// holds thousands of values; with them, each chunk's loads are issued kRing
+// chunks ahead of its products.
+__device__ __forceinline__ void pin8(double* v) {
+  asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+               "+v"(v[6]), "+v"(v[7])::"memory");
+}
+
+// Diagonal block p, one wave: lane i holds row i of the 64 x 64 block in
+// VGPRs.  Right-looking Cholesky, column c: the pivot reaches every lane by
+// readlane, lane i puts L[i][c] in row c of LT (the factor transposed, in
+// LDS), and every lane reads that row at once (a broadcast) for its updates.
+// The next column's pivot comes first (its one update takes L[c+1][c] by
+// readlane) so that its square root overlaps the rest of column c's updates.
+// Then the factor's inverse, right-looking too: lane m holds column m of
+// L^-1; step k scales entry k by 1 / L[k][k] and subtracts its multiples of
+// L[a][k] (row k of LT) from the entries a > k.  One wave and LDS accesses
+// in program order: a wave barrier suffices between a row's writes and its
+// reads.  Written to A (lower, zeros above) and Dinv[p].
 __global__ __launch_bounds__(64) void k_chol_panel(double* __restrict__ A, int64_t K, int p,
                                                    double* __restrict__ Dinv) {
-  __shared__ double L[NB][LDP];
+  __shared__ __align__(16) double LT[NB][NB];   // LT[c][i] = L[i][c]
+  __shared__ double Rd[NB];                     // 1 / L[c][c]
   const int i = threadIdx.x;
   const int64_t o = (int64_t)p * NB;
   double r[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) r[j] = A[(o + i) * K + o + j];   // upper part: never read
+  double ring[kRing][8];
+  double piv = readlane_f64(r[0], 0);
+  double y = rsqrt_nr(piv);
 #pragma unroll
   for (int c = 0; c < NB; ++c) {
-    const double d = sqrt(readlane_f64(r[c], c));
-    const double lc = (i == c) ? d : r[c] / d;
+    const double lc = (i == c) ? piv * y : r[c] * y;
     r[c] = lc;
+    LT[c][i] = lc;
+    if (i == c) Rd[c] = y;
+    __builtin_amdgcn_wave_barrier();
+    if (c + 1 < NB) {
+      // the next pivot first; the rest of the column's updates run meanwhile,
+      // their LT reads kRing chunks ahead within the row
+      r[c + 1] = fma(-lc, readlane_f64(lc, c + 1), r[c + 1]);
+      piv = readlane_f64(r[c + 1], c + 1);
+      y = rsqrt_nr(piv);
+      const int g0 = (c + 2) / 8, ng = c + 2 < NB ? NB / 8 - g0 : 0;
+      auto fetch = [&](int u) {
 #pragma unroll
-    for (int j = c + 1; j < NB; ++j) r[j] = r[j] - lc * readlane_f64(lc, j);
+        for (int t = 0; t < 8; ++t) ring[u % kRing][t] = LT[c][8 * (g0 + u) + t];
+      };
+#pragma unroll
+      for (int u = 0; u < kRing; ++u)
+        if (u < ng) fetch(u);
+#pragma unroll
+      for (int u = 0; u < ng; ++u) {
+        const int g = g0 + u;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (8 * g + t >= c + 2) r[8 * g + t] = fma(-lc, ring[u % kRing][t], r[8 * g + t]);
+        if (u + kRing < ng) fetch(u + kRing);
+        pin8(r + 8 * g);   // this chunk's products here, the next reads after
+      }
+    }
   }
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const double v = (j <= i) ? r[j] : 0.0;
-    L[i][j] = v;
-    A[(o + i) * K + o + j] = v;
-  }
-  __syncthreads();
-  // column m = i of L^-1: x[k] = 0 for k < m follows from the zero right side
+  for (int j = 0; j < NB; ++j) A[(o + i) * K + o + j] = (j <= i) ? r[j] : 0.0;
+  __builtin_amdgcn_wave_barrier();
+  // column m = i of L^-1 (entries above m stay 0: zero right side); the rows
+  // of LT stream through the ring kRing chunks ahead, across rows
   double x[NB];
 #pragma unroll
-  for (int a = 0; a < NB; ++a) {
-    double sum = (a == i) ? 1.0 : 0.0;
+  for (int a = 0; a < NB; ++a) x[a] = (a == i) ? 1.0 : 0.0;
+  auto fetch = [&](int ci) {
+    const double* src = &LT[kUChunks.row[ci]][8 * kUChunks.grp[ci]];
 #pragma unroll
-    for (int k = 0; k < a; ++k) sum = sum - L[a][k] * x[k];
-    x[a] = sum / L[a][a];
+    for (int t = 0; t < 8; ++t) ring[ci % kRing][t] = src[t];
+  };
+#pragma unroll
+  for (int ci = 0; ci < kRing; ++ci) fetch(ci);
+  int ci = 0;
+#pragma unroll
+  for (int k = 0; k + 1 < NB; ++k) {
+    x[k] = x[k] * Rd[k];
+#pragma unroll
+    for (int g = (k + 1) / 8; g < NB / 8; ++g, ++ci) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (8 * g + t > k) x[8 * g + t] = fma(-ring[ci % kRing][t], x[k], x[8 * g + t]);
+      if (ci + kRing < kUChunks.n) fetch(ci + kRing);
+      pin8(x + 8 * g);
+    }
   }
+  x[NB - 1] = x[NB - 1] * Rd[NB - 1];
 #pragma unroll
   for (int a = 0; a < NB; ++a) Dinv[(o + a) * NB + i] = x[a];
 }
@@ -403,56 +489,111 @@ __global__ __launch_bounds__(256) void k_gptq_init(const typename In::elem* __re
   for (int e = 0; e < 8; ++e) W64[j * N + n0 + e] = dead[j] ? 0.0 : (double)(v[e] * sj);
 }
 
-// Block b (rows b*64 .. +63) of the rounding, for output channels
-// blockIdx.x*64 .. +63: U[j][k] = X[K-1-j][K-1-k].
-__global__ __launch_bounds__(256) void k_gptq_block(double* __restrict__ W64, int64_t K,
-                                                    int64_t N, int b,
-                                                    const double* __restrict__ X,
-                                                    const float* __restrict__ wscale,
-                                                    int8_t* __restrict__ wq,
-                                                    double* __restrict__ E) {
-  __shared__ double Wb[NB][LDP];
-  __shared__ double Ub[NB][LDP];
-  __shared__ double Es[NB][LDP];
-  __shared__ int8_t Q[NB][NB + 4];
-  const int c = threadIdx.x & 63, rg = threadIdx.x >> 6;
+// Block b (rows r0 = b*64 .. +63) of the rounding for the 64 output channels
+// n = blockIdx.x*64 + lane, one wave: each lane holds its channel's 64 rows in
+// registers and carries the row-by-row updates there; U[r0 + jj][r0 + kk]
+// (kk > jj) is read by every lane at the same LDS address (a broadcast).
+// U[j][k] = X[K-1-j][K-1-k].  The reads stream through a ring of kRing
+// chunks of eight values, issued kRing chunks ahead of their products, and
+// row jj + 1's code and error are computed right after the chunk that updates
+// it.  E has row stride ldE = N rounded up to 64: the lanes past N write
+// zeros there.
+//
+// The code of w / d is rint(w * (1 / d)), except within 1e-9 of a
+// half-integer h, where the sign of w - h d (one fused multiply-add: exact in
+// sign) picks the side, and a zero (w / d = h exactly) rounds h to even.  That
+// is the rounding of the exact quotient; it can differ from rounding the
+// correctly rounded quotient only within half an ulp of h.
+__device__ __forceinline__ double gptq_code(double wv, double d, double rd) {
+  const double t = wv * rd;
+  const double h = floor(t) + 0.5;
+  const double side = fma(-h, d, wv);
+  const double up = h + 0.5, dn = h - 0.5, even = rint(h);
+  double qn = side > 0.0 ? up : even;
+  qn = side < 0.0 ? dn : qn;
+  asm volatile("" : "+v"(qn));   // computed on every row: a select, not a branch
+  const double q = fabs(t - h) < 1e-9 ? qn : rint(t);
+  return d > 0.0 ? fmin(fmax(q, -127.0), 127.0) : 0.0;
+}
+
+__global__ __launch_bounds__(64) void k_gptq_block(const double* __restrict__ W64, int64_t K,
+                                                   int64_t N, int64_t ldE, int b,
+                                                   const double* __restrict__ X,
+                                                   const float* __restrict__ wscale,
+                                                   int8_t* __restrict__ wq,
+                                                   double* __restrict__ E) {
+  __shared__ __align__(16) double Ub[NB][NB];
+  __shared__ double Ur[NB];        // 1 / U_jj
+  const int c = threadIdx.x;
   const int64_t n = (int64_t)blockIdx.x * NB + c;
   const bool live = n < N;
+  const int64_t nc = live ? n : N - 1;   // past-the-end lanes load a valid column
   const int64_t r0 = (int64_t)b * NB;
-  for (int kk = rg; kk < NB; kk += 4) {
-    Wb[kk][c] = live ? W64[(r0 + kk) * N + n] : 0.0;
-    Ub[kk][c] = (c >= kk) ? X[(K - 1 - r0 - kk) * K + (K - 1 - r0 - c)] : 0.0;
-  }
-  const double d = live ? (double)wscale[n] : 0.0;
-  __syncthreads();
+  const double* xr = X + (K - 1 - r0) * K + (K - 1 - r0 - c);   // U[r0][r0 + c]
+  double w[NB];
+#pragma unroll
   for (int jj = 0; jj < NB; ++jj) {
-    if (rg == 0) {
-      const double wv = Wb[jj][c];
-      double q = 0.0;
-      if (d > 0.0) q = fmin(fmax(rint(wv / d), -127.0), 127.0);
-      Q[jj][c] = (int8_t)q;
-      Es[jj][c] = (wv - d * q) / Ub[jj][jj];
+    Ub[jj][c] = xr[-(int64_t)jj * K];
+    const double v = W64[(r0 + jj) * N + nc];
+    w[jj] = live ? v : 0.0;
+  }
+  const double d = live ? (double)wscale[nc] : 0.0;
+  const double rd = d > 0.0 ? 1.0 / d : 0.0;
+  __syncthreads();
+  Ur[c] = 1.0 / Ub[c][c];
+  __syncthreads();
+  double ring[kRing][8];
+  auto fetch = [&](int ci) {
+    const double* src = &Ub[kUChunks.row[ci]][8 * kUChunks.grp[ci]];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ring[ci % kRing][t] = src[t];
+  };
+#pragma unroll
+  for (int ci = 0; ci < kRing; ++ci) fetch(ci);
+  uint32_t packed[NB / 4];
+#pragma unroll
+  for (int i = 0; i < NB / 4; ++i) packed[i] = 0;
+  double q = gptq_code(w[0], d, rd);
+  double e = (w[0] - d * q) * Ur[0];
+  int ci = 0;
+#pragma unroll
+  for (int jj = 0; jj < NB; ++jj) {
+    packed[jj >> 2] |= ((uint32_t)(int)q & 0xffu) << (8 * (jj & 3));
+    E[(int64_t)jj * ldE + n] = e;
+    if (jj + 1 < NB) {
+      double qn = 0.0, en = 0.0;
+#pragma unroll
+      for (int g = (jj + 1) / 8; g < NB / 8; ++g, ++ci) {
+        const int s = ci % kRing;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (8 * g + t > jj) w[8 * g + t] = fma(-ring[s][t], e, w[8 * g + t]);
+        if (g == (jj + 1) / 8) {
+          qn = gptq_code(w[jj + 1], d, rd);
+          en = (w[jj + 1] - d * qn) * Ur[jj + 1];
+        }
+        if (ci + kRing < kUChunks.n) fetch(ci + kRing);
+        pin8(w + 8 * g);   // this chunk's products here, the next reads after
+      }
+      q = qn;
+      e = en;
     }
-    __syncthreads();
-    const double e = Es[jj][c];
-    for (int kk = jj + 1 + ((rg - jj - 1) & 3); kk < NB; kk += 4) Wb[kk][c] = Wb[kk][c] - Ub[jj][kk] * e;
-    __syncthreads();
   }
   if (live) {
-    // codes: output channel n, input channels r0 .. r0+63 (16 per row group)
-    int8_t* dst = wq + n * K + r0 + rg * 16;
+    // codes: output channel n, input channels r0 .. r0+63
+    uint4* dst = reinterpret_cast<uint4*>(wq + n * K + r0);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dst[e] = Q[rg * 16 + e][c];
-    for (int kk = rg; kk < NB; kk += 4) E[(int64_t)kk * N + n] = Es[kk][c];
+    for (int i = 0; i < NB / 16; ++i)
+      dst[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
   }
 }
 
 // Later rows: W64[i][n] -= sum_jj U[r0 + jj][i] * E[jj][n], jj < depth (a
 // multiple of 64: the error rows of one block, or of a whole lazy batch), for
 // the rows i = i_first + 64 * blockIdx.y + (0 .. 63), all past r0 + depth;
-// columns n0 = 64 * blockIdx.x.
+// columns n0 = 64 * blockIdx.x.  E's row stride ldE covers every slab.
 __global__ __launch_bounds__(256) void k_gptq_update(double* __restrict__ W64, int64_t K,
-                                                     int64_t N, int64_t r0, int depth,
+                                                     int64_t N, int64_t ldE, int64_t r0, int depth,
                                                      int64_t i_first,
                                                      const double* __restrict__ X,
                                                      const double* __restrict__ E) {
@@ -473,7 +614,7 @@ __global__ __launch_bounds__(256) void k_gptq_update(double* __restrict__ W64, i
     for (int i = 0; i < 16; ++i) {
       const int e = threadIdx.x + 256 * i;
       pu[i] = X[(K - 1 - j0 - e / NB) * K + (K - 1 - i0 - e % NB)];
-      pe[i] = (n0 + e % NB < N) ? E[((int64_t)c * NB + e / NB) * N + n0 + e % NB] : 0.0;
+      pe[i] = E[((int64_t)c * NB + e / NB) * ldE + n0 + e % NB];
     }
   };
   load(0);
@@ -506,7 +647,8 @@ __global__ __launch_bounds__(256) void k_gptq_update(double* __restrict__ W64, i
 size_t gptq_workspace_bytes(int64_t T, int64_t K, int64_t N) {
   auto r256 = [](int64_t b) { return (size_t)((b + 255) & ~int64_t(255)); };
   return r256(K * K * 8) * 2 + r256(K * NB * 8) + r256(K * 8) + r256(K) + r256(T * 4) +
-         r256(K * N * 8) + r256((int64_t)kLazy * NB * N * 8) + r256(K * K * 2);
+         r256(K * N * 8) + r256((int64_t)kLazy * NB * ((N + NB - 1) / NB * NB) * 8) +
+         r256(K * K * 2);
 }
 
 // X = L^-1 on the block range [b0, b0 + nb) (diagonal blocks already in X):
@@ -540,7 +682,8 @@ void launch_gptq(const void* x, bool xbf16, int64_t T, int64_t ldx, bool norm,
   unsigned char* dead = reinterpret_cast<unsigned char*>(p); p += r256(K);
   float* rr = rrow_out ? rrow_out : reinterpret_cast<float*>(p);  p += r256(T * 4);
   double* W64 = reinterpret_cast<double*>(p);          p += r256(K * N * 8);
-  double* E = reinterpret_cast<double*>(p);             p += r256((int64_t)kLazy * NB * N * 8);
+  const int64_t ldE = (N + NB - 1) / NB * NB;
+  double* E = reinterpret_cast<double*>(p);             p += r256((int64_t)kLazy * NB * ldE * 8);
   double* tmp = reinterpret_cast<double*>(p);
   const int nt = (int)(K / NB);
   const int64_t tiles = (int64_t)nt * (nt + 1) / 2;
@@ -594,18 +737,18 @@ void launch_gptq(const void* x, bool xbf16, int64_t T, int64_t ldx, bool norm,
   for (int s0 = 0; s0 < nt; s0 += kLazy) {
     const int s1 = min(nt, s0 + kLazy);
     for (int b = s0; b < s1; ++b) {
-      double* Eb = E + (int64_t)(b - s0) * NB * N;
-      hipLaunchKernelGGL(k_gptq_block, dim3(nslab), dim3(256), 0, st, W64, K, N, b, H, wscale, wq,
-                         Eb);
+      double* Eb = E + (int64_t)(b - s0) * NB * ldE;
+      hipLaunchKernelGGL(k_gptq_block, dim3(nslab), dim3(64), 0, st, W64, K, N, ldE, b, H, wscale,
+                         wq, Eb);
       const int rest_in = s1 - b - 1;
       if (rest_in > 0)
         hipLaunchKernelGGL(k_gptq_update, dim3(nslab, (unsigned)rest_in), dim3(256), 0, st, W64,
-                           K, N, (int64_t)b * NB, NB, (int64_t)(b + 1) * NB, H, Eb);
+                           K, N, ldE, (int64_t)b * NB, NB, (int64_t)(b + 1) * NB, H, Eb);
     }
     const int rest = nt - s1;
     if (rest > 0)
       hipLaunchKernelGGL(k_gptq_update, dim3(nslab, (unsigned)rest), dim3(256), 0, st, W64, K, N,
-                         (int64_t)s0 * NB, (s1 - s0) * NB, (int64_t)s1 * NB, H, E);
+                         ldE, (int64_t)s0 * NB, (s1 - s0) * NB, (int64_t)s1 * NB, H, E);
   }
 }
 
