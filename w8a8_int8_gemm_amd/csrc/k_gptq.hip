@@ -28,7 +28,7 @@ namespace {
 
 constexpr int NB = 64;          // tile / block edge
 constexpr int LDP = NB + 1;     // padded LDS row (fp64)
-constexpr int kLazy = 4;        // blocks per lazy batch of the GPTQ updates
+constexpr int kLazy = 4;        // blocks per lazy batch (Cholesky and GPTQ updates)
 
 typedef double v4d __attribute__((ext_vector_type(4)));
 
@@ -390,40 +390,76 @@ __global__ __launch_bounds__(256) void k_chol_trsm(double* __restrict__ A, int64
   acc.each([&](int r, int c, double v) { A[(ro + r) * K + co + c] = v; });
 }
 
-// Trailing update: A_ij -= L_ip L_jp^T for p < j <= i.
-__global__ __launch_bounds__(256) void k_chol_syrk(double* __restrict__ A, int64_t K, int p) {
+// Trailing update A_ij -= sum over the column blocks c of L_ic L_jc^T, c0 =
+// 64 * (first c) and depth = 64 * (number of c), for the tiles
+//   tri:  j0 <= j <= i < nt (the index lower_pair(blockIdx.x), offset by j0)
+//   else: j = j0 + blockIdx.y, i = j + blockIdx.x < nt.
+// The tiles written (j >= j0) never hold the columns read (c < j0).  The next
+// 64-deep chunk of both operands is loaded while this one's products run.
+__global__ __launch_bounds__(256) void k_chol_syrk(double* __restrict__ A, int64_t K, int64_t c0,
+                                                   int depth, int j0, int nt, int tri) {
   __shared__ double As[NB][LDP];
   __shared__ double Bs[NB][LDP];
   int i, j;
-  lower_pair(blockIdx.x, i, j);
-  i += p + 1;
-  j += p + 1;
-  const int64_t co = (int64_t)p * NB;
-  for (int e = threadIdx.x; e < NB * NB; e += 256) {
-    const int a = e / NB, b = e % NB;
-    As[a][b] = A[((int64_t)i * NB + a) * K + co + b];
-    Bs[b][a] = A[((int64_t)j * NB + a) * K + co + b];   // Bs[k][c] = L_jp[c][k]
+  if (tri) {
+    lower_pair(blockIdx.x, i, j);
+    i += j0;
+    j += j0;
+  } else {
+    j = j0 + (int)blockIdx.y;
+    i = j + (int)blockIdx.x;
+    if (i >= nt) return;   // whole workgroup
   }
-  __syncthreads();
+  const int64_t ri = (int64_t)i * NB, rj = (int64_t)j * NB;
   Tile64 acc;
   acc.zero();
-  acc.mma(As, Bs);
+  // element e = threadIdx.x + 256 u (u < 16): row e / 64, column e % 64 of the
+  // chunk, As[a][b] = L_ic[a][b] and Bs[b][a] = L_jc[a][b]
+  double pa[16], pb[16];
+  auto load = [&](int c) {
+    const int64_t co = c0 + (int64_t)c * NB;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = threadIdx.x + 256 * u, a = e / NB, b = e % NB;
+      pa[u] = A[(ri + a) * K + co + b];
+      pb[u] = A[(rj + a) * K + co + b];
+    }
+  };
+  load(0);
+  for (int c = 0; c < depth / NB; ++c) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = threadIdx.x + 256 * u, a = e / NB, b = e % NB;
+      As[a][b] = pa[u];
+      Bs[b][a] = pb[u];
+    }
+    __syncthreads();
+    if (c + 1 < depth / NB) load(c + 1);
+    asm volatile("" ::: "memory");   // keep those loads ahead of the products
+    acc.mma(As, Bs);
+    __syncthreads();
+  }
   acc.each([&](int r, int c, double v) {
-    double* q = A + ((int64_t)i * NB + r) * K + (int64_t)j * NB + c;
+    double* q = A + (ri + r) * K + rj + c;
     *q = *q - v;
   });
 }
 
-// C = alpha * A B + beta * C on 64 x 64 tiles (M, N, Kd multiples of 64),
-// row-major with leading dimensions; tile (blockIdx.y, blockIdx.x).  Used for
-// the triangular inverse and for the deferred GPTQ updates.
+// C = alpha * A B on 64 x 64 tiles (M, N, Kd multiples of 64), row-major
+// with leading dimensions; tile (blockIdx.y, blockIdx.x).  Used for the
+// triangular inverse.  tri bit 0: A is block lower triangular (its 64 x 64
+// blocks right of the diagonal are zero); bit 1: B is; the products of zero
+// blocks are skipped.
+constexpr int kTriA = 1, kTriB = 2;
 __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t Kd, double alpha,
                                                const double* __restrict__ A, int64_t lda,
                                                const double* __restrict__ B, int64_t ldb,
-                                               double beta, double* __restrict__ C, int64_t ldc) {
+                                               double* __restrict__ C, int64_t ldc, int tri) {
   __shared__ double As[NB][LDP];
   __shared__ double Bs[NB][LDP];
   const int64_t m0 = (int64_t)blockIdx.y * NB, n0 = (int64_t)blockIdx.x * NB;
+  const int64_t k_lo = (tri & kTriB) ? n0 : 0;
+  const int64_t k_hi = (tri & kTriA) ? min(Kd, m0 + NB) : Kd;
   Tile64 acc;
   acc.zero();
   // element e = threadIdx.x + 256 i (i < 16) of each 64 x 64 operand chunk;
@@ -437,8 +473,8 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t Kd,
       pb[i] = B[(k0 + a) * ldb + n0 + b];
     }
   };
-  load(0);
-  for (int64_t k0 = 0; k0 < Kd; k0 += NB) {
+  if (k_lo < k_hi) load(k_lo);
+  for (int64_t k0 = k_lo; k0 < k_hi; k0 += NB) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int e = threadIdx.x + 256 * i, a = e / NB, b = e % NB;
@@ -446,16 +482,12 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t Kd,
       Bs[a][b] = pb[i];
     }
     __syncthreads();
-    if (k0 + NB < Kd) load(k0 + NB);
+    if (k0 + NB < k_hi) load(k0 + NB);
     asm volatile("" ::: "memory");   // keep those loads ahead of the products
     acc.mma(As, Bs);
     __syncthreads();
   }
-  acc.each([&](int r, int c, double x) {
-    double* q = C + (m0 + r) * ldc + n0 + c;
-    const double v = alpha * x;
-    *q = (beta == 0.0) ? v : v + beta * *q;
-  });
+  acc.each([&](int r, int c, double x) { C[(m0 + r) * ldc + n0 + c] = alpha * x; });
 }
 
 // X = L^-1 before the recursion: X_ii = Dinv[i], every other block 0 (the
@@ -663,10 +695,10 @@ static void trinv_rec(const double* L, double* X, double* tmp, int64_t K, int b0
   const int64_t s1 = (int64_t)h * NB, s2 = (int64_t)h2 * NB;
   // tmp [s2, s1] = L21 X11
   hipLaunchKernelGGL(k_dgemm, dim3((unsigned)h, (unsigned)h2), dim3(256), 0, st, s2, s1, s1, 1.0,
-                     L + o2 * K + o1, K, X + o1 * K + o1, K, 0.0, tmp, s1);
+                     L + o2 * K + o1, K, X + o1 * K + o1, K, tmp, s1, kTriB);
   // X21 = -X22 tmp
   hipLaunchKernelGGL(k_dgemm, dim3((unsigned)h, (unsigned)h2), dim3(256), 0, st, s2, s1, s2, -1.0,
-                     X + o2 * K + o2, K, tmp, s1, 0.0, X + o2 * K + o1, K);
+                     X + o2 * K + o2, K, tmp, s1, X + o2 * K + o1, K, kTriA);
 }
 
 void launch_gptq(const void* x, bool xbf16, int64_t T, int64_t ldx, bool norm,
@@ -709,15 +741,27 @@ void launch_gptq(const void* x, bool xbf16, int64_t T, int64_t ldx, bool norm,
   // 2. dead inputs, damping, reversal
   hipLaunchKernelGGL(k_hess_diag, dim3(1), dim3(256), 0, st, H, K, damp, dg, dead);
   hipLaunchKernelGGL(k_hess_reverse, gt, dim3(256), 0, st, H, K, dg, A);
-  // 3. Cholesky of A, then X = L^-1 into H's storage
-  for (int q = 0; q < nt; ++q) {
-    hipLaunchKernelGGL(k_chol_panel, dim3(1), dim3(64), 0, st, A, K, q, Dinv);
-    const int rest = nt - q - 1;
-    if (rest > 0) {
-      hipLaunchKernelGGL(k_chol_trsm, dim3((unsigned)rest), dim3(256), 0, st, A, K, q, Dinv);
-      hipLaunchKernelGGL(k_chol_syrk, dim3((unsigned)((int64_t)rest * (rest + 1) / 2)), dim3(256),
-                         0, st, A, K, q);
+  // 3. Cholesky of A, then X = L^-1 into H's storage.  Right-looking in
+  // lazy batches of kLazy column blocks: a block column's update reaches the
+  // rest of its batch's columns (all rows) at once, and the columns past the
+  // batch once per batch with all of its column blocks, so the trailing
+  // matrix is read and written K / (64 kLazy) times instead of K / 64.
+  for (int s0 = 0; s0 < nt; s0 += kLazy) {
+    const int s1 = min(nt, s0 + kLazy);
+    for (int q = s0; q < s1; ++q) {
+      hipLaunchKernelGGL(k_chol_panel, dim3(1), dim3(64), 0, st, A, K, q, Dinv);
+      const int rest = nt - q - 1;
+      if (rest > 0) {
+        hipLaunchKernelGGL(k_chol_trsm, dim3((unsigned)rest), dim3(256), 0, st, A, K, q, Dinv);
+        if (q + 1 < s1)
+          hipLaunchKernelGGL(k_chol_syrk, dim3((unsigned)rest, (unsigned)(s1 - q - 1)), dim3(256),
+                             0, st, A, K, (int64_t)q * NB, NB, q + 1, nt, 0);
+      }
     }
+    const int rest = nt - s1;
+    if (rest > 0)
+      hipLaunchKernelGGL(k_chol_syrk, dim3((unsigned)((int64_t)rest * (rest + 1) / 2)), dim3(256),
+                         0, st, A, K, (int64_t)s0 * NB, (s1 - s0) * NB, s1, nt, 1);
   }
   hipLaunchKernelGGL(k_trinv_init, dim3((unsigned)nt, (unsigned)nt), dim3(256), 0, st, K, Dinv, H);
   trinv_rec(A, H, tmp, K, 0, nt, st);
