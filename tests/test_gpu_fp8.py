@@ -108,6 +108,18 @@ def test_quant_act_fp8_ties_subnormals_and_zero_rows():
     r3[1:40] = np.float32(2.0 ** -12) * np.arange(1, 40)            # deep subnormal quotients
     r3[40] = -0.0
     rows.append(r3)
+    # step 1: one fp32 ulp either side of every midpoint; step 3 (1/3 is
+    # inexact in fp32): three times every midpoint, exactly (ties) and one ulp
+    # below -- quotients the quantizer's product by the reciprocal cannot
+    # place on its own
+    for scale in (1.0, 3.0):
+        for toward in (np.inf, -np.inf):
+            r = np.zeros(K, np.float32)
+            r[0] = np.float32(448.0 * scale)
+            m = (mids[: K - 1] * np.float32(scale)).astype(np.float32)
+            r[1:1 + len(m)] = m if (scale != 1.0 and toward == np.inf) else \
+                np.nextafter(m, np.float32(toward))
+            rows.append(r)
     x = np.stack(rows).astype(np.float32)
     xq, xs = _u8(x.shape), f32(x.shape[0])
     sq.sq_quant_act_fp8(to_dev(x), None, xq, xs)

@@ -96,6 +96,41 @@ __device__ __forceinline__ u32x2 quant8_fp8(const float (&xh)[8], float d) {
   return out;
 }
 
+// FP8 E4M3 codes of 8 values by the reciprocal.  With rc = fp32(1/d) finite,
+// rlo = fp32(rc * (1 - 2^-20)) and rhi = fp32(rc * (1 + 2^-20)), the products
+// x^ * rlo and x^ * rhi miss x^ * (1 -+ 2^-20) / d by under 3 * 2^-24
+// relative, so they bracket both x^ / d and its correctly rounded fp32 value.
+// The conversion is monotonic: where the two ends give the same code, that is
+// quant8_fp8's code.  `split` is set when some pair differs (a quotient near
+// a point where the E4M3 rounding changes, about 4e-5 of them): those 8 codes
+// must then come from quant8_fp8.  CLAMP as there.
+template <bool CLAMP = false>
+__device__ __forceinline__ u32x2 quant8_fp8_rc(const float (&xh)[8], float rlo, float rhi,
+                                               bool& split) {
+  float lo[8], hi[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    lo[i] = xh[i] * rlo;
+    hi[i] = xh[i] * rhi;
+    if (CLAMP) {
+      lo[i] = fminf(fmaxf(lo[i], -448.0f), 448.0f);
+      hi[i] = fminf(fmaxf(hi[i], -448.0f), 448.0f);
+    }
+  }
+  u32x2 a, b;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(lo[4 * h], lo[4 * h + 1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(lo[4 * h + 2], lo[4 * h + 3], w, true);
+    a[h] = (uint32_t)w;
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(hi[4 * h], hi[4 * h + 1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(hi[4 * h + 2], hi[4 * h + 3], w, true);
+    b[h] = (uint32_t)w;
+  }
+  split = ((a[0] ^ b[0]) | (a[1] ^ b[1])) != 0u;
+  return a;
+}
+
 enum { QF_INT8 = 0, QF_FP8 = 1 };
 
 // ---------------------------------------------------------------------------
@@ -210,6 +245,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV, Q
   // division below.
   const bool fast = rc <= 3.0e38f;
   const float rcu = fast ? rc : 0.0f;
+  const float rlo = rcu * (1.0f - 0x1p-20f), rhi = rcu * (1.0f + 0x1p-20f);
   if (lane == 0) xscale[r] = d;
   int8_t* qrow = xq + r * K;
   // exact path for the whole row when 1/d overflows
@@ -221,7 +257,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV, Q
     smooth(jc, xh);
     u32x2 c;
     if constexpr (QF == QF_FP8) {
-      c = quant8_fp8<STATIC>(xh, d);
+      bool split = true;
+      if (fast) c = quant8_fp8_rc<STATIC>(xh, rlo, rhi, split);
+      // rare: near an E4M3 rounding point; d == 0 or 1/d overflowing: all
+      if (split) c = quant8_fp8<STATIC>(xh, d);
     } else {
       bool tie;
       c = quant8<STATIC>(xh, rcu, tie);
@@ -291,6 +330,7 @@ __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem*
   if (threadIdx.x == 0) xscale[r] = d;
   const float rc = 1.0f / d;
   const bool fast = d > 0.0f && rc <= 3.0e38f;
+  const float rlo = rc * (1.0f - 0x1p-20f), rhi = rc * (1.0f + 0x1p-20f);
   for (int64_t ch = threadIdx.x; ch < nchunk; ch += 256) {
     float v[8], xh[8];
     In::load8(row + ch * 8, v);
@@ -303,7 +343,9 @@ __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem*
     c[0] = 0u;
     c[1] = 0u;
     if constexpr (QF == QF_FP8) {
-      c = quant8_fp8<STATIC>(xh, d);
+      bool split = true;
+      if (fast) c = quant8_fp8_rc<STATIC>(xh, rlo, rhi, split);
+      if (split) c = quant8_fp8<STATIC>(xh, d);
     } else {
       bool tie = true;
       if (fast) c = quant8<STATIC>(xh, rc, tie);
