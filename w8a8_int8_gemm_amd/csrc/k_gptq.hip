@@ -11,14 +11,17 @@
 //   3. GPTQ needs U, the upper Cholesky factor of H^-1 (H^-1 = U^T U).  With J
 //      the index reversal, A = J H J = L L^T (lower Cholesky) gives
 //      H = (J L J)(J L J)^T with J L J upper, so H^-1 = (J L^-1 J)^T (J L^-1 J)
-//      and U = J L^-1 J: one blocked Cholesky and one recursive triangular
-//      inverse (X21 = -X22 L21 X11 on halves, as fp64 GEMMs), and U[j][k] is
-//      read as X[K-1-j][K-1-k] from X = L^-1.
+//      and U = J L^-1 J: one blocked Cholesky (one-wave diagonal panels,
+//      trailing updates in lazy batches of kLazy column blocks) and one
+//      recursive triangular inverse (X21 = -X22 L21 X11 on halves, as fp64
+//      GEMMs), and U[j][k] is read as X[K-1-j][K-1-k] from X = L^-1.
 //   4. Rows of W^ (input channels) in blocks of 64: inside a block each row
 //      is rounded with the plain quantizer's per-channel step, its error
-//      e = (w - step * q) / U_jj is pushed onto the block's later rows, and
-//      the block's errors then update every later row at once (an fp64
-//      GEMM).  Output channels are independent, so workgroups split N.
+//      e = (w - step * q) / U_jj is pushed onto the block's later rows (one
+//      wave per 64 output channels, in registers), and the errors of a lazy
+//      batch of kLazy blocks then update the later rows (fp64 GEMMs).  Output
+//      channels are independent, so workgroups split N.
+// The tile products run on the fp64 matrix instruction (Tile64).
 #include "sq_common.h"
 #include "sq_internal.h"
 
