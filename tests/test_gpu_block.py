@@ -39,7 +39,8 @@ def _ln_inputs(T, K, N, Tc, dt="bf16", seed_shift=0):
 
 
 @pytest.mark.parametrize("T,K,dt", [(37, 512, "bf16"), (64, 4096, "bf16"), (20, 1344, "f32"),
-                                    (9, 8192, "bf16"), (5, 16384, "bf16")])
+                                    (9, 8192, "bf16"), (5, 16384, "bf16"), (11, 12352, "bf16"),
+                                    (6, 9216, "f32"), (3, 20480, "bf16")])
 def test_quant_act_ln(T, K, dt):
     wl, inp = _ln_inputs(T, K, 64, 16, dt)
     say(f"ln quant T={T} K={K} {dt}")

@@ -171,8 +171,11 @@ def test_quant_weight_zero_column():
 # (c) fused RMSNorm -> smooth -> per-token quant
 # ---------------------------------------------------------------------------
 
+# K past 8192: a workgroup per token, the row in registers up to 16384 (whole
+# and ragged chunk counts), three passes over the row beyond
 QACT_CASES = [(37, 256, "f32"), (300, 4096, "bf16"), (129, 8192, "bf16"), (3, 320, "bf16"),
-              (5, 16384, "bf16"), (64, 1024, "f32")]
+              (5, 16384, "bf16"), (64, 1024, "f32"), (11, 14336, "bf16"), (4, 8256, "bf16"),
+              (7, 10304, "f32"), (3, 24576, "bf16")]
 
 
 @pytest.mark.parametrize("norm", [False, True])

@@ -134,7 +134,9 @@ __device__ __forceinline__ u32x2 quant8_fp8_rc(const float (&xh)[8], float rlo, 
 enum { QF_INT8 = 0, QF_FP8 = 1 };
 
 // ---------------------------------------------------------------------------
-// K <= 8192: one token per wave, WPB tokens per workgroup.  Lane l owns the
+// K <= 8192 (bf16: K <= 16384, 128 VGPRs of raw values and 64 KiB of LDS
+// for gamma at NV = 32): one token per wave, WPB tokens per workgroup.  Lane
+// l owns the
 // 8-element chunks l, l + 64, ... (NV of them), so every load of a wave is
 // 1 KiB contiguous and every store 512 B.  The token's raw values stay in
 // VGPRs from the load to the store (HBM is read once and written once) and
@@ -272,8 +274,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV, Q
 }
 
 // ---------------------------------------------------------------------------
-// K > 8192: one workgroup per token, three passes over the row (sum of
-// squares, max, quantize); the re-reads hit L2.
+// K > 16384 (K > 8192 for fp32 input): one workgroup per token, three passes
+// over the row (sum of squares, max, quantize); the re-reads hit L2.
 // ---------------------------------------------------------------------------
 template <class In, bool NORM, bool STATIC, int QF>
 __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem* __restrict__ x,
@@ -361,9 +363,9 @@ __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem*
 //   m_t = fp32(mean), r_t = fp32(1/sqrt(var + eps)) (fp64 sums, the variance
 //   about the fp64 mean), x^ = fp32(fp32(fp32(h - m_t) * r_t) * gamma'_k) +
 //   beta'_k, then the per-token INT8 quantizer above.
-// K <= 8192: one token per wave, the row's raw values in VGPRs from the load
-// to the store; gamma' and beta' come through the caches (every token reads
-// the same K floats).
+// K <= 8192 (bf16: K <= 16384): one token per wave, the row's raw values in
+// VGPRs from the load to the store; gamma' and beta' come through the caches
+// (every token reads the same K floats).
 // ---------------------------------------------------------------------------
 template <class In, int NV>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void k_quant_act_ln(
@@ -458,8 +460,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_quant_act_ln(
   }
 }
 
-// K > 8192: one workgroup per token, four passes over the row (sum, squared
-// deviations, maximum, quantize); the re-reads hit L2.
+// K > 16384 (K > 8192 for fp32 input): one workgroup per token, four passes
+// over the row (sum, squared deviations, maximum, quantize); the re-reads hit
+// L2.
 template <class In>
 __global__ __launch_bounds__(256) void k_quant_act_ln_wide(
     const typename In::elem* __restrict__ x, int64_t T, int64_t K, int64_t ld,
@@ -565,7 +568,9 @@ static void quant_act_t(const void* x, int64_t T, int64_t K, int64_t ld, const f
   else if (nchunk <= 256) SQ_QA(4);
   else if (nchunk <= 512) SQ_QA(8);
   else if (nchunk <= 1024) SQ_QA(16);
-  else
+  else if (In::kBytes == 2 && nchunk <= 2048) {
+    if constexpr (In::kBytes == 2) SQ_QA(32);   // bf16 rows up to 16384 in VGPRs
+  } else
     hipLaunchKernelGGL((k_quant_act_wide<In, NORM, STATIC, QF>), dim3((unsigned)T), dim3(256), 0, st,
                        (const typename In::elem*)x, T, K, ld, gamma_f, eps, sscale, xq, xscale,
                        rrow);
@@ -633,7 +638,10 @@ static void quant_act_ln_t(const void* x, int64_t T, int64_t K, int64_t ld, cons
   else if (nchunk <= 512) quant_act_ln_nv<In, 8>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
   else if (nchunk <= 1024)
     quant_act_ln_nv<In, 16>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
-  else
+  else if (In::kBytes == 2 && nchunk <= 2048) {
+    if constexpr (In::kBytes == 2)   // bf16 rows up to 16384 in VGPRs
+      quant_act_ln_nv<In, 32>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
+  } else
     hipLaunchKernelGGL((k_quant_act_ln_wide<In>), dim3((unsigned)T), dim3(256), 0, st,
                        (const typename In::elem*)x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow);
 }
