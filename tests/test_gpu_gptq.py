@@ -49,6 +49,7 @@ def _check_codes(q_gpu, q_ref, quot):
     ("rmsnorm_qkv", dict(T=64, Tc=517, K=512, N=264), "bf16"),
     ("qproj_prefill", dict(T=64, Tc=200, K=320, N=64), "f32"),
     ("rmsnorm_qkv", dict(T=64, Tc=1000, K=1024, N=520), "bf16"),
+    ("qproj_prefill", dict(T=64, Tc=100, K=64, N=72), "bf16"),      # one block, one panel
 ])
 def test_gptq_codes(name, sizes, dt):
     wl = synth.WORKLOADS[name].with_sizes(**sizes)
