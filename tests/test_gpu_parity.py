@@ -205,6 +205,23 @@ def test_quant_act(T, K, dt, norm):
         assert _ulps(r_gpu, r_own).max() <= 1
 
 
+@pytest.mark.parametrize("T,K", [(6, 14336), (3, 4096)])
+def test_quant_act_without_gamma(T, K):
+    """gamma_f = NULL (an unsmoothed linear): the factor 1 on both sides."""
+    rng = np.random.default_rng(T + K)
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    x[:, rng.permutation(K)[:5]] *= 40
+    xin = synth.f32_to_bf16_bits(x)
+    say(f"quant act without gamma T={T} K={K}")
+    xq = torch.empty((T, K), dtype=torch.int8, device=DEV)
+    xs = f32(T)
+    sq.sq_quant_act(to_dev(xin), None, xq, xs)
+    torch.cuda.synchronize()
+    q_ref, xs_ref, _ = oracle.quant_act(xin, np.ones(K, np.float32))
+    np.testing.assert_array_equal(to_np(xs), xs_ref)
+    np.testing.assert_array_equal(to_np(xq), q_ref)
+
+
 def test_quant_act_ties_and_fallback():
     """Rows whose quotients sit exactly on half-integers take the division path."""
     K = 512

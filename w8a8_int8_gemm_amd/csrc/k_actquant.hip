@@ -568,8 +568,12 @@ static void quant_act_t(const void* x, int64_t T, int64_t K, int64_t ld, const f
   else if (nchunk <= 256) SQ_QA(4);
   else if (nchunk <= 512) SQ_QA(8);
   else if (nchunk <= 1024) SQ_QA(16);
-  else if (In::kBytes == 2 && nchunk <= 2048) {
-    if constexpr (In::kBytes == 2) SQ_QA(32);   // bf16 rows up to 16384 in VGPRs
+  else if (In::kBytes == 2 && nchunk <= 2048 && gamma_f != nullptr) {
+    // bf16 rows up to 16384 in VGPRs, gamma_f staged once per workgroup; the
+    // wide kernel reads gamma_f per token through the caches, which costs
+    // more than its extra row passes (104 vs 25 us, 2048 x 14336), but with
+    // no gamma_f its four waves per token win (23 vs 34 us)
+    if constexpr (In::kBytes == 2) SQ_QA(32);
   } else
     hipLaunchKernelGGL((k_quant_act_wide<In, NORM, STATIC, QF>), dim3((unsigned)T), dim3(256), 0, st,
                        (const typename In::elem*)x, T, K, ld, gamma_f, eps, sscale, xq, xscale,
