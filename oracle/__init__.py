@@ -417,30 +417,62 @@ def gptq(w_hat: np.ndarray, xhat: np.ndarray, *, damp: float = 0.01, return_quot
     w_hat [K,N] fp32, xhat [T,K] fp32.  Returns (qw [N,K] int8, w_scale [N]),
     plus the quotients W[j,n] / w_scale[n] the rounding saw [K,N] when asked.
     Output channels never interact, so ``columns`` (indices) computes only
-    those channels; the results are then [len(columns), ...] in that order."""
-    damp = float(np.float32(damp))
+    those channels; the results are then [len(columns), ...] in that order.
+    The two halves are gptq_factor (H and U) and gptq_round (the row loop)."""
     W = np.asarray(w_hat, np.float32)
     if columns is not None:
         W = np.ascontiguousarray(W[:, np.asarray(columns)])
-    K, N = W.shape
-    ws = (np.abs(W).max(axis=0) / np.float32(127)).astype(np.float32)
+    U, dead = gptq_factor(xhat, damp=damp)
+    return gptq_round(W, U, dead, return_quotients=return_quotients)
+
+
+def gptq_factor(xhat: np.ndarray, *, damp: float = 0.01):
+    """(U [K,K] fp64, dead [K] bool): the damped Hessian's inverse factor of
+    gptq.  H = X^T X of the fp32 x^ in fp64; a dead input gets H_jj = 1;
+    H += fp32(damp) * mean(diag H) * I; U = the upper Cholesky factor of H^-1."""
+    damp = float(np.float32(damp))
     X = np.asarray(xhat, np.float32).astype(np.float64)
+    K = X.shape[1]
     H = X.T @ X
-    W = W.astype(np.float64)
     dead = np.diag(H) == 0
     H[dead, dead] = 1.0
-    W[dead, :] = 0.0
     H[np.diag_indices(K)] += damp * np.mean(np.diag(H))
     U = np.linalg.cholesky(np.linalg.inv(H)).T
+    return U, dead
+
+
+def gptq_round(w_hat: np.ndarray, U: np.ndarray, dead: np.ndarray, *, return_quotients=False,
+               force_codes: Optional[np.ndarray] = None,
+               force_rows: Optional[np.ndarray] = None):
+    """The row loop of gptq on w_hat [K,N] fp32 with gptq_factor's (U, dead).
+    force_codes [N,K] int8 with force_rows [N]: in output channel n the rows
+    j < force_rows[n] take the code force_codes[n, j] instead of their own
+    rounding (the error they leave still reaches the later rows).  That
+    continues the algorithm from a given set of earlier decisions, e.g. the
+    other side of a quotient that sits on a rounding boundary."""
+    W = np.array(w_hat, np.float32)
+    K, N = W.shape
+    ws = (np.abs(W).max(axis=0) / np.float32(127)).astype(np.float32)
+    W = W.astype(np.float64)
+    W[dead, :] = 0.0
     d = ws.astype(np.float64)
     live = d > 0
     Q = np.zeros((K, N), np.int8)
     quot = np.zeros((K, N)) if return_quotients else None
+    forced = None
+    if force_codes is not None:
+        fc = np.asarray(force_codes, np.int8)
+        fr = np.asarray(force_rows, np.int64)
+        assert fc.shape == (N, K) and fr.shape == (N,)
+        forced = (fc, fr)
     for j in range(K):
         q = np.zeros(N)
         if quot is not None:
             quot[j, live] = W[j, live] / d[live]
         q[live] = np.clip(np.rint(W[j, live] / d[live]), -127, 127)
+        if forced is not None:
+            take = j < forced[1]
+            q[take] = forced[0][take, j]
         Q[j] = q.astype(np.int8)
         e = (W[j] - d * q) / U[j, j]
         W[j + 1:] -= np.outer(U[j, j + 1:], e)
