@@ -23,10 +23,10 @@
  *   - Argument checks run on the host before any launch and return a status;
  *     nothing is launched when a check fails.  A launch failure reported by
  *     the HIP runtime returns SQ_ERR_HIP.  No call throws across the ABI.
- *   - Supported shapes: K % 64 == 0 and 64 <= K <= 65536; 0 <= T, N <= 2^24
- *     (0 launches nothing); every matrix pointer 16-byte aligned and every
- *     leading dimension a multiple of 16 bytes.  Anything else is
- *     SQ_ERR_UNSUPPORTED.
+ *   - Supported shapes: K % 64 == 0 and 64 <= K <= 65536; any 0 <= T, N <= 2^24
+ *     (0 launches nothing; a ragged last tile or row end is masked); every
+ *     matrix pointer 16-byte aligned and every leading dimension a multiple
+ *     of 16 bytes.  Anything else is SQ_ERR_UNSUPPORTED.
  *   - Scales are fp32.  Rounding is IEEE round-to-nearest-even throughout and
  *     no multiply-add is fused, so results are reproducible bit for bit.
  */
@@ -56,9 +56,13 @@ typedef enum { SQ_F32 = 0, SQ_BF16 = 1, SQ_I8 = 2, SQ_I32 = 3 } sq_dtype;
 
 typedef enum { SQ_NORM_NONE = 0, SQ_NORM_RMS = 1 } sq_norm;
 
-/* sq_calibrate flag: a[] holds a running maximum from earlier calls and is
-   only raised (otherwise it is overwritten). */
+/* sq_calibrate flags.
+   SQ_CALIB_ACCUMULATE: a[] holds a running maximum from earlier calls and is
+     only raised (otherwise it is overwritten).
+   SQ_CALIB_SKIP_ACT: no activation pass; x_cal is not read (pass NULL) and a[]
+     is used as given -- e.g. an alpha sweep over one calibration. */
 #define SQ_CALIB_ACCUMULATE 1u
+#define SQ_CALIB_SKIP_ACT 2u
 
 /*
  * (a) Calibration: per-input-channel activation absmax, per-input-channel
@@ -76,14 +80,16 @@ typedef enum { SQ_NORM_NONE = 0, SQ_NORM_RMS = 1 } sq_norm;
  * gamma the norm's own weight ("SmoothQuant and W8A8", The trick: the smoothed
  * linears read the output of an RMSNorm).
  *
- *   x_cal  [t_cal, k] fp32 or bf16, leading dimension ldx; NULL skips the
- *          activation pass and a[] is used as given (e.g. an alpha sweep)
+ *   x_cal  [t_cal, k] fp32 or bf16, leading dimension ldx; required unless
+ *          flags has SQ_CALIB_SKIP_ACT (then not read: a[] is used as given)
  *   gamma  [k] fp32, norm mode only (NULL = ones)
  *   w      [k, n] fp32 or bf16, leading dimension ldw; NULL skips wmax and s
  *   alpha  migration strength in [0, 1]
- *   a      [k] fp32, out (in/out with SQ_CALIB_ACCUMULATE or x_cal == NULL)
+ *   flags  SQ_CALIB_ACCUMULATE, SQ_CALIB_SKIP_ACT (others: SQ_ERR_UNSUPPORTED)
+ *   a      [k] fp32, out (in/out with SQ_CALIB_ACCUMULATE or SQ_CALIB_SKIP_ACT)
  *   wmax   [k] fp32 out, s [k] fp32 out (both required when w != NULL)
- * Norm mode requires k <= 8192.
+ * Errors: SQ_ERR_NULL for a missing x_cal (without SQ_CALIB_SKIP_ACT), a, or
+ * wmax / s with w; SQ_ERR_ALPHA for alpha outside [0, 1] (checked with w).
  */
 sq_status sq_calibrate(const void *x_cal, sq_dtype x_dt, int64_t t_cal, int64_t k, int64_t ldx,
                        sq_norm norm, const float *gamma, float eps,
@@ -109,6 +115,8 @@ sq_status sq_smooth_fold(const float *s, int64_t k, const float *gamma, float *g
  * Outliers", The Problem: Delta = max|W| / (2^(N-1) - 1), codes rounded to
  * nearest):
  *   W^[j, n]   = W[j, n] * s_j in fp32 when s != NULL (fused fold), else W[j, n]
+ *              (any n >= 1; the columns past n in each padded row of W are
+ *              not read)
  *   w_scale[n] = fp32( max_j |W^[j, n]| / 127 )
  *   wq[n, j]   = clamp( round_half_even( fp32(W^[j, n] / w_scale[n]) ), -127, 127 )
  *                (0 when w_scale[n] == 0)
@@ -305,7 +313,7 @@ sq_status sq_w8a8_linear_static_fp8(const void *x, sq_dtype x_dt, int64_t t, int
  *         row's mean and mean squared deviation from mu_t, summed in fp64
  *   LN(h)[t,j] = fp32( fp32( fp32(h - m_t) * r_t ) * gamma_j ) + beta_j  (fp32)
  * sq_calibrate_ln: as sq_calibrate in norm mode with a[j] = max_t |LN(h)[t,j]|
- *   under the norm's own gamma and beta (NULL = ones / zeros).  k <= 8192.
+ *   under the norm's own gamma and beta (NULL = ones / zeros); same flags.
  * sq_smooth_fold_ln: gamma_out[j] = fp32(gamma_j / s_j), beta_out[j] =
  *   fp32(beta_j / s_j) (NULL gamma = ones, NULL beta = zeros); all outputs
  *   required.
@@ -363,8 +371,8 @@ sq_status sq_fold_prev_linear(const float *s, int64_t k, const void *w_prev, sq_
  * damp >= 0 (0.01 is the usual value); row_rscale (nullable, norm mode)
  * receives the calibration rows' r_t.  workspace: at least
  * sq_gptq_workspace_bytes(t_cal, k, n) bytes of device memory, 256-byte
- * aligned (about 16 k^2 + 8 k n bytes).  k <= 16384, n % 8 == 0; t_cal = 0
- * or n = 0 is SQ_ERR_SHAPE.  The rounding order is the algorithm's; sums
+ * aligned (about 16 k^2 + 8 k n bytes).  k <= 16384; t_cal = 0 or n = 0 is
+ * SQ_ERR_SHAPE.  The rounding order is the algorithm's; sums
  * inside it (the Hessian, the factorizations, the blocked updates) are
  * reordered, so codes can differ from another evaluation only where a
  * quotient lies within rounding of a half-integer.

@@ -16,9 +16,12 @@
 // division.  The result equals round-half-even of the correctly rounded
 // quotient, bit for bit.
 //
-// No clamp to [-127, 127] is needed: |x^| <= max|x^| = 127 * Delta * (1 + e)
-// with |e| <= 2^-24, so |x^ / Delta| and its rounded forms stay below 127.5 and
-// round to at most 127 in magnitude.
+// The reciprocal path needs no clamp to [-127, 127]: it runs only while
+// 1/Delta is finite (Delta >= 2^-128), where Delta = fp32(max|x^| / 127) keeps
+// at least 21 significant bits, so |x^ / Delta| and its rounded forms stay
+// below 127.5 and round to at most 127 in magnitude.  Below that a subnormal
+// step can be rounded by far more (max|x^| = 2e-43 gives Delta = 1e-45 and a
+// quotient of 143), so the division path clamps, as the definition does.
 //
 // Static per-tensor step ("SmoothQuant and W8A8", One layer, measured: one
 // scale per tensor from the calibration tokens' maximum): Delta is given, the
@@ -57,7 +60,9 @@ __device__ __forceinline__ u32x2 quant8(const float (&xh)[8], float rc, bool& ne
   return out;
 }
 
-// exact path for every element (Delta so small that 1/Delta overflows)
+// exact path for every element (near-ties, and Delta so small that 1/Delta
+// overflows); always clamped: a deep subnormal step can leave quotients above
+// 127.5 even for the per-token step
 template <bool CLAMP = false>
 __device__ __forceinline__ u32x2 quant8_div(const float (&xh)[8], float d) {
   u32x2 out;
@@ -65,16 +70,19 @@ __device__ __forceinline__ u32x2 quant8_div(const float (&xh)[8], float d) {
   out[1] = 0u;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    out[i >> 2] |= code_byte(clamp127<CLAMP>(rintf(xh[i] / d))) << (8 * (i & 3));
+    out[i >> 2] |= code_byte(clamp127<true>(rintf(xh[i] / d))) << (8 * (i & 3));
   return out;
 }
 
 // FP8 E4M3 codes of 8 values: the fp32 quotient x^ / d (IEEE division), then
 // v_cvt_pk_fp8_f32, which rounds to the nearest E4M3 value, ties to even.
 // With d = amax / 448 every quotient is at most 448 up to one rounding, inside
-// the format's finite range.  A static step (CLAMP) can see larger quotients:
-// they clip to +-448 first (the conversion would give NaN from 480 up).
-// d == 0 (an all-zero token, or a zero static step) gives codes 0.
+// the format's finite range -- unless d is a deep subnormal rounded far from
+// amax / 448 -- and a static step (CLAMP) can see larger quotients: every
+// quotient clips to +-448 first (the largest finite code, which the
+// definition gives for anything at or past it; the conversion would give NaN
+// from 480 up).  d == 0 (an all-zero token, or a zero static step) gives
+// codes 0.
 template <bool CLAMP = false>
 __device__ __forceinline__ u32x2 quant8_fp8(const float (&xh)[8], float d) {
   u32x2 out;
@@ -84,8 +92,7 @@ __device__ __forceinline__ u32x2 quant8_fp8(const float (&xh)[8], float d) {
   float y[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    y[i] = xh[i] / d;
-    if (CLAMP) y[i] = fminf(fmaxf(y[i], -448.0f), 448.0f);
+    y[i] = fminf(fmaxf(xh[i] / d, -448.0f), 448.0f);
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {

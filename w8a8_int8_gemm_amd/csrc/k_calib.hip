@@ -44,14 +44,24 @@ __global__ __launch_bounds__(256) void k_col_absmax(const typename In::elem* __r
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t c0 = (int64_t)blockIdx.x * 512 + lane * 8;
-  const bool active = c0 < cols;   // cols % 8 == 0, so a lane is all-in or all-out
+  const int64_t nv = cols - c0;   // columns of this lane's 8 that exist
   float mx[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) mx[i] = 0.0f;
 
   const int64_t step = (int64_t)gridDim.y * 4;
   int64_t r = (int64_t)blockIdx.y * 4 + wave;
-  if (active) {
+  if (nv > 0 && nv < 8) {
+    // the ragged end of the rows: the missing columns read as 0
+    const typename In::elem* base = m + c0;
+    for (; r < rows; r += step) {
+      float v[8];
+      In::widen(In::raw8_part(base + r * ld, (int)nv), v);
+      const float sc = kRowScale ? rs[r] : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(kRowScale ? v[i] * sc : v[i]));
+    }
+  } else if (nv > 0) {
     const typename In::elem* base = m + c0;
     for (; r + (U - 1) * step < rows; r += U * step) {
       // the U rows' loads (and their row scales) all in flight before any use
@@ -308,6 +318,143 @@ __global__ __launch_bounds__(256) void k_ln_act_absmax(const typename In::elem* 
 }
 
 // ---------------------------------------------------------------------------
+// Wide rows (K > 8192) in norm mode: the column maxima no longer fit in
+// registers, so they live in LDS.  A workgroup owns a slice of CS columns
+// (the slices of one row range run as blockIdx.y); each wave takes one row at
+// a time, reads it whole for the norm's statistics (fp64 sums, as the narrow
+// kernels), then reads its slice again -- from L2, the row is a few tens of
+// KiB -- and raises the slice maxima with LDS atomics.  Column c of the slice
+// sits at index c + c/64, so the 64 lanes' stride-8 updates fall on 64
+// different banks.
+// ---------------------------------------------------------------------------
+constexpr int kWideCS = 16384;   // columns per slice
+constexpr int kWideLds = kWideCS + kWideCS / 64;
+
+__device__ __forceinline__ int wide_idx(int c) { return c + (c >> 6); }
+
+// fp64 sum over the row of f(v) for every element v (chunks of 8, 4 loads in
+// flight per lane), reduced across the wave
+template <class In, class F>
+__device__ __forceinline__ double wide_row_sum(const typename In::elem* row, int64_t nchunk,
+                                               int lane, F f) {
+  double acc = 0.0;
+  int64_t ch = lane;
+  for (; ch + 3 * 64 < nchunk; ch += 4 * 64) {
+    typename In::Raw raw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) raw[u] = In::raw8(row + (ch + u * 64) * 8);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float v[8];
+      In::widen(raw[u], v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc += f((double)v[i]);
+    }
+  }
+  for (; ch < nchunk; ch += 64) {
+    float v[8];
+    In::load8(row + ch * 8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += f((double)v[i]);
+  }
+  return wave_sum(acc);
+}
+
+template <class In>
+__global__ __launch_bounds__(512) void k_rms_act_absmax_wide(const typename In::elem* __restrict__ h,
+                                                             int64_t rows, int64_t K, int64_t ld,
+                                                             const float* __restrict__ gamma,
+                                                             float eps, float* __restrict__ out) {
+  __shared__ unsigned int lmax[kWideLds];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t c_lo = (int64_t)blockIdx.y * kWideCS;
+  const int cw = (int)min((int64_t)kWideCS, K - c_lo);   // a multiple of 64
+  for (int c = threadIdx.x; c < kWideLds; c += 512) lmax[c] = 0u;
+  __syncthreads();
+  const int64_t nchunk = K >> 3;
+  const double dK = (double)K;
+  for (int64_t r = (int64_t)blockIdx.x * 8 + wave; r < rows; r += (int64_t)gridDim.x * 8) {
+    const typename In::elem* row = h + r * ld;
+    // squares of bf16/fp32 values are exact in fp64
+    const double ss = wide_row_sum<In>(row, nchunk, lane, [](double d) { return d * d; });
+    const float rt = (float)(1.0 / sqrt(ss / dK + (double)eps));
+    for (int ch = lane; ch < (cw >> 3); ch += 64) {
+      float v[8];
+      In::load8(row + c_lo + (int64_t)ch * 8, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        atomicMax(&lmax[wide_idx(ch * 8 + i)], __float_as_uint(fabsf(v[i] * rt)));
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < cw; c += 512) {
+    const float g = gamma ? fabsf(gamma[c_lo + c]) : 1.0f;
+    atomic_max_nonneg(out + c_lo + c, __uint_as_float(lmax[wide_idx(c)]) * g);
+  }
+}
+
+// LayerNorm form of the wide path: the mean, then the squared deviations from
+// it (two fp64 passes over the row), then the slice's running maximum and
+// minimum of n = fp32(fp32(h - m_t) * r_t) as ordered bits in LDS; gamma and
+// beta are applied once per column at the end (f(n) monotone, as in
+// k_ln_act_absmax).
+constexpr int kWideCSLn = 8192;
+constexpr int kWideLdsLn = kWideCSLn + kWideCSLn / 64;
+
+template <class In>
+__global__ __launch_bounds__(512) void k_ln_act_absmax_wide(const typename In::elem* __restrict__ h,
+                                                            int64_t rows, int64_t K, int64_t ld,
+                                                            const float* __restrict__ gamma,
+                                                            const float* __restrict__ beta,
+                                                            float eps, float* __restrict__ out) {
+  __shared__ unsigned int lmax[kWideLdsLn];
+  __shared__ unsigned int lmin[kWideLdsLn];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t c_lo = (int64_t)blockIdx.y * kWideCSLn;
+  const int cw = (int)min((int64_t)kWideCSLn, K - c_lo);
+  for (int c = threadIdx.x; c < kWideLdsLn; c += 512) {
+    lmax[c] = 0u;            // below every ordered value
+    lmin[c] = 0xffffffffu;   // above every ordered value
+  }
+  __syncthreads();
+  const int64_t nchunk = K >> 3;
+  const double dK = (double)K;
+  bool any = false;
+  for (int64_t r = (int64_t)blockIdx.x * 8 + wave; r < rows; r += (int64_t)gridDim.x * 8) {
+    any = true;
+    const typename In::elem* row = h + r * ld;
+    const double mu = wide_row_sum<In>(row, nchunk, lane, [](double d) { return d; }) / dK;
+    const double s2 = wide_row_sum<In>(row, nchunk, lane, [mu](double d) {
+      const double e = d - mu;
+      return e * e;
+    });
+    const float mt = (float)mu;
+    const float rt = (float)(1.0 / sqrt(s2 / dK + (double)eps));
+    for (int ch = lane; ch < (cw >> 3); ch += 64) {
+      float v[8];
+      In::load8(row + c_lo + (int64_t)ch * 8, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const unsigned int o = ordered_bits((v[i] - mt) * rt);
+        atomicMax(&lmax[wide_idx(ch * 8 + i)], o);
+        atomicMin(&lmin[wide_idx(ch * 8 + i)], o);
+      }
+    }
+  }
+  __syncthreads();
+  if (!__syncthreads_or(any)) return;   // this workgroup saw no row
+  for (int c = threadIdx.x; c < cw; c += 512) {
+    const float g = gamma ? gamma[c_lo + c] : 1.0f;
+    const float b = beta ? beta[c_lo + c] : 0.0f;
+    const float hi = from_ordered_bits(lmax[wide_idx(c)]) * g + b;
+    const float lo = from_ordered_bits(lmin[wide_idx(c)]) * g + b;
+    atomic_max_nonneg(out + c_lo + c, fmaxf(fabsf(hi), fabsf(lo)));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Weight row absmax and smoothing factor.  A workgroup of 4 waves takes 16
 // input channels (rows j of the [K, N] weight); each wave streams 4 rows at
 // once, U 16-byte loads per row in flight.  s_j = fp32(a_j^alpha /
@@ -327,7 +474,7 @@ __global__ __launch_bounds__(256) void k_wrow_absmax_s(const typename In::elem* 
   const int64_t j0 = (int64_t)blockIdx.x * 16 + wave * 4;   // K % 16 == 0: all 4 rows exist
   float mx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   int64_t c = (int64_t)lane * 8;
-  for (; c + (U - 1) * 512 < N; c += U * 512) {
+  for (; c + (U - 1) * 512 + 8 <= N; c += U * 512) {
     typename In::Raw raw[4][U];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -343,11 +490,11 @@ __global__ __launch_bounds__(256) void k_wrow_absmax_s(const typename In::elem* 
         for (int i = 0; i < 8; ++i) mx[q] = fmaxf(mx[q], fabsf(v[i]));
       }
   }
-  for (; c < N; c += 512) {
+  for (; c < N; c += 512) {   // the rest, the ragged end of the rows read as 0
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float v[8];
-      In::load8(w + (j0 + q) * ld + c, v);
+      In::widen(raw8_upto<In>(w + (j0 + q) * ld + c, N - c), v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) mx[q] = fmaxf(mx[q], fabsf(v[i]));
     }
@@ -437,9 +584,26 @@ static void rms_absmax_t(const void* h, int64_t rows, int64_t K, int64_t ld, con
   else rms_absmax_nv<In, 16>(h, rows, K, ld, gamma, eps, out, st);
 }
 
+// wide rows: 256 row blocks of 8 rows per column slice (2 workgroups per CU)
+static dim3 wide_grid(int64_t rows, int64_t K, int cs) {
+  int64_t gx = (rows + 7) / 8;
+  if (gx > 256) gx = 256;
+  return dim3((unsigned)gx, (unsigned)((K + cs - 1) / cs));
+}
+
 void launch_rms_act_absmax(const void* h, bool bf16, int64_t rows, int64_t K, int64_t ld,
                            const float* gamma, float eps, float* out, hipStream_t st) {
   if (rows <= 0 || K <= 0) return;
+  if (K > 8192) {
+    const dim3 g = wide_grid(rows, K, kWideCS);
+    if (bf16)
+      hipLaunchKernelGGL(k_rms_act_absmax_wide<Bf16In>, g, dim3(512), 0, st, (const uint16_t*)h,
+                         rows, K, ld, gamma, eps, out);
+    else
+      hipLaunchKernelGGL(k_rms_act_absmax_wide<F32In>, g, dim3(512), 0, st, (const float*)h, rows,
+                         K, ld, gamma, eps, out);
+    return;
+  }
   if (bf16) rms_absmax_t<Bf16In>(h, rows, K, ld, gamma, eps, out, st);
   else rms_absmax_t<F32In>(h, rows, K, ld, gamma, eps, out, st);
 }
@@ -472,6 +636,16 @@ void launch_ln_act_absmax(const void* h, bool bf16, int64_t rows, int64_t K, int
                           const float* gamma, const float* beta, float eps, float* out,
                           hipStream_t st) {
   if (rows <= 0 || K <= 0) return;
+  if (K > 8192) {
+    const dim3 g = wide_grid(rows, K, kWideCSLn);
+    if (bf16)
+      hipLaunchKernelGGL(k_ln_act_absmax_wide<Bf16In>, g, dim3(512), 0, st, (const uint16_t*)h,
+                         rows, K, ld, gamma, beta, eps, out);
+    else
+      hipLaunchKernelGGL(k_ln_act_absmax_wide<F32In>, g, dim3(512), 0, st, (const float*)h, rows,
+                         K, ld, gamma, beta, eps, out);
+    return;
+  }
   if (bf16) ln_absmax_t<Bf16In>(h, rows, K, ld, gamma, beta, eps, out, st);
   else ln_absmax_t<F32In>(h, rows, K, ld, gamma, beta, eps, out, st);
 }

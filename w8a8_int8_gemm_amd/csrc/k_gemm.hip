@@ -37,17 +37,16 @@ namespace sqk {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// 16-byte chunk permutation of an LDS row of 64 bytes.  An MFMA operand read
-// (ds_read_b128) is served 16 lanes at a time, i.e. 16 consecutive rows at one
-// logical chunk; with 64 four-byte banks a pass covers 256 bytes = 16 chunk
-// slots, and row r starts at slot 4*(r % 4).  (r >> 2) & 3 moves the 4 rows
-// that share a start slot onto 4 different chunk slots: no two lanes of a pass
-// share a bank.  (r & 3) would suit a 32-bank LDS that serves 8 lanes a pass.
-template <int SWZ>
+// 16-byte chunk permutation of an LDS row of BK bytes (BK = 64 or 128).  An
+// MFMA operand read (ds_read_b128) is served 16 lanes at a time, i.e. 16
+// consecutive rows at one logical chunk; 64 four-byte banks cover 256 bytes,
+// so 256/BK consecutive rows share one bank window and a row's chunk slots
+// span BK/16 of its 4-bank groups.  Moving row r's chunks by
+// (r / (256/BK)) mod (BK/16) gives the rows that start in the same window
+// different slots: no two lanes of a pass share a bank.
+template <int BK>
 __device__ __forceinline__ int swz(int row) {
-  if (SWZ == 1) return row & 3;
-  if (SWZ == 2) return (row >> 2) & 3;
-  return 0;
+  return (row / (256 / BK)) & (BK / 16 - 1);
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -93,7 +92,7 @@ __device__ __forceinline__ void issue_rows(__amdgpu_buffer_rsrc_t r, int8_t* dst
 // consecutive k (MFMA order, which keeps 16-byte K runs together here), each
 // aligned to the group's largest product with the bits below 2^-13 of it
 // dropped, then adds the group sums in fp32.
-template <int BT, int BN, int WGT, int WGN, int SWZ, int OUT, bool F8>
+template <int BT, int BN, int WGT, int WGN, int BK, int NS, int OUT, bool F8>
 __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __restrict__ xq,
                                                    const float* __restrict__ xs, int T, int K,
                                                    const int8_t* __restrict__ wq,
@@ -104,15 +103,19 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
   // The body uses buffer-resource types that exist only for the GPU target;
   // the host pass needs nothing but the signature for the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int BK = 64;                    // bytes of K per stage
-  constexpr int NS = 4;                     // LDS stages (loads run 3-4 stages ahead)
+  // BK bytes of K per stage (64 or 128), NS stages in LDS
+  static_assert((BK == 64 && NS == 4) || (BK == 128 && NS == 2), "stage shape");
+  static_assert(!F8 || BK == 64, "the FP8 pipeline stages 64 bytes");
   constexpr int NW = WGT * WGN;             // waves: WGT along tokens x WGN along channels
   constexpr int NTH = 64 * NW;
   constexpr int WTT = BT / WGT, WTN = BN / WGN;  // wave tile
   constexpr int NTT = WTT / 32;             // 32x32 tiles per wave along tokens
   constexpr int NTN = WTN / 32;             // ... along output channels
   constexpr int XS = BT * BK, WS = BN * BK; // bytes per stage
-  constexpr int XL = BT / (16 * NW), WL = BN / (16 * NW);  // 1 KiB loads per wave per stage
+  constexpr int CPR = BK / 16;              // 16-byte chunks per staged row
+  constexpr int RPL = 64 / CPR;             // rows per 1 KiB load
+  constexpr int KS = BK / 32;               // INT8 k-steps (32 bytes) per stage
+  constexpr int XL = BT / (RPL * NW), WL = BN / (RPL * NW);  // 1 KiB loads per wave per stage
   constexpr int LPS = XL + WL;              // loads per wave per stage
   constexpr int OPB = NS * (XS + WS);       // operand stages
   constexpr int EPS = WTN * 2 + 16;         // epilogue: bytes per staged output row
@@ -133,23 +136,24 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
 
   // --- global -> LDS through buffer resources based at the tile's first row.
   // Rows past T (or N) are outside the resource's range and read as zeros.
-  // Lane l of a 1 KiB load fills row 16b + l/4, chunk position l%4, which holds
-  // the row's 16-byte K chunk (l%4) ^ swz(row); k0 goes in the scalar offset.
+  // Lane l of a 1 KiB load fills row RPL*b + l/CPR, chunk position l%CPR,
+  // which holds the row's 16-byte K chunk (l%CPR) ^ swz(row); k0 goes in the
+  // scalar offset.  With BK = 128 every load covers whole 128-byte lines.
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(xq + (int64_t)t0 * K), 0, min(BT, T - t0) * K, 0x00020000);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(wq + (int64_t)n0 * K), 0, min(BN, N - n0) * K, 0x00020000);
-  const int lrow = lane >> 2, lchunk = lane & 3;
+  const int lrow = lane / CPR, lchunk = lane % CPR;
   int xoff[XL], woff[WL];
 #pragma unroll
   for (int bb = 0; bb < XL; ++bb) {
-    const int row = (bb * NW + wave) * 16 + lrow;
-    xoff[bb] = row * K + ((lchunk ^ swz<SWZ>(row)) << 4);
+    const int row = (bb * NW + wave) * RPL + lrow;
+    xoff[bb] = row * K + ((lchunk ^ swz<BK>(row)) << 4);
   }
 #pragma unroll
   for (int bb = 0; bb < WL; ++bb) {
-    const int row = (bb * NW + wave) * 16 + lrow;
-    woff[bb] = row * K + ((lchunk ^ swz<SWZ>(row)) << 4);
+    const int row = (bb * NW + wave) * RPL + lrow;
+    woff[bb] = row * K + ((lchunk ^ swz<BK>(row)) << 4);
   }
   auto issue = [&](int stage) {   // K stage `stage` -> LDS buffer stage % NS
     const int buf = stage & (NS - 1);
@@ -190,12 +194,12 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
 #pragma unroll
     for (int i = 0; i < NTN; ++i) {
       const int row = wn * WTN + i * 32 + frow;
-      a[i] = *reinterpret_cast<const v4i*>(wb + row * BK + ((c ^ swz<SWZ>(row)) << 4));
+      a[i] = *reinterpret_cast<const v4i*>(wb + row * BK + ((c ^ swz<BK>(row)) << 4));
     }
 #pragma unroll
     for (int j = 0; j < NTT; ++j) {
       const int row = wt * WTT + j * 32 + frow;
-      b[j] = *reinterpret_cast<const v4i*>(xb + row * BK + ((c ^ swz<SWZ>(row)) << 4));
+      b[j] = *reinterpret_cast<const v4i*>(xb + row * BK + ((c ^ swz<BK>(row)) << 4));
     }
   };
   auto mfmas = [&](const v4i (&a)[NTN], const v4i (&b)[NTT]) {
@@ -208,22 +212,25 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
     }
   };
 
-  // --- pipeline.  Stage s lives in LDS buffer s % 4.  In iteration s the
-  // operands of k-step 1 are read while k-step 0 multiplies; then every wave
-  // waits for stage s+1 to land (its own loads; the barrier makes them
-  // everyone's) and for its reads of stage s to finish, so after the barrier
-  // buffer s % 4 is free: the loads of stage s+4 go there, and k-step 0 of
-  // stage s+1 is read while k-step 1 of stage s multiplies.
+  // --- pipeline.  Stage s lives in LDS buffer s % NS.  In iteration s the
+  // operands of k-step kk+1 are read while k-step kk multiplies; before the
+  // last k-step every wave waits for stage s+1 to land (its own loads; the
+  // barrier makes them everyone's) and for its reads of stage s to finish, so
+  // after the barrier buffer s % NS is free: the loads of stage s+NS go there,
+  // and k-step 0 of stage s+1 is read while the last k-step of s multiplies.
   const int nst = K / BK;
-  issue(0);
-  if (nst > 1) issue(1);
-  if (nst > 2) issue(2);
-  if (nst > 3) issue(3);
-  // stage 0 landed: at most min(nst-1, 3) later stages still in flight
-  if (nst >= 4) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LPS) : "memory");
-  else if (nst == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPS) : "memory");
-  else if (nst == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPS) : "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  static_for<NS>([&](auto s_) {
+    constexpr int sv = decltype(s_)::value;
+    if (sv < nst) issue(sv);
+  });
+  // stage 0 landed: at most min(nst-1, NS-1) later stages still in flight
+  {
+    const int fly0 = min(nst - 1, NS - 1);
+    static_for<NS>([&](auto f_) {
+      constexpr int f = decltype(f_)::value;
+      if (fly0 == f) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(f * LPS) : "memory");
+    });
+  }
   __syncthreads();
   if constexpr (F8) {
     // FP8: one v_mfma_f32_32x32x64_f8f6f4 per 32x32 tile per stage.  A lane's
@@ -241,14 +248,14 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
     auto fa = [&](int stage, int i, v4i& lo, v4i& hi) {
       const int8_t* wb = ws_l + (stage & (NS - 1)) * WS;
       const int row = wn * WTN + i * 32 + frow;
-      lo = *reinterpret_cast<const v4i*>(wb + row * BK + ((fhalf ^ swz<SWZ>(row)) << 4));
-      hi = *reinterpret_cast<const v4i*>(wb + row * BK + (((2 + fhalf) ^ swz<SWZ>(row)) << 4));
+      lo = *reinterpret_cast<const v4i*>(wb + row * BK + ((fhalf ^ swz<BK>(row)) << 4));
+      hi = *reinterpret_cast<const v4i*>(wb + row * BK + (((2 + fhalf) ^ swz<BK>(row)) << 4));
     };
     auto fb = [&](int stage, int j, v4i& lo, v4i& hi) {
       const int8_t* xb = xs_l + (stage & (NS - 1)) * XS;
       const int row = wt * WTT + j * 32 + frow;
-      lo = *reinterpret_cast<const v4i*>(xb + row * BK + ((fhalf ^ swz<SWZ>(row)) << 4));
-      hi = *reinterpret_cast<const v4i*>(xb + row * BK + (((2 + fhalf) ^ swz<SWZ>(row)) << 4));
+      lo = *reinterpret_cast<const v4i*>(xb + row * BK + ((fhalf ^ swz<BK>(row)) << 4));
+      hi = *reinterpret_cast<const v4i*>(xb + row * BK + (((2 + fhalf) ^ swz<BK>(row)) << 4));
     };
     // A1/B1 are written before they are read whenever a next stage exists; the
     // zeros only keep the optimizer from treating them as undefined.
@@ -290,18 +297,17 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
     }
     if (st < nst) step8(st, A0, B0, A1, B1);
   } else {
-  v4i a0[NTN], b0[NTT], a1[NTN], b1[NTT];
-  frags(0, 0, a0, b0);
-  // one iteration; FLY = stages still in flight after stage s+1 has landed
-  // (-1: s is the last stage), ISSUE: the loads of stage s+4 exist.  One wave
-  // per SIMD means nothing else can issue while this wave is busy with
-  // non-MFMA work, so the operand reads and global loads are interleaved
-  // one-for-one with the MFMAs (sched_group_barrier) and run under them:
-  //   A: MFMAs of k-step 0 of stage s   | LDS reads of k-step 1 of stage s
+  v4i fa[2][NTN], fb[2][NTT];
+  frags(0, 0, fa[0], fb[0]);
+  // one stage; FLY = stages still in flight after stage s+1 has landed
+  // (-1: s is the last stage), ISSUE: the loads of stage s+NS exist.  The
+  // operand reads and global loads are interleaved one-for-one with the
+  // MFMAs (sched_group_barrier) and run under them:
+  //   k-step kk < KS-1: MFMAs of kk        | LDS reads of k-step kk+1
   //   wait: stage s+1 landed, own reads of stage s done; workgroup barrier
-  //   B: MFMAs of k-step 1 of stage s   | LDS reads of k-step 0 of stage s+1,
-  //                                     | then the loads of stage s+4 into the
-  //                                     | buffer stage s just vacated
+  //   k-step KS-1:      MFMAs of KS-1      | LDS reads of k-step 0 of stage
+  //                                        | s+1, then the loads of stage
+  //                                        | s+NS into the buffer s vacated
   // The steady state has no branch inside, so nothing forces a full wait.
   auto iter = [&](int st, auto fly_tag, auto issue_tag) {
     constexpr int FLY = decltype(fly_tag)::value;
@@ -309,44 +315,45 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
     constexpr int NF = NTN + NTT;                 // operand reads per k-step
     constexpr int NM = NTN * NTT;                 // MFMAs per k-step
     constexpr int PA = NF < NM ? NF : NM;         // (MFMA, read) pairs
-    frags(st, 1, a1, b1);
-    mfmas(a0, b0);
-#pragma unroll
-    for (int q = 0; q < PA; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-    }
-    if (NM > PA) __builtin_amdgcn_sched_group_barrier(0x008, NM - PA, 0);
-    __builtin_amdgcn_sched_barrier(0);   // keep k-step 0's MFMAs above the barrier
-    if (FLY >= 0) {
-      if (FLY >= 2) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * LPS) : "memory");
-      else if (FLY == 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LPS) : "memory");
-      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (ISSUE) issue(st + NS);
-      frags(st + 1, 0, a0, b0);
-      mfmas(a1, b1);
+    static_for<KS - 1>([&](auto kk_) {
+      constexpr int kk = decltype(kk_)::value;
+      frags(st, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      mfmas(fa[kk & 1], fb[kk & 1]);
 #pragma unroll
       for (int q = 0; q < PA; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);   // 1 LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, kk);   // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, kk);   // 1 LDS read
       }
-      if (NM > PA) __builtin_amdgcn_sched_group_barrier(0x008, NM - PA, 1);
+      if (NM > PA) __builtin_amdgcn_sched_group_barrier(0x008, NM - PA, kk);
+      __builtin_amdgcn_sched_barrier(0);   // keep this k-step's MFMAs in place
+    });
+    constexpr int L = KS - 1;
+    if constexpr (FLY >= 0) {
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(FLY * LPS) : "memory");
+      __syncthreads();
+      if (ISSUE) issue(st + NS);
+      frags(st + 1, 0, fa[(L + 1) & 1], fb[(L + 1) & 1]);
+      mfmas(fa[L & 1], fb[L & 1]);
+#pragma unroll
+      for (int q = 0; q < PA; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, KS);   // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, KS);   // 1 LDS read
+      }
+      if (NM > PA) __builtin_amdgcn_sched_group_barrier(0x008, NM - PA, KS);
     } else {
-      mfmas(a1, b1);
+      mfmas(fa[L & 1], fb[L & 1]);
     }
   };
-  using I2 = std::integral_constant<int, 2>;
-  using I1 = std::integral_constant<int, 1>;
-  using I0 = std::integral_constant<int, 0>;
   using IN = std::integral_constant<int, -1>;
   using BT_ = std::integral_constant<bool, true>;
   using BF_ = std::integral_constant<bool, false>;
   int st = 0;
-  for (; st + NS < nst; ++st) iter(st, I2(), BT_());
-  if (st == nst - 4) iter(st++, I2(), BF_());
-  if (st == nst - 3) iter(st++, I1(), BF_());
-  if (st == nst - 2) iter(st++, I0(), BF_());
+  for (; st + NS < nst; ++st) iter(st, std::integral_constant<int, NS - 2>(), BT_());
+  // the last stages issue nothing: FLY = nst - st - 2 of them still fly
+  static_for<NS - 1>([&](auto i_) {
+    constexpr int f = NS - 2 - decltype(i_)::value;
+    if (st == nst - 2 - f) iter(st++, std::integral_constant<int, f>(), BF_());
+  });
   iter(st, IN(), BF_());
   }
   __syncthreads();
@@ -474,23 +481,39 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
 // host launcher
 // ---------------------------------------------------------------------------
 
-template <int BT, int BN, int WGT, int WGN, bool F8>
+template <int BT, int BN, int WGT, int WGN, int BK, int NS, bool F8>
 static void gemm_tile(const int8_t* xq, const float* xs, int T, int K, const int8_t* wq,
                       const float* ws, int N, const float* bias, void* y, int ldy, int out,
                       hipStream_t st) {
-  constexpr int SWZ = 2;
   const int ntiles = ((T + BT - 1) / BT) * ((N + BN - 1) / BN);
   const dim3 grid((unsigned)ntiles), block(64 * WGT * WGN);
   const int group_t = 4;
   if (out == OUT_BF16)
-    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, SWZ, OUT_BF16, F8>), grid, block, 0, st, xq,
-                       xs, T, K, wq, ws, N, bias, y, ldy, group_t);
+    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, BK, NS, OUT_BF16, F8>), grid, block, 0, st,
+                       xq, xs, T, K, wq, ws, N, bias, y, ldy, group_t);
   else if (out == OUT_F32)
-    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, SWZ, OUT_F32, F8>), grid, block, 0, st, xq,
-                       xs, T, K, wq, ws, N, bias, y, ldy, group_t);
+    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, BK, NS, OUT_F32, F8>), grid, block, 0, st,
+                       xq, xs, T, K, wq, ws, N, bias, y, ldy, group_t);
   else
-    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, SWZ, OUT_I32, F8>), grid, block, 0, st, xq,
-                       xs, T, K, wq, ws, N, bias, y, ldy, group_t);
+    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, BK, NS, OUT_I32, F8>), grid, block, 0, st,
+                       xq, xs, T, K, wq, ws, N, bias, y, ldy, group_t);
+}
+
+// INT8 with K % 128 == 0 stages 128 bytes of K per row in two buffers: every
+// load then covers whole 128-byte lines, which streams the panels into LDS
+// about 1.5x faster than 64-byte half lines in four buffers.  Other K, and
+// the FP8 pipeline, stage 64 bytes in four buffers.
+template <int BT, int BN, int WGT, int WGN, bool F8>
+static void gemm_tile_k(const int8_t* xq, const float* xs, int T, int K, const int8_t* wq,
+                        const float* ws, int N, const float* bias, void* y, int ldy, int out,
+                        hipStream_t st) {
+  if constexpr (!F8) {
+    if (K % 128 == 0) {
+      gemm_tile<BT, BN, WGT, WGN, 128, 2, F8>(xq, xs, T, K, wq, ws, N, bias, y, ldy, out, st);
+      return;
+    }
+  }
+  gemm_tile<BT, BN, WGT, WGN, 64, 4, F8>(xq, xs, T, K, wq, ws, N, bias, y, ldy, out, st);
 }
 
 // compute units of the current device (looked up once per device; threads
@@ -521,11 +544,11 @@ static void gemm_sizes(const int8_t* xq, const float* xs, int64_t T, int64_t K, 
   const int64_t t256 = ((T + 255) / 256) * ((N + 255) / 256);
   const int64_t t128x256 = ((T + 127) / 128) * ((N + 255) / 256);
   if (t256 >= busy)
-    gemm_tile<256, 256, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+    gemm_tile_k<256, 256, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
   else if (t128x256 >= busy)
-    gemm_tile<128, 256, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+    gemm_tile_k<128, 256, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
   else
-    gemm_tile<128, 128, 2, 2, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+    gemm_tile_k<128, 128, 2, 2, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
 }
 
 void launch_gemm(const int8_t* xq, const float* xs, int64_t T, int64_t K, const int8_t* wq,

@@ -513,15 +513,16 @@ __global__ __launch_bounds__(256) void k_gptq_init(const typename In::elem* __re
                                                    const float* __restrict__ s,
                                                    const unsigned char* __restrict__ dead,
                                                    double* __restrict__ W64) {
-  const int64_t per = N >> 3;
+  const int64_t per = (N + 7) >> 3;   // the last chunk of a row may be ragged
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= K * per) return;
   const int64_t j = c / per, n0 = (c - j * per) * 8;
   float v[8];
-  In::load8(w + j * ld + n0, v);
+  In::widen(raw8_upto<In>(w + j * ld + n0, N - n0), v);
   const float sj = s ? s[j] : 1.0f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) W64[j * N + n0 + e] = dead[j] ? 0.0 : (double)(v[e] * sj);
+  for (int e = 0; e < 8; ++e)
+    if (n0 + e < N) W64[j * N + n0 + e] = dead[j] ? 0.0 : (double)(v[e] * sj);
 }
 
 // Block b (rows r0 = b*64 .. +63) of the rounding for the 64 output channels
@@ -770,7 +771,7 @@ void launch_gptq(const void* x, bool xbf16, int64_t T, int64_t ldx, bool norm,
   trinv_rec(A, H, tmp, K, 0, nt, st);
   // 4. rounding
   {
-    const int64_t chunks = K * (N >> 3);
+    const int64_t chunks = K * ((N + 7) >> 3);
     const dim3 g((unsigned)((chunks + 255) / 256));
     if (wbf16) hipLaunchKernelGGL(k_gptq_init<Bf16In>, g, dim3(256), 0, st, (const uint16_t*)w, K, N, ldw, s, dead, W64);
     else hipLaunchKernelGGL(k_gptq_init<F32In>, g, dim3(256), 0, st, (const float*)w, K, N, ldw, s, dead, W64);

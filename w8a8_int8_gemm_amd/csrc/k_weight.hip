@@ -67,28 +67,36 @@ __global__ __launch_bounds__(256) void k_fold_prev(const typename In::elem* __re
   *reinterpret_cast<f32x4*>(wout + i * ldo + j0 + 4) = o1;
 }
 
-// 8 consecutive elements of one row per thread
+// 8 consecutive elements of one row per thread (fewer at the ragged end of a
+// row; the output rows are 16-byte aligned only when N % 4 == 0)
 template <class In>
 __global__ __launch_bounds__(256) void k_fold_w(const typename In::elem* __restrict__ w,
                                                 int64_t K, int64_t N, int64_t ld,
                                                 const float* __restrict__ s,
                                                 float* __restrict__ wout) {
-  const int64_t chunks_per_row = N >> 3;
+  const int64_t chunks_per_row = (N + 7) >> 3;
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= K * chunks_per_row) return;
   const int64_t j = c / chunks_per_row;
   const int64_t n0 = (c - j * chunks_per_row) * 8;
+  const int64_t nv = N - n0;
   float v[8];
-  In::load8(w + j * ld + n0, v);
+  In::widen(raw8_upto<In>(w + j * ld + n0, nv), v);
   const float sj = s[j];
-  f32x4 o0, o1;
+  if (nv >= 8 && (N & 3) == 0) {
+    f32x4 o0, o1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o0[i] = v[i] * sj;
-    o1[i] = v[4 + i] * sj;
+    for (int i = 0; i < 4; ++i) {
+      o0[i] = v[i] * sj;
+      o1[i] = v[4 + i] * sj;
+    }
+    *reinterpret_cast<f32x4*>(wout + j * N + n0) = o0;
+    *reinterpret_cast<f32x4*>(wout + j * N + n0 + 4) = o1;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < nv) wout[j * N + n0 + i] = v[i] * sj;
   }
-  *reinterpret_cast<f32x4*>(wout + j * N + n0) = o0;
-  *reinterpret_cast<f32x4*>(wout + j * N + n0 + 4) = o1;
 }
 
 // Tile of 128 input channels (k) x 64 output channels (n).  Thread (tx, ty),
@@ -108,19 +116,11 @@ __global__ __launch_bounds__(256) void k_quant_weight_t(const typename In::elem*
   const int64_t n0 = (int64_t)blockIdx.x * NT;
   const int64_t k0 = (int64_t)blockIdx.y * KT;
   const int64_t nb = n0 + tx * 8;
-  const bool ncol = nb < N;   // N % 8 == 0: a thread's 8 columns are all valid or none
+  const bool ncol = nb < N;
+  const int64_t nv = ncol ? N - nb : 8;   // columns of the thread's 8 that exist
 
   float d[8];
-  {
-    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-    const f32x4 d0 = ncol ? *reinterpret_cast<const f32x4*>(wscale + nb) : z;
-    const f32x4 d1 = ncol ? *reinterpret_cast<const f32x4*>(wscale + nb + 4) : z;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      d[i] = d0[i];
-      d[4 + i] = d1[i];
-    }
-  }
+  F32In::widen(ncol ? raw8_upto<F32In>(wscale + nb, nv) : F32In::raw8_part(wscale, 0), d);
 
   // all four rows' loads in flight at once (rows past K read row K-1 and
   // are dropped; columns past N read column 0 and are dropped)
@@ -129,11 +129,11 @@ __global__ __launch_bounds__(256) void k_quant_weight_t(const typename In::elem*
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t k = min(k0 + ty * 4 + r, K - 1);
-    raw[r] = In::raw8(w + k * ld + (ncol ? nb : 0));
+    raw[r] = raw8_upto<In>(w + k * ld + (ncol ? nb : 0), nv);
     sk[r] = kRowScale ? s[k] : 1.0f;
   }
   uint32_t packed[8];
-  // W^ (0 for rows past K and columns past N, whose codes are then 0)
+  // W^ (0 for rows past K and columns past N, whose codes are never written)
   float wh[4][8];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -148,10 +148,12 @@ __global__ __launch_bounds__(256) void k_quant_weight_t(const typename In::elem*
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       // the IEEE quotient, then the nearest E4M3, ties to even; |quotient|
-      // <= 448 up to one rounding
+      // <= 448 up to one rounding except for a deep subnormal step, so it
+      // clips to the largest finite code first
       float q[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) q[r] = d[i] != 0.0f ? wh[r][i] / d[i] : 0.0f;
+      for (int r = 0; r < 4; ++r)
+        q[r] = d[i] != 0.0f ? fminf(fmaxf(wh[r][i] / d[i], -448.0f), 448.0f) : 0.0f;
       int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
       w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
       packed[i] = (uint32_t)w;
@@ -261,12 +263,14 @@ __global__ __launch_bounds__(NT) void k_quant_weight_strip(const uint16_t* __res
   const int strip = (nstrips & 7) == 0 ? (b & 7) * (nstrips >> 3) + (b >> 3) : b;
   const int64_t n0 = (int64_t)strip * 16;
   const int64_t nb = n0 + 8 * h;
-  const bool ncol = nb < N;   // N % 8 == 0: a thread's 8 columns are all valid or none
+  const bool ncol = nb < N;
+  const int64_t nv = ncol ? N - nb : 8;   // columns of the thread's 8 that exist
   const int64_t kq = K >> 2;  // groups of 4 rows (K % 64 == 0)
 
   // The whole strip.  Rows past K read row K-1 again (a duplicate cannot
-  // change a maximum) and columns past N read column 0 (those maxima belong
-  // to no column); neither is ever written out.
+  // change a maximum); a thread wholly past N reads column 0 and one at the
+  // ragged end of the rows reads 0 past N (those values belong to no
+  // column); neither is ever written out.
   float wh[M][4][8];
   {
     Bf16In::Raw raw[M][4];
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(NT) void k_quant_weight_strip(const uint16_t* __res
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t k = min(4 * ((int64_t)rt + RT * m) + r, K - 1);
-        raw[m][r] = Bf16In::raw8(w + k * ld + (ncol ? nb : 0));
+        raw[m][r] = raw8_upto<Bf16In>(w + k * ld + (ncol ? nb : 0), nv);
         sk[m][r] = kRowScale ? s[k] : 1.0f;
       }
 #pragma unroll
@@ -340,7 +344,8 @@ __global__ __launch_bounds__(NT) void k_quant_weight_strip(const uint16_t* __res
         for (int i = 0; i < 8; ++i) {
           float q[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) q[r] = d[i] != 0.0f ? wh[m][r][i] / d[i] : 0.0f;
+          for (int r = 0; r < 4; ++r)
+            q[r] = d[i] != 0.0f ? fminf(fmaxf(wh[m][r][i] / d[i], -448.0f), 448.0f) : 0.0f;
           int x = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
           x = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], x, true);
           pk[i] = (uint32_t)x;
@@ -426,7 +431,7 @@ void launch_fold_prev(const void* w, bool bf16, int64_t Kp, int64_t K, int64_t l
 
 void launch_fold_w(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, const float* s,
                    float* wout, hipStream_t st) {
-  const int64_t chunks = K * (N >> 3);
+  const int64_t chunks = K * ((N + 7) >> 3);
   if (chunks <= 0) return;
   const dim3 grid((unsigned)((chunks + 255) / 256));
   if (bf16)
@@ -473,7 +478,7 @@ void launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, int64
 // K <= 2048 it won at every shape measured (N = 4096: 8.6 vs 13.4 us at
 // K = 1024, 12.1 vs 17.0 at K = 2048).
 bool quant_weight_strip_ok(bool bf16, int64_t K, int64_t N) {
-  if (!(bf16 && K > 0 && K <= 4096 && K % 64 == 0 && N > 0 && N % 8 == 0)) return false;
+  if (!(bf16 && K > 0 && K <= 4096 && K % 64 == 0 && N > 0)) return false;
   const int64_t strips = (N + 15) / 16;
   if (K <= 2048) return strips <= (int64_t)INT32_MAX;
   const int64_t cu = cu_count();

@@ -71,6 +71,16 @@ struct Bf16In {
     r.v = *reinterpret_cast<const u32x4*>(p);
     return r;
   }
+  // the first nv (< 8) of the eight elements at p; the rest read as 0 and are
+  // not touched in memory (the ragged end of a row)
+  __device__ __forceinline__ static Raw raw8_part(const uint16_t* p, int nv) {
+    Raw r;
+    r.v = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < nv) r.v[i >> 1] |= (uint32_t)p[i] << (16 * (i & 1));
+    return r;
+  }
   // hide the value from the optimizer, so that values derived from it are
   // recomputed rather than kept alive
   __device__ __forceinline__ static void opaque(Raw& r) { asm volatile("" : "+v"(r.v)); }
@@ -114,6 +124,17 @@ struct F32In {
     r.b = *reinterpret_cast<const f32x4*>(p + 4);
     return r;
   }
+  __device__ __forceinline__ static Raw raw8_part(const float* p, int nv) {
+    Raw r;
+    r.a = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    r.b = r.a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < nv) r.a[i] = p[i];
+      if (i + 4 < nv) r.b[i] = p[i + 4];
+    }
+    return r;
+  }
   __device__ __forceinline__ static void opaque(Raw& r) {
     asm volatile("" : "+v"(r.a));
     asm volatile("" : "+v"(r.b));
@@ -126,6 +147,13 @@ struct F32In {
     }
   }
 };
+
+// Eight consecutive elements at p of which nv exist (nv >= 8: all of them,
+// one or two 16-byte loads; else the first nv, the rest 0).
+template <class In>
+__device__ __forceinline__ typename In::Raw raw8_upto(const typename In::elem* p, int64_t nv) {
+  return nv >= 8 ? In::raw8(p) : In::raw8_part(p, (int)nv);
+}
 
 // Butterfly reductions across the 64 lanes of a wave.  The combining order is
 // fixed, so the result is deterministic.

@@ -12,7 +12,6 @@ namespace {
 
 constexpr int64_t kMaxK = 65536;
 constexpr int64_t kMaxRows = int64_t(1) << 24;   // tokens (T) and output channels (N) per call
-constexpr int64_t kMaxNormCalibK = 8192;
 constexpr int64_t kMaxGptqK = 16384;   // the K x K fp64 Hessian and its factor: 2 GiB each
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -109,19 +108,18 @@ sq_status sq_calibrate(const void* x_cal, sq_dtype x_dt, int64_t t_cal, int64_t 
                        float* s, hipStream_t stream) {
   SQ_TRY(check_k(k));
   if (a == nullptr) return SQ_ERR_NULL;
-  if ((flags & ~SQ_CALIB_ACCUMULATE) != 0u) return SQ_ERR_UNSUPPORTED;
-  if (x_cal != nullptr) {
+  if ((flags & ~(SQ_CALIB_ACCUMULATE | SQ_CALIB_SKIP_ACT)) != 0u) return SQ_ERR_UNSUPPORTED;
+  const bool act = (flags & SQ_CALIB_SKIP_ACT) == 0u;
+  if (act) {
     SQ_TRY(check_act(x_cal, x_dt, t_cal, k, ldx, norm, eps));
-    if (norm == SQ_NORM_RMS && k > kMaxNormCalibK) return SQ_ERR_UNSUPPORTED;
   }
   if (w != nullptr) {
     SQ_TRY(check_mat(w, w_dt, k, n, ldw));
-    if (n % 8 != 0) return SQ_ERR_UNSUPPORTED;
     if (wmax == nullptr || s == nullptr) return SQ_ERR_NULL;
     if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ALPHA;
   }
-  if (x_cal == nullptr && w == nullptr) return SQ_OK;
-  if (x_cal != nullptr) {
+  if (!act && w == nullptr) return SQ_OK;
+  if (act) {
     if ((flags & SQ_CALIB_ACCUMULATE) == 0u) sqk::launch_fill_f32(a, k, 0.0f, stream);
     if (norm == SQ_NORM_RMS)
       sqk::launch_rms_act_absmax(x_cal, x_dt == SQ_BF16, t_cal, k, ldx, gamma, eps, a, stream);
@@ -141,7 +139,7 @@ sq_status sq_smooth_fold(const float* s, int64_t k, const float* gamma, float* g
   const bool do_w = (w != nullptr && w_out != nullptr);
   if (do_w) {
     SQ_TRY(check_mat(w, w_dt, k, n, ldw));
-    if (n % 8 != 0 || !aligned16(w_out)) return SQ_ERR_UNSUPPORTED;
+    if (!aligned16(w_out)) return SQ_ERR_UNSUPPORTED;
   }
   if (gamma_out == nullptr && !do_w) return SQ_OK;
   if (gamma_out != nullptr) sqk::launch_fold_gamma(s, gamma, gamma_out, k, stream);
@@ -154,7 +152,7 @@ sq_status sq_quant_weight(const void* w, sq_dtype w_dt, int64_t k, int64_t n, in
   SQ_TRY(check_k(k));
   SQ_TRY(check_mat(w, w_dt, k, n, ldw));
   if (wq == nullptr || w_scale == nullptr) return SQ_ERR_NULL;
-  if (n % 8 != 0 || !aligned16(wq)) return SQ_ERR_UNSUPPORTED;
+  if (!aligned16(wq)) return SQ_ERR_UNSUPPORTED;
   if (n == 0) return SQ_OK;
   if (sqk::quant_weight_strip_ok(w_dt == SQ_BF16, k, n)) {
     sqk::launch_quant_weight_strip(w, k, n, ldw, s, w_scale, wq, stream);
@@ -171,7 +169,7 @@ sq_status sq_quant_weight_fp8(const void* w, sq_dtype w_dt, int64_t k, int64_t n
   SQ_TRY(check_k(k));
   SQ_TRY(check_mat(w, w_dt, k, n, ldw));
   if (wq == nullptr || w_scale == nullptr) return SQ_ERR_NULL;
-  if (n % 8 != 0 || !aligned16(wq)) return SQ_ERR_UNSUPPORTED;
+  if (!aligned16(wq)) return SQ_ERR_UNSUPPORTED;
   if (n == 0) return SQ_OK;
   if (sqk::quant_weight_strip_ok(w_dt == SQ_BF16, k, n)) {
     sqk::launch_quant_weight_strip_fp8(w, k, n, ldw, s, w_scale, wq, stream);
@@ -403,7 +401,7 @@ sq_status sq_quant_weight_gptq(const void* x_cal, sq_dtype x_dt, int64_t t_cal, 
   SQ_TRY(check_mat(w, w_dt, k, n, ldw));
   if (wq == nullptr || w_scale == nullptr) return SQ_ERR_NULL;
   if (t_cal == 0 || n == 0) return SQ_ERR_SHAPE;
-  if (k > kMaxGptqK || n % 8 != 0 || !aligned16(wq)) return SQ_ERR_UNSUPPORTED;
+  if (k > kMaxGptqK || !aligned16(wq)) return SQ_ERR_UNSUPPORTED;
   if (!(damp >= 0.0f && isfinite(damp))) return SQ_ERR_SHAPE;
   if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0 ||
       ws_bytes < sqk::gptq_workspace_bytes(t_cal, k, n))
@@ -422,19 +420,18 @@ sq_status sq_calibrate_ln(const void* x_cal, sq_dtype x_dt, int64_t t_cal, int64
                           float* a, float* wmax, float* s, hipStream_t stream) {
   SQ_TRY(check_k(k));
   if (a == nullptr) return SQ_ERR_NULL;
-  if ((flags & ~SQ_CALIB_ACCUMULATE) != 0u) return SQ_ERR_UNSUPPORTED;
-  if (x_cal != nullptr) {
+  if ((flags & ~(SQ_CALIB_ACCUMULATE | SQ_CALIB_SKIP_ACT)) != 0u) return SQ_ERR_UNSUPPORTED;
+  const bool act = (flags & SQ_CALIB_SKIP_ACT) == 0u;
+  if (act) {
     SQ_TRY(check_act(x_cal, x_dt, t_cal, k, ldx, SQ_NORM_RMS, eps));
-    if (k > kMaxNormCalibK) return SQ_ERR_UNSUPPORTED;
   }
   if (w != nullptr) {
     SQ_TRY(check_mat(w, w_dt, k, n, ldw));
-    if (n % 8 != 0) return SQ_ERR_UNSUPPORTED;
     if (wmax == nullptr || s == nullptr) return SQ_ERR_NULL;
     if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ALPHA;
   }
-  if (x_cal == nullptr && w == nullptr) return SQ_OK;
-  if (x_cal != nullptr) {
+  if (!act && w == nullptr) return SQ_OK;
+  if (act) {
     if ((flags & SQ_CALIB_ACCUMULATE) == 0u) sqk::launch_fill_f32(a, k, 0.0f, stream);
     sqk::launch_ln_act_absmax(x_cal, x_dt == SQ_BF16, t_cal, k, ldx, gamma, beta, eps, a, stream);
   }
