@@ -191,6 +191,28 @@ sq_status sq_w8a8_linear(const void *x, sq_dtype x_dt, int64_t t, int64_t k, int
                          hipStream_t stream);
 
 /*
+ * sq_w8a8_linear without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The codes and per-token steps go to a
+ * scratch array the library holds on each GPU it runs on
+ * (SQ_NOALLOC_SCRATCH_BYTES, kept until the process ends); the call allocates
+ * nothing.  Arguments, results and errors are those of sq_w8a8_linear, plus
+ * SQ_ERR_WORKSPACE when sq_linear_workspace_bytes(t, k) exceeds
+ * SQ_NOALLOC_SCRATCH_BYTES (no debug xq / x_scale supplied) and SQ_ERR_HIP if
+ * the scratch array's address cannot be obtained for the current device.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be serialized by the
+ * caller.  The array is fully written before it is read in each call, so
+ * nothing needs clearing between calls.
+ */
+#define SQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+sq_status sq_w8a8_linear_noalloc(const void *x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
+                                 sq_norm norm, const float *gamma_f, float eps,
+                                 const int8_t *wq, const float *w_scale, int64_t n,
+                                 const float *bias, void *y, sq_dtype y_dt, int64_t ldy,
+                                 const sq_debug_out *dbg, hipStream_t stream);
+
+/*
  * Static per-tensor activation step -- one scale for every token, from the
  * calibration tokens' maximum ("SmoothQuant and W8A8", One layer, measured;
  * "06 -- SmoothQuant" section 7: per-token or per-tensor activation scales).

@@ -273,6 +273,19 @@ def test_gptq_validation(L):
 
 
 @no_device
+def test_noalloc_validation(L):
+    f = L.sq_w8a8_linear_noalloc
+    assert f(None, sq.SQ_BF16, 4, 64, 64, 0, None, 1e-6, A16, A16, 8, None, A16, sq.SQ_BF16, 8,
+             None, None) == sq.SQ_ERR_NULL
+    assert f(A16, sq.SQ_BF16, 4, 96, 96, 0, None, 1e-6, A16, A16, 8, None, A16, sq.SQ_BF16, 8,
+             None, None) == sq.SQ_ERR_UNSUPPORTED
+    # past the scratch array: refused before the device is touched
+    t = (64 << 20) // 4096
+    assert f(A16, sq.SQ_BF16, t, 4096, 4096, 0, None, 1e-6, A16, A16, 8, None, A16, sq.SQ_BF16, 8,
+             None, None) == sq.SQ_ERR_WORKSPACE
+
+
+@no_device
 def test_row_limits(L):
     big = (1 << 24) + 1
     assert L.sq_quant_act(A16, sq.SQ_BF16, big, 64, 64, 0, None, 1e-6, A16, A16, None,

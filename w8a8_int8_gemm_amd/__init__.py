@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.sq_linear_workspace_bytes.restype = ctypes.c_size_t
         L.sq_w8a8_linear.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, I64, P, P, I, I64, P,
                                      ctypes.c_size_t, ctypes.POINTER(_DebugOut), P]
+        L.sq_w8a8_linear_noalloc.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, I64, P, P, I,
+                                             I64, ctypes.POINTER(_DebugOut), P]
         L.sq_act_static_scale.argtypes = [P, P, I64, P, P]
         L.sq_quant_act_static.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, P, P, P]
         L.sq_w8a8_linear_static.argtypes = [P, I, I64, I64, I64, I, P, F, P, P, P, I64, P, P, I,
@@ -86,7 +88,7 @@ def lib() -> ctypes.CDLL:
         L.sq_status_string.restype = ctypes.c_char_p
         L.sq_abi_version.restype = I
         for name in ("sq_calibrate", "sq_smooth_fold", "sq_quant_weight", "sq_quant_act",
-                     "sq_gemm_w8a8", "sq_w8a8_linear"):
+                     "sq_gemm_w8a8", "sq_w8a8_linear", "sq_w8a8_linear_noalloc"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -309,6 +311,26 @@ def sq_w8a8_linear(x, gamma_f, wq, w_scale, y, workspace, *, norm: bool = False,
                                 _ptr(wq), _ptr(w_scale), N, _ptr(bias), _ptr(y), ydt, yld,
                                 _ptr(workspace), ws_bytes, dbg, _stream(stream)),
            "sq_w8a8_linear")
+
+
+def sq_w8a8_linear_noalloc(x, gamma_f, wq, w_scale, y, *, norm: bool = False,
+                           eps: float = 1e-6, bias=None, dbg_xq=None, dbg_x_scale=None,
+                           dbg_row_rscale=None, dbg_acc=None, stream=None) -> None:
+    """sq_w8a8_linear with the library's per-device scratch array in place of a
+    workspace: no allocation (SQ_NOALLOC_SCRATCH_BYTES) -- see sq_w8a8_linear_noalloc."""
+    T, K, ld = _mat(x, "x", _FP)
+    N, _, _ = _mat(wq, "wq", ("int8",), cols=K)
+    _need(wq, "wq", ("int8",), N * K)
+    _need(gamma_f, "gamma_f", ("float32",), K)
+    _need(w_scale, "w_scale", ("float32",), N, required=dbg_acc is None)
+    _need(bias, "bias", ("float32",), N)
+    dbg = _dbg(T, K, N, ("int8",), dbg_xq, dbg_x_scale, dbg_row_rscale, dbg_acc, ("int32",))
+    ydt, yld = _out(y, T, N, dbg_acc)
+    _check(lib().sq_w8a8_linear_noalloc(_ptr(x), _dtype(x), T, K, ld,
+                                        SQ_NORM_RMS if norm else SQ_NORM_NONE, _ptr(gamma_f), eps,
+                                        _ptr(wq), _ptr(w_scale), N, _ptr(bias), _ptr(y), ydt, yld,
+                                        dbg, _stream(stream)),
+           "sq_w8a8_linear_noalloc")
 
 
 def sq_act_static_scale(a, gamma_f, x_scale_static, *, stream=None) -> None:

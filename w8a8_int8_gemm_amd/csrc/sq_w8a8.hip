@@ -1,9 +1,13 @@
 // sq_w8a8.hip -- the C ABI of libsqw8a8.so (declared in include/sq_w8a8.h).
 // Host side only: argument checks, then stream-ordered kernel launches.  The
-// library allocates nothing and keeps no state.
+// library allocates nothing; its only state is the per-device address of the
+// scratch array behind sq_w8a8_linear_noalloc.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <atomic>
+#include <mutex>
 
 #include "sq_internal.h"
 #include "sq_w8a8.h"
@@ -282,6 +286,42 @@ size_t sq_linear_workspace_bytes(int64_t t, int64_t k) {
 
 }  // extern "C"
 
+// The workspace of sq_w8a8_linear_noalloc (codes and per-token steps): one
+// copy on each GPU the library runs on, for the life of the process.  Host
+// code never uses this name as an address -- on the host it is a stand-in --
+// only the device address hipGetSymbolAddress returns for it.
+static __device__ __align__(256) int8_t scratch[SQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// the current device's address of `scratch`, looked up on the first call on
+// that device (with it current) and kept
+sq_status scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SQ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SQ_ERR_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+        (void)hipGetLastError();
+        return SQ_ERR_HIP;
+      }
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SQ_OK;
+}
+
+}  // namespace
+
 namespace {
 
 // the forward of sq_w8a8_linear (static_scale NULL), sq_w8a8_linear_static and
@@ -349,6 +389,22 @@ sq_status sq_w8a8_linear(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int
                          const sq_debug_out* dbg, hipStream_t stream) {
   return linear_impl(x, x_dt, t, k, ldx, norm, gamma_f, eps, nullptr, false, wq, w_scale, n, bias,
                      y, y_dt, ldy, workspace, ws_bytes, dbg, stream);
+}
+
+sq_status sq_w8a8_linear_noalloc(const void* x, sq_dtype x_dt, int64_t t, int64_t k,
+                                 int64_t ldx, sq_norm norm, const float* gamma_f, float eps,
+                                 const int8_t* wq, const float* w_scale, int64_t n,
+                                 const float* bias, void* y, sq_dtype y_dt, int64_t ldy,
+                                 const sq_debug_out* dbg, hipStream_t stream) {
+  // the activation's own checks first, so that a bad call touches no device state
+  SQ_TRY(check_act(x, x_dt, t, k, ldx, norm, eps));
+  const bool own_codes = dbg != nullptr && dbg->xq != nullptr && dbg->x_scale != nullptr;
+  if (!own_codes && sq_linear_workspace_bytes(t, k) > SQ_NOALLOC_SCRATCH_BYTES)
+    return SQ_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (t > 0) SQ_TRY(scratch_ptr(&ws));
+  return linear_impl(x, x_dt, t, k, ldx, norm, gamma_f, eps, nullptr, false, wq, w_scale, n, bias,
+                     y, y_dt, ldy, ws, SQ_NOALLOC_SCRATCH_BYTES, dbg, stream);
 }
 
 sq_status sq_w8a8_linear_fp8(const void* x, sq_dtype x_dt, int64_t t, int64_t k, int64_t ldx,
