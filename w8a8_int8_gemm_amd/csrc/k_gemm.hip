@@ -105,7 +105,6 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
 #if defined(__HIP_DEVICE_COMPILE__)
   // BK bytes of K per stage (64 or 128), NS stages in LDS
   static_assert((BK == 64 && NS == 4) || (BK == 128 && NS == 2), "stage shape");
-  static_assert(!F8 || BK == 64, "the FP8 pipeline stages 64 bytes");
   constexpr int NW = WGT * WGN;             // waves: WGT along tokens x WGN along channels
   constexpr int NTH = 64 * NW;
   constexpr int WTT = BT / WGT, WTN = BN / WGN;  // wave tile
@@ -114,7 +113,8 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
   constexpr int XS = BT * BK, WS = BN * BK; // bytes per stage
   constexpr int CPR = BK / 16;              // 16-byte chunks per staged row
   constexpr int RPL = 64 / CPR;             // rows per 1 KiB load
-  constexpr int KS = BK / 32;               // INT8 k-steps (32 bytes) per stage
+  constexpr int KB = F8 ? 64 : 32;          // bytes of K per MFMA (one k-step)
+  constexpr int KS = BK / KB;               // k-steps per stage
   constexpr int XL = BT / (RPL * NW), WL = BN / (RPL * NW);  // 1 KiB loads per wave per stage
   constexpr int LPS = XL + WL;              // loads per wave per stage
   constexpr int OPB = NS * (XS + WS);       // operand stages
@@ -184,32 +184,48 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
-  // --- MFMA operands of k-step kk (32 bytes of K) of a stage
+  // --- MFMA operands of k-step kk of a stage.  INT8: the 16-byte chunk
+  // 2kk + h of the row (h = lane / 32), the K layout of
+  // v_mfma_i32_32x32x32_i8.  FP8: the chunks 4kk + h and 4kk + 2 + h, the 32
+  // bytes a lane gives v_mfma_f32_32x32x64_f8f6f4; A and B take the same
+  // positions, so each stage's sum runs over its 128 (or 64) K values in a
+  // permuted order, and each group of 8 consecutive MFMA k is 8 consecutive k
+  // of one 16-byte chunk.
+  typedef int v8i_t __attribute__((ext_vector_type(8)));
+  typedef typename std::conditional<F8, v8i_t, v4i>::type OpT;
   const int frow = lane & 31, fhalf = lane >> 5;
-  auto frags = [&](int stage, int kk, v4i (&a)[NTN], v4i (&b)[NTT]) {
+  auto frags = [&](int stage, int kk, OpT (&a)[NTN], OpT (&b)[NTT]) {
     const int buf = stage & (NS - 1);
     const int8_t* wb = ws_l + buf * WS;
     const int8_t* xb = xs_l + buf * XS;
-    const int c = kk * 2 + fhalf;
+    auto chunk = [&](const int8_t* base, int row, int c) {
+      return *reinterpret_cast<const v4i*>(base + row * BK + ((c ^ swz<BK>(row)) << 4));
+    };
+    auto op = [&](const int8_t* base, int row) -> OpT {
+      if constexpr (F8) {
+        const int c0 = kk * 4 + fhalf;
+        return __builtin_shufflevector(chunk(base, row, c0), chunk(base, row, c0 + 2), 0, 1, 2,
+                                       3, 4, 5, 6, 7);
+      } else {
+        return chunk(base, row, kk * 2 + fhalf);
+      }
+    };
 #pragma unroll
-    for (int i = 0; i < NTN; ++i) {
-      const int row = wn * WTN + i * 32 + frow;
-      a[i] = *reinterpret_cast<const v4i*>(wb + row * BK + ((c ^ swz<BK>(row)) << 4));
-    }
+    for (int i = 0; i < NTN; ++i) a[i] = op(wb, wn * WTN + i * 32 + frow);
 #pragma unroll
-    for (int j = 0; j < NTT; ++j) {
-      const int row = wt * WTT + j * 32 + frow;
-      b[j] = *reinterpret_cast<const v4i*>(xb + row * BK + ((c ^ swz<BK>(row)) << 4));
-    }
+    for (int j = 0; j < NTT; ++j) b[j] = op(xb, wt * WTT + j * 32 + frow);
   };
-  auto mfmas = [&](const v4i (&a)[NTN], const v4i (&b)[NTT]) {
-    if constexpr (!F8) {
+  auto mfmas = [&](const OpT (&a)[NTN], const OpT (&b)[NTT]) {
 #pragma unroll
-      for (int i = 0; i < NTN; ++i)
+    for (int i = 0; i < NTN; ++i)
 #pragma unroll
-        for (int j = 0; j < NTT; ++j)
+      for (int j = 0; j < NTT; ++j) {
+        if constexpr (F8)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0,
+                                                                       0, 0, 0, 0);
+        else
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
+      }
   };
 
   // --- pipeline.  Stage s lives in LDS buffer s % NS.  In iteration s the
@@ -232,72 +248,7 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
     });
   }
   __syncthreads();
-  if constexpr (F8) {
-    // FP8: one v_mfma_f32_32x32x64_f8f6f4 per 32x32 tile per stage.  A lane's
-    // 32 operand bytes are its two 16-byte chunks of the INT8 layout (k-steps
-    // 0 and 1): the A and B operands take the same K positions, so the sum is
-    // over the stage's 64 K values in a permuted order.  Iteration s: wait for
-    // stage s+1 and for this wave's reads of stage s (issued last iteration),
-    // barrier, loads of stage s+4 into the buffer stage s vacated, then the
-    // MFMAs of stage s column by column, each column's B operands of stage s+1
-    // read as soon as its MFMAs have consumed stage s's.
-    typedef int v8i_t __attribute__((ext_vector_type(8)));
-    auto cat = [](const v4i& lo, const v4i& hi) -> v8i_t {
-      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    auto fa = [&](int stage, int i, v4i& lo, v4i& hi) {
-      const int8_t* wb = ws_l + (stage & (NS - 1)) * WS;
-      const int row = wn * WTN + i * 32 + frow;
-      lo = *reinterpret_cast<const v4i*>(wb + row * BK + ((fhalf ^ swz<BK>(row)) << 4));
-      hi = *reinterpret_cast<const v4i*>(wb + row * BK + (((2 + fhalf) ^ swz<BK>(row)) << 4));
-    };
-    auto fb = [&](int stage, int j, v4i& lo, v4i& hi) {
-      const int8_t* xb = xs_l + (stage & (NS - 1)) * XS;
-      const int row = wt * WTT + j * 32 + frow;
-      lo = *reinterpret_cast<const v4i*>(xb + row * BK + ((fhalf ^ swz<BK>(row)) << 4));
-      hi = *reinterpret_cast<const v4i*>(xb + row * BK + (((2 + fhalf) ^ swz<BK>(row)) << 4));
-    };
-    // A1/B1 are written before they are read whenever a next stage exists; the
-    // zeros only keep the optimizer from treating them as undefined.
-    v4i A0[NTN][2], B0[NTT][2], A1[NTN][2], B1[NTT][2];
-#pragma unroll
-    for (int i = 0; i < NTN; ++i) A1[i][0] = A1[i][1] = v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < NTT; ++j) B1[j][0] = B1[j][1] = v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < NTN; ++i) fa(0, i, A0[i][0], A0[i][1]);
-#pragma unroll
-    for (int j = 0; j < NTT; ++j) fb(0, j, B0[j][0], B0[j][1]);
-    auto step8 = [&](int st, v4i (&ca)[NTN][2], v4i (&cb)[NTT][2], v4i (&na)[NTN][2],
-                     v4i (&nb)[NTT][2]) {
-      const int left = nst - 1 - st;          // stages after st
-      if (left >= 3) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * LPS) : "memory");
-      else if (left == 2) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LPS) : "memory");
-      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (st + NS < nst) issue(st + NS);
-      const bool more = left >= 1;
-#pragma unroll
-      for (int j = 0; j < NTT; ++j) {
-#pragma unroll
-        for (int i = 0; i < NTN; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              cat(ca[i][0], ca[i][1]), cat(cb[j][0], cb[j][1]), acc[i][j], 0, 0, 0, 0, 0, 0);
-        if (more) fb(st + 1, j, nb[j][0], nb[j][1]);
-      }
-      if (more) {
-#pragma unroll
-        for (int i = 0; i < NTN; ++i) fa(st + 1, i, na[i][0], na[i][1]);
-      }
-    };
-    int st = 0;
-    for (; st + 1 < nst; st += 2) {
-      step8(st, A0, B0, A1, B1);
-      step8(st + 1, A1, B1, A0, B0);
-    }
-    if (st < nst) step8(st, A0, B0, A1, B1);
-  } else {
-  v4i fa[2][NTN], fb[2][NTT];
+  OpT fa[2][NTN], fb[2][NTT];
   frags(0, 0, fa[0], fb[0]);
   // one stage; FLY = stages still in flight after stage s+1 has landed
   // (-1: s is the last stage), ISSUE: the loads of stage s+NS exist.  The
@@ -309,16 +260,20 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
   //                                        | s+1, then the loads of stage
   //                                        | s+NS into the buffer s vacated
   // The steady state has no branch inside, so nothing forces a full wait.
-  auto iter = [&](int st, auto fly_tag, auto issue_tag) {
+  // P: which of the two register sets holds k-step 0 of this stage.  With an
+  // even number of k-steps per stage every stage starts in set 0; with an odd
+  // number (FP8 with 64-byte stages: one k-step) the sets alternate by stage.
+  auto iter = [&](int st, auto fly_tag, auto issue_tag, auto par_tag) {
     constexpr int FLY = decltype(fly_tag)::value;
     constexpr bool ISSUE = decltype(issue_tag)::value;
-    constexpr int NF = NTN + NTT;                 // operand reads per k-step
+    constexpr int P = decltype(par_tag)::value;
+    constexpr int NF = (F8 ? 2 : 1) * (NTN + NTT);  // operand reads per k-step
     constexpr int NM = NTN * NTT;                 // MFMAs per k-step
     constexpr int PA = NF < NM ? NF : NM;         // (MFMA, read) pairs
     static_for<KS - 1>([&](auto kk_) {
       constexpr int kk = decltype(kk_)::value;
-      frags(st, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-      mfmas(fa[kk & 1], fb[kk & 1]);
+      frags(st, kk + 1, fa[(P + kk + 1) & 1], fb[(P + kk + 1) & 1]);
+      mfmas(fa[(P + kk) & 1], fb[(P + kk) & 1]);
 #pragma unroll
       for (int q = 0; q < PA; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, kk);   // 1 MFMA
@@ -332,8 +287,8 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(FLY * LPS) : "memory");
       __syncthreads();
       if (ISSUE) issue(st + NS);
-      frags(st + 1, 0, fa[(L + 1) & 1], fb[(L + 1) & 1]);
-      mfmas(fa[L & 1], fb[L & 1]);
+      frags(st + 1, 0, fa[(P + L + 1) & 1], fb[(P + L + 1) & 1]);
+      mfmas(fa[(P + L) & 1], fb[(P + L) & 1]);
 #pragma unroll
       for (int q = 0; q < PA; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, KS);   // 1 MFMA
@@ -341,21 +296,30 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
       }
       if (NM > PA) __builtin_amdgcn_sched_group_barrier(0x008, NM - PA, KS);
     } else {
-      mfmas(fa[L & 1], fb[L & 1]);
+      mfmas(fa[(P + L) & 1], fb[(P + L) & 1]);
+    }
+  };
+  using I0_ = std::integral_constant<int, 0>;
+  using I1_ = std::integral_constant<int, 1>;
+  auto step = [&](int st, auto fly_tag, auto issue_tag) {
+    if constexpr (KS % 2 == 0) {
+      iter(st, fly_tag, issue_tag, I0_());
+    } else {
+      if (st & 1) iter(st, fly_tag, issue_tag, I1_());
+      else iter(st, fly_tag, issue_tag, I0_());
     }
   };
   using IN = std::integral_constant<int, -1>;
   using BT_ = std::integral_constant<bool, true>;
   using BF_ = std::integral_constant<bool, false>;
   int st = 0;
-  for (; st + NS < nst; ++st) iter(st, std::integral_constant<int, NS - 2>(), BT_());
+  for (; st + NS < nst; ++st) step(st, std::integral_constant<int, NS - 2>(), BT_());
   // the last stages issue nothing: FLY = nst - st - 2 of them still fly
   static_for<NS - 1>([&](auto i_) {
     constexpr int f = NS - 2 - decltype(i_)::value;
-    if (st == nst - 2 - f) iter(st++, std::integral_constant<int, f>(), BF_());
+    if (st == nst - 2 - f) step(st++, std::integral_constant<int, f>(), BF_());
   });
-  iter(st, IN(), BF_());
-  }
+  step(st, IN(), BF_());
   __syncthreads();
 
   // --- epilogue.  Lane l of tile (i, j): token t = .. + l%32; channels
@@ -499,21 +463,18 @@ static void gemm_tile(const int8_t* xq, const float* xs, int T, int K, const int
                        xq, xs, T, K, wq, ws, N, bias, y, ldy, group_t);
 }
 
-// INT8 with K % 128 == 0 stages 128 bytes of K per row in two buffers: every
-// load then covers whole 128-byte lines, which streams the panels into LDS
-// about 1.5x faster than 64-byte half lines in four buffers.  Other K, and
-// the FP8 pipeline, stage 64 bytes in four buffers.
+// K % 128 == 0 stages 128 bytes of K per row in two buffers: every load then
+// covers whole 128-byte lines, which streams the panels into LDS about 1.5x
+// faster than 64-byte half lines in four buffers.  Other K stage 64 bytes in
+// four buffers.
 template <int BT, int BN, int WGT, int WGN, bool F8>
 static void gemm_tile_k(const int8_t* xq, const float* xs, int T, int K, const int8_t* wq,
                         const float* ws, int N, const float* bias, void* y, int ldy, int out,
                         hipStream_t st) {
-  if constexpr (!F8) {
-    if (K % 128 == 0) {
-      gemm_tile<BT, BN, WGT, WGN, 128, 2, F8>(xq, xs, T, K, wq, ws, N, bias, y, ldy, out, st);
-      return;
-    }
-  }
-  gemm_tile<BT, BN, WGT, WGN, 64, 4, F8>(xq, xs, T, K, wq, ws, N, bias, y, ldy, out, st);
+  if (K % 128 == 0)
+    gemm_tile<BT, BN, WGT, WGN, 128, 2, F8>(xq, xs, T, K, wq, ws, N, bias, y, ldy, out, st);
+  else
+    gemm_tile<BT, BN, WGT, WGN, 64, 4, F8>(xq, xs, T, K, wq, ws, N, bias, y, ldy, out, st);
 }
 
 // compute units of the current device (looked up once per device; threads
