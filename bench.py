@@ -71,7 +71,8 @@ def _parse():
                     help="instead of benchmarking, run only the headline GEMM back to back for "
                          "this long (for sampling power and clocks from outside) and print the "
                          "time per launch")
-    ap.add_argument("--only", choices=("gptq", "decoder_layer"), default=None,
+    ap.add_argument("--only", choices=("gptq", "decoder_layer", "configs", "decode"),
+                    default=None,
                     help="instead of benchmarking, run only this extra and print its JSON "
                          "(for profiling one part on its own)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -266,6 +267,51 @@ def alpha_sweep(sq, torch, inp, wl, x_cal, x, w, bias, dev, sample=256):
     res["reference"] = ("X W + b in fp64 over evenly spaced tokens; relative Frobenius norm; "
                         "top level: INT8 per-token activation steps")
     return res
+
+
+def hbm_ceilings(torch, dev, T=8192, K=4096, copies=3, iters=20):
+    """Practical HBM ceilings on this machine, measured in the same run with the
+    vendor's own kernels of the same traffic shape as the path's memory-bound
+    kernels, on `copies` rotating inputs (past the Infinity Cache):
+      column_absmax: torch.amax over dim 0 of |X| for X [T, K] bf16 (reads 2 B
+                     per element, writes K floats) -- the calibration pass;
+      read2_write1:  X [T, K] bf16 -> int8 (reads 2 B, writes 1 B per element)
+                     -- the activation and weight quantizers' traffic;
+      copy:          a [T, K] fp32 copy (reads 4 B, writes 4 B per element)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    xs = [torch.randn((T, K), dtype=torch.bfloat16, device=dev, generator=g) for _ in range(copies)]
+    o8 = torch.empty((T, K), dtype=torch.int8, device=dev)
+    f32 = [x.float() for x in xs[:2]]
+    of = torch.empty_like(f32[0])
+    am = torch.empty(K, dtype=torch.bfloat16, device=dev)
+
+    def timed(fn, n):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    out = {}
+    us = timed(lambda i: torch.amax(xs[i % copies], dim=0, out=am), iters)
+    out["column_max"] = {"us": us, "GB/s": 2.0 * T * K / (us * 1e-6) / 1e9,
+                         "note": "torch.amax over dim 0: the calibration pass's traffic"}
+    us = timed(lambda i: o8.copy_(xs[i % copies]), iters)
+    out["read2_write1"] = {"us": us, "GB/s": 3.0 * T * K / (us * 1e-6) / 1e9,
+                           "note": "bf16 -> int8 conversion: the quantizers' traffic"}
+    us = timed(lambda i: of.copy_(f32[i % 2]), iters)
+    out["copy"] = {"us": us, "GB/s": 8.0 * T * K / (us * 1e-6) / 1e9, "note": "fp32 copy"}
+    for v in out.values():
+        v["frac_of_peak"] = v["GB/s"] / PEAK_HBM_GBS
+    out["workload"] = f"[{T}, {K}] inputs, {copies} rotating copies, vendor kernels"
+    del xs, f32
+    return out
 
 
 def vendor_int8_gemm(torch, xq, wq, iters=20):
@@ -558,16 +604,20 @@ def decode_linear_graph(sq, torch, dev, T=16, K=8192, N=8192, iters=50):
             "graph_replay_us": graph_us}
 
 
-def config_step(sq, torch, dev, name, steps=10, warmup=3):
-    """The same whole step (calibrate, fold, quantize the weight, the online
-    linear) on another workload's own synthetic inputs: the RMSNorm -> q|k|v
-    and the MLP gate|up configurations.  One input set (no rotation)."""
+def config_step(sq, torch, dev, name, steps=10, warmup=3, nsets=3):
+    """The same whole step (calibrate, fold, quantize the weight, quantize the
+    activation, the GEMM) on another workload's own synthetic inputs: the
+    RMSNorm -> q|k|v and the MLP gate|up configurations.  As in the headline,
+    the steps take X_cal, X and W in turn from `nsets` copies in HBM, so the
+    Infinity Cache does not hold a step's inputs from the step before.  The
+    timed steps carry no events; a breakdown pass times every call with
+    fence-free HIP events, and each kernel gets its own roofline entry."""
     import numpy as np
 
     import synth
 
     wl = synth.WORKLOADS[name]
-    T, K, N = wl.T, wl.K, wl.N
+    T, K, N, Tc = wl.T, wl.K, wl.N, wl.Tc
     inp = synth.make_inputs(wl)
 
     def d(a):
@@ -576,49 +626,72 @@ def config_step(sq, torch, dev, name, steps=10, warmup=3):
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    x_cal, x, w, bias = d(inp.x_cal), d(inp.x), d(inp.w), d(inp.bias)
+    sets = [(d(inp.x_cal), d(inp.x), d(inp.w)) for _ in range(nsets)]
+    bias = d(inp.bias)
     gamma = None if inp.gamma is None else d(inp.gamma)
     del inp
     f = lambda n: torch.empty(n, dtype=torch.float32, device=dev)  # noqa: E731
-    a, wm, s, gp, wsc = f(K), f(K), f(K), f(K), f(N)
+    a, wm, s, gp, wsc, xs = f(K), f(K), f(K), f(K), f(N), f(T)
+    rr = f(T) if wl.norm else None
     wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    xq = torch.empty((T, K), dtype=torch.int8, device=dev)
     y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
-    work = torch.empty(sq.sq_linear_workspace_bytes(T, K), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    calls = [
-        ("calibrate", lambda: sq.sq_calibrate(x_cal, w, wl.alpha, a, wm, s, norm=wl.norm,
-                                              gamma=gamma, stream=stream)),
-        ("smooth_fold", lambda: sq.sq_smooth_fold(s, gamma, gp, stream=stream)),
-        ("quant_weight", lambda: sq.sq_quant_weight(w, s, wq, wsc, stream=stream)),
-        ("linear", lambda: sq.sq_w8a8_linear(x, gp, wq, wsc, y, work, norm=wl.norm, bias=bias,
-                                             stream=stream)),
-    ]
-    for _ in range(warmup):
-        for _, c in calls:
+    names = ["calibrate", "smooth_fold", "quant_weight", "quant_act", "gemm"]
+
+    def calls(i):
+        x_cal, x, w = sets[i % nsets]
+        return [
+            lambda: sq.sq_calibrate(x_cal, w, wl.alpha, a, wm, s, norm=wl.norm, gamma=gamma,
+                                    stream=stream),
+            lambda: sq.sq_smooth_fold(s, gamma, gp, stream=stream),
+            lambda: sq.sq_quant_weight(w, s, wq, wsc, stream=stream),
+            lambda: sq.sq_quant_act(x, gp, xq, xs, norm=wl.norm, row_rscale=rr, stream=stream),
+            lambda: sq.sq_gemm_w8a8(xq, xs, wq, wsc, y, bias=bias, stream=stream),
+        ]
+
+    for i in range(warmup):
+        for c in calls(i):
             c()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        for _, c in calls:
+        for c in calls(warmup + i):
             c()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    # per-call breakdown in a pass of its own: timing events idle the stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-           for _ in range(steps)]
+    hip = HipTimer()
+    evs = [[hip.event() for _ in range(len(names) + 1)] for _ in range(steps)]
     for i in range(steps):
-        evs[i][0].record(stream)
-        for j, (_, c) in enumerate(calls):
+        hip.record(evs[i][0], stream)
+        for j, c in enumerate(calls(warmup + steps + i)):
             c()
-            evs[i][j + 1].record(stream)
+            hip.record(evs[i][j + 1], stream)
     torch.cuda.synchronize()
-    per = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps * 1e3
-           for j, (n, _) in enumerate(calls)}
+    per = {n: sum(hip.ms(evs[i][j], evs[i][j + 1]) for i in range(steps)) / steps * 1e3
+           for j, n in enumerate(names)}
+    hip.destroy([e for row in evs for e in row])
     ops = 2.0 * T * K * N
-    return {"workload": f"{name}: T={T} K={K} N={N} calib_tokens={wl.Tc} norm={wl.norm}",
-            "ms_per_step": ms, "step_tops": ops / (ms * 1e-3) / 1e12,
-            "linear_us": per["linear"], "linear_tops": ops / (per["linear"] * 1e-6) / 1e12,
-            "calls_us": per}
+    lin = per["quant_act"] + per["gemm"]
+
+    def hbm(byts, us):
+        ach = byts / (us * 1e-6) / 1e9
+        return {"bound": "hbm", "us": us, "achieved": ach, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS, "algorithmic_bytes": byts}
+
+    g_ach = ops / (per["gemm"] * 1e-6) / 1e12
+    roof = {
+        "gemm": {"bound": "mfma", "us": per["gemm"], "achieved": g_ach, "unit": "TOP/s",
+                 "peak": PEAK_INT8_TOPS, "frac": g_ach / PEAK_INT8_TOPS,
+                 "algorithmic": f"2*T*K*N = {ops:.4g} int8 ops"},
+        "calibrate": hbm(2.0 * Tc * K + 2.0 * K * N + 12.0 * K, per["calibrate"]),
+        "quant_weight": hbm(3.0 * K * N + 4.0 * (N + K), per["quant_weight"]),
+        "quant_act": hbm(3.0 * T * K + 4.0 * (T + K), per["quant_act"]),
+    }
+    return {"workload": f"{name}: T={T} K={K} N={N} calib_tokens={Tc} norm={wl.norm}",
+            "input_sets": nsets, "ms_per_step": ms, "step_tops": ops / (ms * 1e-3) / 1e12,
+            "linear_us": lin, "linear_tops": ops / (lin * 1e-6) / 1e12, "calls_us": per,
+            "roofline": roof}
 
 
 def gptq_timing(sq, torch, inp, wl, d, dev, iters=2):
@@ -728,6 +801,14 @@ def main():
         return
     if args.only == "decoder_layer":
         print(json.dumps(block_timing(sq, torch, dev)), flush=True)
+        return
+    if args.only == "configs":
+        print(json.dumps({n: config_step(sq, torch, dev, n) for n in ("rmsnorm_qkv", "gate_up")}),
+              flush=True)
+        return
+    if args.only == "decode":
+        print(json.dumps({"decode_gemm": decode_gemm(sq, torch, dev),
+                          "decode_calibration": decode_calibration(sq, torch, dev)}), flush=True)
         return
     nsets = max(1, args.sets)
     sets = [(d(inp.x_cal), d(inp.x), d(inp.w)) for _ in range(nsets)]
@@ -854,6 +935,7 @@ def main():
         out["decode_gemm"] = decode_gemm(sq, torch, dev)
         out["fp8"] = fp8_timing(sq, torch, sets, wl, s, gp, bias, dev)
         out["vendor_int8_gemm"] = vendor_int8_gemm(torch, xq, wq)
+        out["hbm_ceilings"] = hbm_ceilings(torch, dev)
         out["decoder_layer"] = block_timing(sq, torch, dev)
         out["decode_calibration"] = decode_calibration(sq, torch, dev)
         out["configs"] = {n: config_step(sq, torch, dev, n) for n in ("rmsnorm_qkv", "gate_up")}

@@ -147,10 +147,10 @@ sq_status sq_quant_act(const void *x, sq_dtype x_dt, int64_t t, int64_t k, int64
                        int8_t *xq, float *x_scale, float *row_rscale, hipStream_t stream);
 
 /*
- * (d) INT8 GEMM with int32 accumulation and the fused dequantization epilogue
- * ("06 -- SmoothQuant" section 7: INT8 x INT8 -> INT32, then
- * Y = scale_x * scale_w * Y_int32; "Taming the Outliers", step I6, add bias
- * and dequantize):
+ * (d) INT8 GEMM with exact int32 sums and the fused dequantization epilogue:
+ * the integer product is scaled by the token's step times the output
+ * channel's step, then the bias is added ("06 -- SmoothQuant" section 7;
+ * "Taming the Outliers", System Architecture step I6):
  *   acc[t, n] = sum_k xq[t, k] * wq[n, k]            (exact int32)
  *   y[t, n]   = fp32( fp32(x_scale[t] * w_scale[n]) * fp32(acc[t, n]) ) + bias[n]
  *               rounded to y_dt (bf16: nearest-even)

@@ -161,37 +161,61 @@ constexpr int quant_act_min_waves() {
   return In::kBytes * NV <= 16 ? (QF == 1 ? 6 : 8) : 1;   // FP8: 8 quotients live per chunk
 }
 
+// (x is not __restrict__: that would let the compiler move the token loads
+// past the barrier that the gamma_f staging needs, serializing them again)
 template <class In, int NV, bool NORM, bool STATIC, int QF>
 __global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV, QF>())) void k_quant_act(
-    const typename In::elem* __restrict__ x, int64_t T, int64_t K, int64_t ld,
+    const typename In::elem* x, int64_t T, int64_t K, int64_t ld,
     const float* __restrict__ gamma_f, float eps, const float* __restrict__ static_scale,
     int8_t* __restrict__ xq, float* __restrict__ xscale, float* __restrict__ rrow) {
   // gamma_f of chunk c: elements 0-3 at gs[c], 4-7 at gs[NV * 64 + c] (1
   // without gamma, 0 past K)
-  __shared__ f32x4 gs[NV * 64 * 2];
+  __shared__ __attribute__((aligned(1024))) f32x4 gs[NV * 64 * 2];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nchunk = (int)(K >> 3);   // <= 64 * NV
-  for (int i = threadIdx.x; i < NV * 64 * 2; i += 64 * kWavesPerBlock) {
-    const int ch = i % (NV * 64), half = i / (NV * 64);
-    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (ch < nchunk) {
-      if (gamma_f) v = *reinterpret_cast<const f32x4*>(gamma_f + ch * 8 + half * 4);
-      else v = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+  // gamma_f goes to LDS by direct-to-LDS loads (no VGPRs), issued before
+  // this wave's token loads; the wait below covers only those gamma loads
+  // (loads complete in order), so the token's loads are in flight during the
+  // staging and the barrier: the two memory latencies overlap instead of
+  // adding up, which is what sets the time at a few thousand tokens.
+  // Positions past K read as 0 (outside the buffer resource).
+  if (gamma_f != nullptr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t gr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)gamma_f, 0, (int)(K * 4), 0x00020000);
+    for (int base = wave * 64; base < NV * 64 * 2; base += 64 * kWavesPerBlock) {
+      const int i = base + lane;
+      const int ch = i % (NV * 64), half = i / (NV * 64);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          gr, (__attribute__((address_space(3))) void*)&gs[base], 16, (ch * 8 + half * 4) * 4, 0,
+          0, 0);
     }
-    gs[i] = v;
+#endif
+  } else {
+    for (int i = threadIdx.x; i < NV * 64 * 2; i += 64 * kWavesPerBlock) {
+      const float one = (i % (NV * 64)) < nchunk ? 1.0f : 0.0f;
+      gs[i] = f32x4{one, one, one, one};
+    }
   }
-  __syncthreads();
-  const uint32_t gaddr = lds_addr(&gs[lane]);
   const int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-  if (r >= T) return;
-  const typename In::elem* row = x + r * ld;
+  const bool live = r < T;
+  const typename In::elem* row = x + (live ? r : T - 1) * ld;
   typename In::Raw raw[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int ch = j * 64 + lane;
     raw[j] = In::raw8_nt(row + (ch < nchunk ? ch : 0) * 8);   // read once
   }
+  // keep the token's loads here, ahead of the barrier (the scheduler would
+  // otherwise sink them below it); they (NV for bf16, 2 NV for fp32) may
+  // still fly
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(NV * In::kBytes / 2) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  const uint32_t gaddr = lds_addr(&gs[lane]);
+  if (!live) return;
   float rt = 1.0f;
   if (NORM) {
     double ss = 0.0;

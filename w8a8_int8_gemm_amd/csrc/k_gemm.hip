@@ -1,9 +1,10 @@
-// k_gemm.hip -- INT8 x INT8 -> INT32 GEMM on the gfx950 matrix cores with the
-// fused dequantization epilogue ("06 -- SmoothQuant", section 7: the matmul is
-// a straight INT8 x INT8 -> INT32 product followed by
-// Y = scale_x * scale_w * Y_int32; "Taming the Outliers", step I6: add bias
-// and dequantize), and the same kernel for FP8 E4M3 operands with fp32
-// accumulation ("SmoothQuant and W8A8", One layer, measured: FP8 E4M3).
+// k_gemm.hip -- the integer GEMM of the smoothed linear on the gfx950 matrix
+// cores: 8-bit activation codes times 8-bit weight codes summed exactly in
+// 32-bit integers, then scaled back to real values by the token's step times
+// the output channel's step, with the bias added ("06 -- SmoothQuant",
+// section 7; "Taming the Outliers", System Architecture step I6); and the same
+// kernel for FP8 E4M3 codes with fp32 sums ("SmoothQuant and W8A8", One layer,
+// measured).
 //
 //   acc[t, n] = sum_k xq[t, k] * wq[n, k]     (xq [T, K], wq [N, K], K contiguous)
 //   y[t, n]   = fp32(fp32(xs[t] * ws[n]) * fp32(acc)) + bias[n]  -> bf16 / fp32
