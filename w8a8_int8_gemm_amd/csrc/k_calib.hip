@@ -198,14 +198,15 @@ __global__ __launch_bounds__(256) void k_rms_act_absmax(const typename In::elem*
 }
 
 // ---------------------------------------------------------------------------
-// LayerNorm-mode calibration absmax.  Same row-per-wave layout.  Per row: the
-// fp64 mean, the fp64 sum of squared deviations from it, m_t = fp32(mean) and
-// r_t = fp32(1/sqrt(var + eps)); then per column the running maximum and
-// minimum of n = fp32(fp32(h - m_t) * r_t).  f(n) = fp32(fp32(n * gamma_j) +
-// beta_j) is monotone in n (fp32 multiply and add round monotonically), so
-// max_t |f(n_t)| = max(|f(max_t n)|, |f(min_t n)|): gamma and beta are applied
-// once per column at the end, exactly.  Maxima and minima are combined across
-// waves in LDS through an order-preserving map of the float bits.
+// LayerNorm-mode calibration absmax, K <= 4096.  Same row-per-wave layout.
+// Per row: the fp64 mean, the fp64 sum of squared deviations from it,
+// m_t = fp32(mean) and r_t = fp32(1/sqrt(var + eps)); then every element's
+// norm output x = fp32(fp32(fp32(h - m_t) * r_t) * gamma_j) + beta_j, exactly
+// as the norm forms it, and the running maximum of |x| per column -- one
+// value per column in registers (tracking the maximum and minimum of the
+// normalized value and applying gamma and beta at the end needs two, and
+// twice the registers).  gamma and beta are staged once per workgroup in LDS
+// and read there chunk by chunk.  Wider rows take k_ln_act_absmax_wide.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ unsigned int ordered_bits(float f) {
   const unsigned int u = __float_as_uint(f);
@@ -215,45 +216,46 @@ __device__ __forceinline__ float from_ordered_bits(unsigned int o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-template <class In, int NV, int SPLIT>
+template <class In, int NV>
 __global__ __launch_bounds__(256) void k_ln_act_absmax(const typename In::elem* __restrict__ h,
                                                        int64_t rows, int64_t K, int64_t ld,
                                                        const float* __restrict__ gamma,
                                                        const float* __restrict__ beta, float eps,
                                                        float* __restrict__ out) {
-  // SPLIT waves share a row: each takes the whole row for the statistics and
-  // keeps the running maximum and minimum of its own NV / SPLIT chunks.
-  constexpr int NM = NV / SPLIT;
-  constexpr int RPB = 4 / SPLIT;           // rows per workgroup pass
-  extern __shared__ unsigned int lmm[];   // [K] maxima, then [K] minima (ordered bits)
-  unsigned int* lmax = lmm;
-  unsigned int* lmin = lmm + K;
+  // gamma and beta of chunk c: elements 0-3 at [c], 4-7 at [NV * 64 + c]
+  __shared__ f32x4 gsm[NV * 64 * 2];
+  __shared__ f32x4 bsm[NV * 64 * 2];
+  __shared__ unsigned int lmax[NV * 512];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int slice = wave % SPLIT;
-  const int64_t nchunk = K >> 3;
-  for (int64_t c = threadIdx.x; c < K; c += 256) {
-    lmax[c] = 0u;            // below every ordered value
-    lmin[c] = 0xffffffffu;   // above every ordered value
-  }
-  float mx[NM][8], mn[NM][8];
-#pragma unroll
-  for (int j = 0; j < NM; ++j)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      mx[j][i] = -INFINITY;
-      mn[j][i] = INFINITY;
+  const int nchunk = (int)(K >> 3);
+  for (int i = threadIdx.x; i < NV * 64 * 2; i += 256) {
+    const int ch = i % (NV * 64), half = i / (NV * 64);
+    f32x4 g = {0.0f, 0.0f, 0.0f, 0.0f}, bt = g;
+    if (ch < nchunk) {
+      g = gamma ? *reinterpret_cast<const f32x4*>(gamma + ch * 8 + half * 4)
+                : f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+      if (beta) bt = *reinterpret_cast<const f32x4*>(beta + ch * 8 + half * 4);
     }
+    gsm[i] = g;
+    bsm[i] = bt;
+  }
+  for (int c = threadIdx.x; c < NV * 512; c += 256) lmax[c] = 0u;
+  __syncthreads();
+  const uint32_t gaddr = lds_addr(&gsm[lane]);
+  const uint32_t baddr = lds_addr(&bsm[lane]);
+  float mx[NV][8];
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mx[j][i] = 0.0f;
   const double dK = (double)K;
-  bool any = false;
-  for (int64_t r = (int64_t)blockIdx.x * RPB + wave / SPLIT; r < rows;
-       r += (int64_t)gridDim.x * RPB) {
-    any = true;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < rows; r += (int64_t)gridDim.x * 4) {
     typename In::Raw raw[NV];
     const typename In::elem* row = h + r * ld;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int64_t ch = (int64_t)j * 64 + lane;
+      const int ch = j * 64 + lane;
       raw[j] = In::raw8_nt(row + (ch < nchunk ? ch : 0) * 8);   // read once
     }
     double s1 = 0.0;
@@ -261,17 +263,21 @@ __global__ __launch_bounds__(256) void k_ln_act_absmax(const typename In::elem* 
     for (int j = 0; j < NV; ++j) {
       float v[8];
       In::widen(raw[j], v);
-      if ((int64_t)j * 64 + lane < nchunk)
+      if (j * 64 + lane < nchunk)
 #pragma unroll
         for (int i = 0; i < 8; ++i) s1 += (double)v[i];
     }
     const double mu = wave_sum(s1) / dK;
+    // keep only the raw values alive between the passes (each pass widens
+    // them again): otherwise the compiler keeps every value's fp64 form
+#pragma unroll
+    for (int j = 0; j < NV; ++j) In::opaque(raw[j]);
     double s2 = 0.0;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       float v[8];
       In::widen(raw[j], v);
-      if ((int64_t)j * 64 + lane < nchunk)
+      if (j * 64 + lane < nchunk)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const double d = (double)v[i] - mu;
@@ -282,39 +288,38 @@ __global__ __launch_bounds__(256) void k_ln_act_absmax(const typename In::elem* 
     const float mt = (float)mu;
     const float rt = (float)(1.0 / sqrt(s2 / dK + (double)eps));
 #pragma unroll
-    for (int jj = 0; jj < NM; ++jj) {
+    for (int j = 0; j < NV; ++j) In::opaque(raw[j]);
+    static_for<NV>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
       float v[8];
-      In::widen(raw[slice * NM + jj], v);
+      In::widen(raw[j], v);
+      // gamma and beta of this chunk from LDS, the wait in the same asm block
+      // (the compiler cannot then hoist every chunk's values into VGPRs)
+      f32x4 g0, g1, b0, b1;
+      asm volatile(
+          "ds_read_b128 %0, %4 offset:%6\n\tds_read_b128 %1, %4 offset:%7\n\t"
+          "ds_read_b128 %2, %5 offset:%6\n\tds_read_b128 %3, %5 offset:%7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=v"(g0), "=v"(g1), "=v"(b0), "=v"(b1)
+          : "v"(gaddr), "v"(baddr), "n"(j * 1024), "n"(NV * 1024 + j * 1024)
+          : "memory");
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float n = (v[i] - mt) * rt;
-        mx[jj][i] = fmaxf(mx[jj][i], n);
-        mn[jj][i] = fminf(mn[jj][i], n);
+        const float x = n * (i < 4 ? g0[i] : g1[i - 4]) + (i < 4 ? b0[i] : b1[i - 4]);
+        mx[j][i] = fmaxf(mx[j][i], fabsf(x));
       }
-    }
+    });
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int ch = j * 64 + lane;
+    if (ch < nchunk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) atomicMax(&lmax[ch * 8 + i], __float_as_uint(mx[j][i]));
   }
   __syncthreads();
-  if (any) {
-#pragma unroll
-    for (int jj = 0; jj < NM; ++jj) {
-      const int64_t ch = (int64_t)(slice * NM + jj) * 64 + lane;
-      if (ch < nchunk)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          atomicMax(&lmax[ch * 8 + i], ordered_bits(mx[jj][i]));
-          atomicMin(&lmin[ch * 8 + i], ordered_bits(mn[jj][i]));
-        }
-    }
-  }
-  __syncthreads();
-  for (int64_t c = threadIdx.x; c < K; c += 256) {
-    if (lmax[c] == 0u) continue;   // this workgroup saw no row
-    const float g = gamma ? gamma[c] : 1.0f;
-    const float b = beta ? beta[c] : 0.0f;
-    const float hi = from_ordered_bits(lmax[c]) * g + b;
-    const float lo = from_ordered_bits(lmin[c]) * g + b;
-    atomic_max_nonneg(out + c, fmaxf(fabsf(hi), fabsf(lo)));
-  }
+  for (int c = threadIdx.x; c < K; c += 256) atomic_max_nonneg(out + c, __uint_as_float(lmax[c]));
 }
 
 // ---------------------------------------------------------------------------
@@ -611,32 +616,29 @@ void launch_rms_act_absmax(const void* h, bool bf16, int64_t rows, int64_t K, in
 template <class In, int NV>
 static void ln_absmax_nv(const void* h, int64_t rows, int64_t K, int64_t ld, const float* gamma,
                          const float* beta, float eps, float* out, hipStream_t st) {
-  // a lane holds the row's raw chunks plus 16 floats of maxima and minima per
-  // chunk it tracks: wider rows share the tracking among 2 or 4 waves
-  constexpr int SPLIT = NV >= 16 ? 4 : (NV >= 8 && In::kBytes == 4) ? 2 : 1;
-  int64_t blocks = (rows + 4 / SPLIT - 1) / (4 / SPLIT);
+  int64_t blocks = (rows + 3) / 4;
   if (blocks > 512) blocks = 512;
-  hipLaunchKernelGGL((k_ln_act_absmax<In, NV, SPLIT>), dim3((unsigned)blocks), dim3(256),
-                     (size_t)K * 2 * sizeof(unsigned int), st, (const typename In::elem*)h, rows,
-                     K, ld, gamma, beta, eps, out);
+  hipLaunchKernelGGL((k_ln_act_absmax<In, NV>), dim3((unsigned)blocks), dim3(256), 0, st,
+                     (const typename In::elem*)h, rows, K, ld, gamma, beta, eps, out);
 }
 
 template <class In>
 static void ln_absmax_t(const void* h, int64_t rows, int64_t K, int64_t ld, const float* gamma,
                         const float* beta, float eps, float* out, hipStream_t st) {
-  const int64_t nv = (K + 511) / 512;
+  const int64_t nv = (K + 511) / 512;   // K <= 4096 here
   if (nv <= 1) ln_absmax_nv<In, 1>(h, rows, K, ld, gamma, beta, eps, out, st);
   else if (nv <= 2) ln_absmax_nv<In, 2>(h, rows, K, ld, gamma, beta, eps, out, st);
   else if (nv <= 4) ln_absmax_nv<In, 4>(h, rows, K, ld, gamma, beta, eps, out, st);
-  else if (nv <= 8) ln_absmax_nv<In, 8>(h, rows, K, ld, gamma, beta, eps, out, st);
-  else ln_absmax_nv<In, 16>(h, rows, K, ld, gamma, beta, eps, out, st);
+  else ln_absmax_nv<In, 8>(h, rows, K, ld, gamma, beta, eps, out, st);
 }
 
 void launch_ln_act_absmax(const void* h, bool bf16, int64_t rows, int64_t K, int64_t ld,
                           const float* gamma, const float* beta, float eps, float* out,
                           hipStream_t st) {
   if (rows <= 0 || K <= 0) return;
-  if (K > 8192) {
+  // above 4096 columns the per-column maxima in LDS beat those in registers
+  // (16384 x 8192 bf16: 136 against 327 us)
+  if (K > 4096) {
     const dim3 g = wide_grid(rows, K, kWideCSLn);
     if (bf16)
       hipLaunchKernelGGL(k_ln_act_absmax_wide<Bf16In>, g, dim3(512), 0, st, (const uint16_t*)h,
