@@ -71,7 +71,8 @@ def _parse():
                     help="instead of benchmarking, run only the headline GEMM back to back for "
                          "this long (for sampling power and clocks from outside) and print the "
                          "time per launch")
-    ap.add_argument("--only", choices=("gptq", "decoder_layer", "configs", "decode"),
+    ap.add_argument("--only", choices=("gptq", "decoder_layer", "configs", "rmsnorm_qkv",
+                                       "gate_up", "decode"),
                     default=None,
                     help="instead of benchmarking, run only this extra and print its JSON "
                          "(for profiling one part on its own)")
@@ -802,9 +803,9 @@ def main():
     if args.only == "decoder_layer":
         print(json.dumps(block_timing(sq, torch, dev)), flush=True)
         return
-    if args.only == "configs":
-        print(json.dumps({n: config_step(sq, torch, dev, n) for n in ("rmsnorm_qkv", "gate_up")}),
-              flush=True)
+    if args.only in ("configs", "rmsnorm_qkv", "gate_up"):
+        names = ("rmsnorm_qkv", "gate_up") if args.only == "configs" else (args.only,)
+        print(json.dumps({n: config_step(sq, torch, dev, n) for n in names}), flush=True)
         return
     if args.only == "decode":
         print(json.dumps({"decode_gemm": decode_gemm(sq, torch, dev),
