@@ -1,9 +1,10 @@
 """The decode GEMM (T <= 64), bit for bit against the oracle: int32
-accumulators and the bf16 / fp32 epilogue.  Both workgroup widths of the
-16-token kernel (16 channels with 8 k-steps in flight; 32 channels with 4,
-used above 8 tokens when N / 32 workgroups cover the GPU), K from one k-step
-to 8192 with unrolled batches and their remainders, N ragged against the
-channel blocks, 1 to 16 tokens, and one shape of each wider token block."""
+accumulators and the bf16 / fp32 epilogue.  Every kernel shape the launcher
+picks on a 256-CU part: 16-channel workgroups of 8 waves (up to 4 tokens, or
+K > 4096 with fewer than 256 * 32 channels) and 32-channel workgroups of 4
+waves, with 1, 2, 3 and 4 token blocks; per-wave stage counts from 0 (waves
+past the last k-step) through the two-stage loop and each of its 1-, 2- and
+3-stage tails; N ragged against the channel blocks."""
 import numpy as np
 import pytest
 
@@ -17,10 +18,11 @@ import oracle  # noqa: E402
 import w8a8_int8_gemm_amd as sq  # noqa: E402
 from _gpu_util import DEV, say, to_dev, to_np  # noqa: E402
 
-# (T, N, K); 32-channel workgroups for T > 8 with N >= 32 * 256
-ACC_SHAPES = [(1, 8, 64), (5, 77, 1088), (16, 520, 704), (16, 4096, 8192), (3, 264, 3072),
-              (16, 136, 4160), (7, 1000, 2048), (16, 16, 5120), (16, 8192, 1088),
-              (9, 8200, 2048), (40, 77, 1088), (64, 300, 576)]
+# (T, N, K)
+ACC_SHAPES = [(1, 8, 64), (4, 300, 14336), (3, 264, 3072), (5, 77, 1088), (16, 520, 704),
+              (16, 4096, 8192), (16, 8192, 4160), (16, 136, 4160), (7, 1000, 2048),
+              (16, 16, 5120), (16, 8192, 1088), (9, 8200, 2048), (20, 33, 14336),
+              (32, 1000, 4160), (40, 77, 1088), (48, 40, 64), (64, 300, 576), (64, 64, 8192)]
 
 
 def _ops(T, N, K, seed):
