@@ -52,14 +52,26 @@ __global__ __launch_bounds__(256) void k_col_absmax(const typename In::elem* __r
   const int64_t step = (int64_t)gridDim.y * 4;
   int64_t r = (int64_t)blockIdx.y * 4 + wave;
   if (nv > 0 && nv < 8) {
-    // the ragged end of the rows: the missing columns read as 0
+    // the ragged end of the rows: the missing columns read as 0; U rows in
+    // flight, rows past the end re-read row r and count with scale 0
     const typename In::elem* base = m + c0;
-    for (; r < rows; r += step) {
-      float v[8];
-      In::widen(In::raw8_part(base + r * ld, (int)nv), v);
-      const float sc = kRowScale ? rs[r] : 1.0f;
+    for (; r < rows; r += U * step) {
+      typename In::Raw raw[U];
+      float sc[U];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(kRowScale ? v[i] * sc : v[i]));
+      for (int u = 0; u < U; ++u) {
+        const bool in = r + u * step < rows;
+        const int64_t rr = in ? r + u * step : r;
+        raw[u] = In::raw8_part(base + rr * ld, (int)nv);
+        sc[u] = in ? (kRowScale ? rs[rr] : 1.0f) : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float v[8];
+        In::widen(raw[u], v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(v[i] * sc[u]));
+      }
     }
   } else if (nv > 0) {
     const typename In::elem* base = m + c0;
@@ -83,12 +95,25 @@ __global__ __launch_bounds__(256) void k_col_absmax(const typename In::elem* __r
         for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(kRowScale ? v[i] * sc[u] : v[i]));
       }
     }
-    for (; r < rows; r += step) {
-      float v[8];
-      In::load8(base + r * ld, v);
-      const float sc = kRowScale ? rs[r] : 1.0f;
+    if (r < rows) {
+      // the last, partial batch: every remaining row's load in flight at once;
+      // rows past the end re-read row r and count with scale 0
+      typename In::Raw raw[U];
+      float sc[U];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(kRowScale ? v[i] * sc : v[i]));
+      for (int u = 0; u < U; ++u) {
+        const bool in = r + u * step < rows;
+        const int64_t rr = in ? r + u * step : r;
+        raw[u] = kRowScale ? In::raw8(base + rr * ld) : In::raw8_nt(base + rr * ld);
+        sc[u] = in ? (kRowScale ? rs[rr] : 1.0f) : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float v[8];
+        In::widen(raw[u], v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(v[i] * sc[u]));
+      }
     }
   }
 #pragma unroll
@@ -535,9 +560,17 @@ void launch_fill_f32(float* p, int64_t n, float v, hipStream_t st) {
   hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)blocks), dim3(256), 0, st, p, n, v);
 }
 
+// One workgroup (4 waves, 8 rows in flight per wave) per compute unit at most,
+// so every unit streams the same number of rows to within one workgroup, and
+// at least 8 rows per wave.  Measured on bf16 inputs rotated past the
+// Infinity Cache (us, this rule / about 2048 workgroups of 8 rows per wave):
+// 8192 x 4096 14.7 / 17.2; 65536 x 4096 83.1 / 94.8; 262144 x 8192 619 / 729
+// (6.9 TB/s); 4096 x 28672 38.1 / 45.2.  Two workgroups per unit, or 16 rows
+// in flight per wave, were slower at every shape but 4096 x 14336: the
+// memory system serves fewer, longer streams better than the whole matrix
+// requested at once.
 static int col_absmax_grid_y(int64_t rows, int64_t gx) {
-  // about 2048 workgroups in all, but at least 8 rows per wave
-  int64_t gy = (2048 + gx - 1) / gx;
+  int64_t gy = (int64_t)cu_count() / gx;
   const int64_t max_gy = (rows + 31) / 32;
   if (gy > max_gy) gy = max_gy;
   if (gy < 1) gy = 1;
