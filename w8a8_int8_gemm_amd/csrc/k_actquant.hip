@@ -394,12 +394,16 @@ __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem*
 //   m_t = fp32(mean), r_t = fp32(1/sqrt(var + eps)) (fp64 sums, the variance
 //   about the fp64 mean), x^ = fp32(fp32(fp32(h - m_t) * r_t) * gamma'_k) +
 //   beta'_k, then the per-token INT8 quantizer above.
-// K <= 8192 (bf16: K <= 16384): one token per wave, the row's raw values in
+// K <= 8192: one token per wave, the row's raw values in
 // VGPRs from the load to the store; gamma' and beta' come through the caches
 // (every token reads the same K floats).
 // ---------------------------------------------------------------------------
-template <class In, int NV>
-__global__ __launch_bounds__(64 * kWavesPerBlock) void k_quant_act_ln(
+// WPB waves (tokens) per workgroup: 8, or 4 for rows of more than 4096
+// elements, whose raw values and the gamma' / beta' chunks in flight need
+// more than the 256 registers a wave has at two waves per SIMD (with 4 it
+// may use 512, so nothing goes to private memory).
+template <class In, int NV, int WPB>
+__global__ __launch_bounds__(64 * WPB) void k_quant_act_ln(
     const typename In::elem* __restrict__ x, int64_t T, int64_t K, int64_t ld,
     const float* __restrict__ gamma_f, const float* __restrict__ beta_f, float eps,
     int8_t* __restrict__ xq, float* __restrict__ xscale, float* __restrict__ mrow,
@@ -407,7 +411,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_quant_act_ln(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nchunk = (int)(K >> 3);
-  const int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  const int64_t r = (int64_t)blockIdx.x * WPB + wave;
   if (r >= T) return;
   const typename In::elem* row = x + r * ld;
   typename In::Raw raw[NV];
@@ -656,8 +660,9 @@ template <class In, int NV>
 static void quant_act_ln_nv(const void* x, int64_t T, int64_t K, int64_t ld, const float* g,
                             const float* b, float eps, int8_t* xq, float* xscale, float* mrow,
                             float* rrow, hipStream_t st) {
-  const int64_t blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL((k_quant_act_ln<In, NV>), dim3((unsigned)blocks), dim3(64 * kWavesPerBlock),
+  constexpr int WPB = NV >= 16 ? 4 : kWavesPerBlock;
+  const int64_t blocks = (T + WPB - 1) / WPB;
+  hipLaunchKernelGGL((k_quant_act_ln<In, NV, WPB>), dim3((unsigned)blocks), dim3(64 * WPB),
                      0, st, (const typename In::elem*)x, T, K, ld, g, b, eps, xq, xscale, mrow,
                      rrow);
 }
@@ -673,10 +678,7 @@ static void quant_act_ln_t(const void* x, int64_t T, int64_t K, int64_t ld, cons
   else if (nchunk <= 512) quant_act_ln_nv<In, 8>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
   else if (nchunk <= 1024)
     quant_act_ln_nv<In, 16>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
-  else if (In::kBytes == 2 && nchunk <= 2048) {
-    if constexpr (In::kBytes == 2)   // bf16 rows up to 16384 in VGPRs
-      quant_act_ln_nv<In, 32>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
-  } else
+  else   // wider rows would not fit the registers of one wave (no private memory)
     hipLaunchKernelGGL((k_quant_act_ln_wide<In>), dim3((unsigned)T), dim3(256), 0, st,
                        (const typename In::elem*)x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow);
 }

@@ -18,11 +18,13 @@
 //  * Workgroup tile BT tokens x BN channels; WGT x WGN waves, each a
 //    (BT/WGT) x (BN/WGN) grid of 32 x 32 MFMA tiles.  The large-T tile is
 //    256 x 256 with 8 waves of 128 x 64 (2 waves per SIMD).
-//  * K is staged through LDS 64 bytes at a time in 4 buffers, loads issued 3-4
-//    stages ahead with buffer_load_dwordx4 ... lds (HBM/L2 -> LDS without
-//    VGPRs).  A 1 KiB load instruction fills 16 rows of 64 bytes; the 16-byte
-//    chunk c of row r is stored at chunk position c ^ swz(r), so the rows an
-//    MFMA operand read touches spread over all 64 LDS banks.
+//  * K is staged through LDS 128 bytes at a time in 2 buffers, the next
+//    stage's loads in flight while one is multiplied, with buffer_load_dwordx4
+//    ... lds (HBM/L2 -> LDS without VGPRs).  A 1 KiB load instruction fills 8
+//    rows of 128 bytes; the 16-byte chunk c of row r is stored at chunk
+//    position c ^ swz(r), so the rows an MFMA operand read touches spread over
+//    all 64 LDS banks.  For K % 128 == 64, INT8 stages 64 bytes in 4 buffers
+//    and FP8 ends on a half stage.
 //  * Operand reads of the next k-step are interleaved one-for-one with the
 //    MFMAs; one workgroup barrier per stage.
 //  * Tiles are ordered so that the workgroups that share an XCD (the
@@ -79,11 +81,11 @@ enum { OUT_BF16 = 0, OUT_F32 = 1, OUT_I32 = 2 };
 #if defined(__HIP_DEVICE_COMPILE__)
 template <int L, int NW>
 __device__ __forceinline__ void issue_rows(__amdgpu_buffer_rsrc_t r, int8_t* dst, const int (&off)[L],
-                                           int wave, int k0) {
+                                           int wave, int k0, int pad) {
 #pragma unroll
   for (int bb = 0; bb < L; ++bb)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (bb * NW + wave) * 1024), 16,
-                                             off[bb], k0, 0, 0);
+                                             off[bb] + pad, k0, 0, 0);
 }
 #endif
 
@@ -93,7 +95,7 @@ __device__ __forceinline__ void issue_rows(__amdgpu_buffer_rsrc_t r, int8_t* dst
 // consecutive k (MFMA order, which keeps 16-byte K runs together here), each
 // aligned to the group's largest product with the bits below 2^-13 of it
 // dropped, then adds the group sums in fp32.
-template <int BT, int BN, int WGT, int WGN, int BK, int NS, int OUT, bool F8>
+template <int BT, int BN, int WGT, int WGN, int BK, int NS, int OUT, bool F8, bool HALF>
 __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __restrict__ xq,
                                                    const float* __restrict__ xs, int T, int K,
                                                    const int8_t* __restrict__ wq,
@@ -156,10 +158,18 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
     const int row = (bb * NW + wave) * RPL + lrow;
     woff[bb] = row * K + ((lchunk ^ swz<BK>(row)) << 4);
   }
+  // The byte offset in the stage of this lane's chunk is the same for every
+  // load (NW even: the swizzle of rows (b * NW + wave) * RPL + lrow does not
+  // depend on b); in a stage that ends past K it sends the chunks past K
+  // outside the resources.
+  static_assert(NW % 2 == 0, "one chunk offset per lane for all its loads");
+  const int cbyte = (lchunk ^ swz<BK>(wave * RPL + lrow)) << 4;
+  constexpr int kOutside = 1 << 30;
   auto issue = [&](int stage) {   // K stage `stage` -> LDS buffer stage % NS
     const int buf = stage & (NS - 1);
-    issue_rows<XL, NW>(xr, xs_l + buf * XS, xoff, wave, stage * BK);
-    issue_rows<WL, NW>(wr, ws_l + buf * WS, woff, wave, stage * BK);
+    const int pad = (HALF && cbyte >= K - stage * BK) ? kOutside : 0;
+    issue_rows<XL, NW>(xr, xs_l + buf * XS, xoff, wave, stage * BK, pad);
+    issue_rows<WL, NW>(wr, ws_l + buf * WS, woff, wave, stage * BK, pad);
   };
 
   // the tile's scales and bias, staged once in their own LDS region (read
@@ -235,7 +245,10 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
   // barrier makes them everyone's) and for its reads of stage s to finish, so
   // after the barrier buffer s % NS is free: the loads of stage s+NS go there,
   // and k-step 0 of stage s+1 is read while the last k-step of s multiplies.
-  const int nst = K / BK;
+  // HALF: K % BK == BK / 2, the last stage holds half a stage of K, and its
+  // loads of the chunks past K go outside the resources (zeros, no memory
+  // access), so its last k-steps multiply zeros.  Otherwise K % BK == 0.
+  const int nst = (K + BK - 1) / BK;
   static_for<NS>([&](auto s_) {
     constexpr int sv = decltype(s_)::value;
     if (sv < nst) issue(sv);
@@ -446,7 +459,7 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
 // host launcher
 // ---------------------------------------------------------------------------
 
-template <int BT, int BN, int WGT, int WGN, int BK, int NS, bool F8>
+template <int BT, int BN, int WGT, int WGN, int BK, int NS, bool F8, bool HALF>
 static void gemm_tile(const int8_t* xq, const float* xs, int T, int K, const int8_t* wq,
                       const float* ws, int N, const float* bias, void* y, int ldy, int out,
                       hipStream_t st) {
@@ -454,28 +467,36 @@ static void gemm_tile(const int8_t* xq, const float* xs, int T, int K, const int
   const dim3 grid((unsigned)ntiles), block(64 * WGT * WGN);
   const int group_t = 4;
   if (out == OUT_BF16)
-    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, BK, NS, OUT_BF16, F8>), grid, block, 0, st,
+    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, BK, NS, OUT_BF16, F8, HALF>), grid, block, 0, st,
                        xq, xs, T, K, wq, ws, N, bias, y, ldy, group_t);
   else if (out == OUT_F32)
-    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, BK, NS, OUT_F32, F8>), grid, block, 0, st,
+    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, BK, NS, OUT_F32, F8, HALF>), grid, block, 0, st,
                        xq, xs, T, K, wq, ws, N, bias, y, ldy, group_t);
   else
-    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, BK, NS, OUT_I32, F8>), grid, block, 0, st,
+    hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, BK, NS, OUT_I32, F8, HALF>), grid, block, 0, st,
                        xq, xs, T, K, wq, ws, N, bias, y, ldy, group_t);
 }
 
-// K % 128 == 0 stages 128 bytes of K per row in two buffers: every load then
-// covers whole 128-byte lines, which streams the panels into LDS about 1.5x
-// faster than 64-byte half lines in four buffers.  Other K stage 64 bytes in
-// four buffers.
+// 128 bytes of K per row are staged in two buffers: every load then covers
+// whole 128-byte lines, which streams the panels into LDS about 1.5x faster
+// than 64-byte half lines in four buffers.  For K % 128 == 64 the INT8 kernel
+// stages 64 bytes in four buffers, and the FP8 kernel (whose 64-byte pipeline
+// needs more registers than two waves per SIMD have, and spilled to private
+// memory) ends on a half stage.
 template <int BT, int BN, int WGT, int WGN, bool F8>
 static void gemm_tile_k(const int8_t* xq, const float* xs, int T, int K, const int8_t* wq,
                         const float* ws, int N, const float* bias, void* y, int ldy, int out,
                         hipStream_t st) {
-  if (K % 128 == 0)
-    gemm_tile<BT, BN, WGT, WGN, 128, 2, F8>(xq, xs, T, K, wq, ws, N, bias, y, ldy, out, st);
-  else
-    gemm_tile<BT, BN, WGT, WGN, 64, 4, F8>(xq, xs, T, K, wq, ws, N, bias, y, ldy, out, st);
+  if (K % 128 == 0) {
+    gemm_tile<BT, BN, WGT, WGN, 128, 2, F8, false>(xq, xs, T, K, wq, ws, N, bias, y, ldy, out, st);
+  } else {
+    if constexpr (F8)
+      gemm_tile<BT, BN, WGT, WGN, 128, 2, true, true>(xq, xs, T, K, wq, ws, N, bias, y, ldy, out,
+                                                     st);
+    else
+      gemm_tile<BT, BN, WGT, WGN, 64, 4, false, false>(xq, xs, T, K, wq, ws, N, bias, y, ldy, out,
+                                                      st);
+  }
 }
 
 // compute units of the current device (looked up once per device; threads

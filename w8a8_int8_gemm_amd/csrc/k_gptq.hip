@@ -273,6 +273,12 @@ constexpr UChunks make_uchunks() {
   return L;
 }
 constexpr UChunks kUChunks = make_uchunks();
+// index in kUChunks of row jj's first chunk
+constexpr int first_uchunk(int jj) {
+  int n = 0;
+  for (int r = 0; r < jj; ++r) n += NB / 8 - (r + 1) / 8;
+  return n;
+}
 constexpr int kRing = 4;   // chunks in flight (4 LDS reads each; lgkmcnt counts to 15)
 
 // An empty asm that takes v[0 .. 7] as read-write VGPR operands, with a
@@ -309,38 +315,39 @@ __global__ __launch_bounds__(64) void k_chol_panel(double* __restrict__ A, int64
   double ring[kRing][8];
   double piv = readlane_f64(r[0], 0);
   double y = rsqrt_nr(piv);
-#pragma unroll
-  for (int c = 0; c < NB; ++c) {
+  // every index below is a compile-time constant (static_for), so r, x and
+  // the ring stay in VGPRs: no private (scratch) memory
+  static_for<NB>([&](auto c_) {
+    constexpr int c = decltype(c_)::value;
     const double lc = (i == c) ? piv * y : r[c] * y;
     r[c] = lc;
     LT[c][i] = lc;
     if (i == c) Rd[c] = y;
     __builtin_amdgcn_wave_barrier();
-    if (c + 1 < NB) {
+    if constexpr (c + 1 < NB) {
       // the next pivot first; the rest of the column's updates run meanwhile,
       // their LT reads kRing chunks ahead within the row
       r[c + 1] = fma(-lc, readlane_f64(lc, c + 1), r[c + 1]);
       piv = readlane_f64(r[c + 1], c + 1);
       y = rsqrt_nr(piv);
-      const int g0 = (c + 2) / 8, ng = c + 2 < NB ? NB / 8 - g0 : 0;
-      auto fetch = [&](int u) {
+      constexpr int g0 = (c + 2) / 8, ng = c + 2 < NB ? NB / 8 - g0 : 0;
+      auto fetch = [&](auto u_) {
+        constexpr int u = decltype(u_)::value;
 #pragma unroll
         for (int t = 0; t < 8; ++t) ring[u % kRing][t] = LT[c][8 * (g0 + u) + t];
       };
-#pragma unroll
-      for (int u = 0; u < kRing; ++u)
-        if (u < ng) fetch(u);
-#pragma unroll
-      for (int u = 0; u < ng; ++u) {
-        const int g = g0 + u;
+      static_for<(kRing < ng ? kRing : ng)>(fetch);
+      static_for<ng>([&](auto u_) {
+        constexpr int u = decltype(u_)::value;
+        constexpr int g = g0 + u;
 #pragma unroll
         for (int t = 0; t < 8; ++t)
           if (8 * g + t >= c + 2) r[8 * g + t] = fma(-lc, ring[u % kRing][t], r[8 * g + t]);
-        if (u + kRing < ng) fetch(u + kRing);
+        if constexpr (u + kRing < ng) fetch(std::integral_constant<int, u + kRing>());
         pin8(r + 8 * g);   // this chunk's products here, the next reads after
-      }
+      });
     }
-  }
+  });
 #pragma unroll
   for (int j = 0; j < NB; ++j) A[(o + i) * K + o + j] = (j <= i) ? r[j] : 0.0;
   __builtin_amdgcn_wave_barrier();
@@ -349,26 +356,27 @@ __global__ __launch_bounds__(64) void k_chol_panel(double* __restrict__ A, int64
   double x[NB];
 #pragma unroll
   for (int a = 0; a < NB; ++a) x[a] = (a == i) ? 1.0 : 0.0;
-  auto fetch = [&](int ci) {
+  auto fetch = [&](auto ci_) {
+    constexpr int ci = decltype(ci_)::value;
     const double* src = &LT[kUChunks.row[ci]][8 * kUChunks.grp[ci]];
 #pragma unroll
     for (int t = 0; t < 8; ++t) ring[ci % kRing][t] = src[t];
   };
-#pragma unroll
-  for (int ci = 0; ci < kRing; ++ci) fetch(ci);
-  int ci = 0;
-#pragma unroll
-  for (int k = 0; k + 1 < NB; ++k) {
+  static_for<kRing>(fetch);
+  static_for<NB - 1>([&](auto k_) {
+    constexpr int k = decltype(k_)::value;
     x[k] = x[k] * Rd[k];
-#pragma unroll
-    for (int g = (k + 1) / 8; g < NB / 8; ++g, ++ci) {
+    constexpr int g0 = (k + 1) / 8, ci0 = first_uchunk(k);
+    static_for<NB / 8 - g0>([&](auto u_) {
+      constexpr int u = decltype(u_)::value;
+      constexpr int g = g0 + u, ci = ci0 + u;
 #pragma unroll
       for (int t = 0; t < 8; ++t)
         if (8 * g + t > k) x[8 * g + t] = fma(-ring[ci % kRing][t], x[k], x[8 * g + t]);
-      if (ci + kRing < kUChunks.n) fetch(ci + kRing);
+      if constexpr (ci + kRing < kUChunks.n) fetch(std::integral_constant<int, ci + kRing>());
       pin8(x + 8 * g);
-    }
-  }
+    });
+  });
   x[NB - 1] = x[NB - 1] * Rd[NB - 1];
 #pragma unroll
   for (int a = 0; a < NB; ++a) Dinv[(o + a) * NB + i] = x[a];
@@ -520,9 +528,15 @@ __global__ __launch_bounds__(256) void k_gptq_init(const typename In::elem* __re
   float v[8];
   In::widen(raw8_upto<In>(w + j * ld + n0, N - n0), v);
   const float sj = s ? s[j] : 1.0f;
+  double* dst = W64 + j * N + n0;
+  if (n0 + 8 <= N) {   // whole chunks: eight adjacent stores the compiler merges
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (n0 + e < N) W64[j * N + n0 + e] = dead[j] ? 0.0 : (double)(v[e] * sj);
+    for (int e = 0; e < 8; ++e) dst[e] = dead[j] ? 0.0 : (double)(v[e] * sj);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (n0 + e < N) dst[e] = dead[j] ? 0.0 : (double)(v[e] * sj);
+  }
 }
 
 // Block b (rows r0 = b*64 .. +63) of the rounding for the 64 output channels
@@ -579,42 +593,44 @@ __global__ __launch_bounds__(64) void k_gptq_block(const double* __restrict__ W6
   Ur[c] = 1.0 / Ub[c][c];
   __syncthreads();
   double ring[kRing][8];
-  auto fetch = [&](int ci) {
+  auto fetch = [&](auto ci_) {
+    constexpr int ci = decltype(ci_)::value;
     const double* src = &Ub[kUChunks.row[ci]][8 * kUChunks.grp[ci]];
 #pragma unroll
     for (int t = 0; t < 8; ++t) ring[ci % kRing][t] = src[t];
   };
-#pragma unroll
-  for (int ci = 0; ci < kRing; ++ci) fetch(ci);
+  static_for<kRing>(fetch);
   uint32_t packed[NB / 4];
 #pragma unroll
   for (int i = 0; i < NB / 4; ++i) packed[i] = 0;
   double q = gptq_code(w[0], d, rd);
   double e = (w[0] - d * q) * Ur[0];
-  int ci = 0;
-#pragma unroll
-  for (int jj = 0; jj < NB; ++jj) {
+  // compile-time indices throughout (static_for): w, packed and the ring
+  // stay in VGPRs, no private (scratch) memory
+  static_for<NB>([&](auto jj_) {
+    constexpr int jj = decltype(jj_)::value;
     packed[jj >> 2] |= ((uint32_t)(int)q & 0xffu) << (8 * (jj & 3));
     E[(int64_t)jj * ldE + n] = e;
-    if (jj + 1 < NB) {
+    if constexpr (jj + 1 < NB) {
       double qn = 0.0, en = 0.0;
-#pragma unroll
-      for (int g = (jj + 1) / 8; g < NB / 8; ++g, ++ci) {
-        const int s = ci % kRing;
+      constexpr int g0 = (jj + 1) / 8, ci0 = first_uchunk(jj);
+      static_for<NB / 8 - g0>([&](auto u_) {
+        constexpr int u = decltype(u_)::value;
+        constexpr int g = g0 + u, ci = ci0 + u;
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-          if (8 * g + t > jj) w[8 * g + t] = fma(-ring[s][t], e, w[8 * g + t]);
-        if (g == (jj + 1) / 8) {
+          if (8 * g + t > jj) w[8 * g + t] = fma(-ring[ci % kRing][t], e, w[8 * g + t]);
+        if constexpr (u == 0) {
           qn = gptq_code(w[jj + 1], d, rd);
           en = (w[jj + 1] - d * qn) * Ur[jj + 1];
         }
-        if (ci + kRing < kUChunks.n) fetch(ci + kRing);
+        if constexpr (ci + kRing < kUChunks.n) fetch(std::integral_constant<int, ci + kRing>());
         pin8(w + 8 * g);   // this chunk's products here, the next reads after
-      }
+      });
       q = qn;
       e = en;
     }
-  }
+  });
   if (live) {
     // codes: output channel n, input channels r0 .. r0+63
     uint4* dst = reinterpret_cast<uint4*>(wq + n * K + r0);
