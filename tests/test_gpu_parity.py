@@ -249,8 +249,10 @@ def test_quant_act_ties_and_fallback():
 GEMM_SHAPES = [(300, 520, 704), (256, 256, 4096), (513, 1000, 128), (1, 520, 704), (16, 520, 704),
                (17, 264, 640), (33, 96, 192), (64, 1024, 1024), (65, 8, 64), (1000, 40, 64),
                (384, 2056, 512),
-               # 128 x 256 tiles (ragged T), then 256 x 256 tiles (ragged T and N)
-               (1500, 4096, 256), (1800, 6104, 128),
+               # 128 x 256 tiles (ragged T), then 128 x 384 tiles (one round of
+               # them fills the GPU where 256 x 256 tiles would not): ragged T
+               # and N, 64- and 128-byte stages, and whole tiles
+               (1500, 4096, 256), (1800, 6104, 128), (1500, 6000, 192), (1536, 6144, 128),
                # ragged N on the tile kernels: 128 x 128 tiles with 64- and
                # 128-byte stages, 128 x 256 and 256 x 256 tiles
                (300, 77, 704), (257, 1003, 128), (129, 4, 64), (2100, 3001, 256),
@@ -286,7 +288,7 @@ def test_gemm_extreme_accumulators(T, N, K):
 @pytest.mark.parametrize("with_bias", [False, True])
 @pytest.mark.parametrize("T,N,K", [(300, 520, 704), (16, 264, 512), (40, 77, 128), (512, 512, 256),
                                    (300, 77, 768), (257, 1003, 128), (129, 4, 64),
-                                   (2100, 3001, 256)])
+                                   (2100, 3001, 256), (1500, 6000, 192)])
 def test_gemm_epilogue(T, N, K, out, with_bias):
     rng = np.random.default_rng(T * N + K)
     q = rng.integers(-127, 128, (T, K), dtype=np.int8)

@@ -374,9 +374,14 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
     constexpr int CPR = WTN / 8;          // 16-byte chunks per staged row
     constexpr int RPI = 64 / CPR;         // rows per store instruction
     const int rr = lane / CPR, cc = lane % CPR;
+    // (RPI * CPR < 64 when CPR does not divide 64, as for 96-channel wave
+    // tiles: the lanes past that, and the rows past the wave's tile in the
+    // last pass, store nothing)
+    const bool lane_on = lane < RPI * CPR;
 #pragma unroll 4
     for (int r0 = 0; r0 < WTT; r0 += RPI) {
       const int tw = r0 + rr;
+      if (!lane_on || tw >= WTT) continue;
       const u32x4 v = *reinterpret_cast<const u32x4*>(ep + tw * EPS + cc * 16);
       const int t = t0 + wt * WTT + tw;
       const int n = n0 + wn * WTN + cc * 8;
@@ -522,11 +527,17 @@ static void gemm_sizes(const int8_t* xq, const float* xs, int64_t T, int64_t K, 
   // 256 x 256 tiles (8 waves) have the most reuse and win whenever they keep
   // at least 3/4 of the compute units busy; below that 128 x 256 tiles (8
   // waves), then 128 x 128 (4 waves), trade reuse for occupancy (measured on
-  // the 2048-token q|k|v, o, down and gate|up shapes).
+  // the 2048-token q|k|v, o, down and gate|up shapes).  Where 256 x 256 tiles
+  // do not fill one round but 128 x 384 tiles (8 waves of 64 x 96) fill more
+  // of it, the latter win: 2048 x 6144 x 4096 54 us against 62, 1536 x 6144 x
+  // 4096 46 against 62, 2048 x 6144 x 14336 155 against 173.
   const int64_t busy = 3 * (int64_t)cu_count() / 4;
   const int64_t t256 = ((T + 255) / 256) * ((N + 255) / 256);
   const int64_t t128x256 = ((T + 127) / 128) * ((N + 255) / 256);
-  if (t256 >= busy)
+  const int64_t t128x384 = ((T + 127) / 128) * ((N + 383) / 384);
+  if (t256 < cu_count() && t128x384 >= busy && t128x384 <= cu_count() && t128x384 > t256)
+    gemm_tile_k<128, 384, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+  else if (t256 >= busy)
     gemm_tile_k<256, 256, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
   else if (t128x256 >= busy)
     gemm_tile_k<128, 256, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
