@@ -186,15 +186,23 @@ __global__ __launch_bounds__(256) void k_quant_weight_t(const typename In::elem*
       packed[i] = lo | hi;
     }
     if (slow || !(dm <= kTieBand)) {
+      // rare: the division for only the values near a tie (every value when
+      // a reciprocal overflowed); a wave runs a value's division only if one
+      // of its lanes needs it
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        packed[i] = 0u;
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float q = d[i] != 0.0f ? rintf(wh[r][i] / d[i]) : 0.0f;
-          packed[i] |= code_byte(fminf(fmaxf(q, -127.0f), 127.0f)) << (8 * r);
+          // y recomputed (rc made opaque, so the fast pass keeps no y alive)
+          float rci = rc[i];
+          asm volatile("" : "+v"(rci));
+          const float y = wh[r][i] * rci;   // rint(y) = tq - 1.5 * 2^23 of the fast pass
+          if (slow || !(fabsf(y - rintf(y)) <= kTieBand)) {
+            const float q = d[i] != 0.0f ? rintf(wh[r][i] / d[i]) : 0.0f;
+            packed[i] = (packed[i] & ~(0xffu << (8 * r))) |
+                        (code_byte(fminf(fmaxf(q, -127.0f), 127.0f)) << (8 * r));
+          }
         }
-      }
     }
   }
 #pragma unroll
@@ -369,15 +377,23 @@ __global__ __launch_bounds__(NT) void k_quant_weight_strip(const uint16_t* __res
           pk[i] = lo | hi;
         }
         if (slow || !(dm <= kTieBand)) {
+          // rare: redo by IEEE division only the values near a tie (or every
+          // value when 1/Delta overflowed); a wave runs a value's division
+          // only if one of its lanes needs it
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            pk[i] = 0u;
+          for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float q = d[i] != 0.0f ? rintf(wh[m][r][i] / d[i]) : 0.0f;
-              pk[i] |= code_byte(fminf(fmaxf(q, -127.0f), 127.0f)) << (8 * r);
+              // y recomputed (rc made opaque, so the fast pass keeps no y alive)
+              float rci = rc[i];
+              asm volatile("" : "+v"(rci));
+              const float y = wh[m][r][i] * rci;   // rint(y) = tq - 1.5 * 2^23 of the fast pass
+              if (slow || !(fabsf(y - rintf(y)) <= kTieBand)) {
+                const float q = d[i] != 0.0f ? rintf(wh[m][r][i] / d[i]) : 0.0f;
+                pk[i] = (pk[i] & ~(0xffu << (8 * r))) |
+                        (code_byte(fminf(fmaxf(q, -127.0f), 127.0f)) << (8 * r));
+              }
             }
-          }
         }
       }
       const int col = (int)(g - TW * p);
