@@ -1,0 +1,37 @@
+"""Host-side checks of bench.py (CPU only): the one-GPU rule, the CPU
+baseline's record, and that the committed GEMM byte counters belong to the
+GEMM source in the tree (bench.py reports roofline.traffic only then)."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
+
+
+def test_cpu_baseline_record_on_the_tiny_workload():
+    wl = synth.WORKLOADS["tiny"]
+    inp = synth.make_inputs(wl)
+    r = bench.cpu_baseline(inp, wl, 0.2)
+    assert r["kind"] == "oracle" and r["unit"] == "TOPS"
+    assert r["value"] > 0 and r["cores"] >= 1 and r["passes"] >= 1
+    assert r["seconds"] > 0 and "pass" in r["sample"]
+
+
+def test_committed_gemm_counters_match_the_gemm_source():
+    with open(bench.COUNTERS) as f:
+        rec = json.load(f)
+    assert rec["kernel_source_sha256_16"] == bench._kernel_hash(), (
+        "k_gemm.hip changed since the FETCH_SIZE / WRITE_SIZE passes: retake them")
+    assert rec["hbm_bytes_per_launch"] > 112 * 2**20   # at least the algorithmic bytes
