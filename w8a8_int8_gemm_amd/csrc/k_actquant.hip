@@ -239,14 +239,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV, Q
   }
   // x^ of chunk j, the same fp32 operations in both passes.  gamma is read
   // from LDS chunk by chunk, with the wait in the same asm block: the
-  // compiler cannot then hoist every chunk's gamma into VGPRs at once.
+  // compiler cannot then hoist every chunk's gamma into VGPRs at once.  The
+  // outputs are early-clobber: the first read's data may land before the
+  // second read has taken its address, so no output may share the address
+  // register.
   auto smooth = [&](auto jc, float (&xh)[8]) {
     constexpr int j = decltype(jc)::value;
     float v[8];
     In::widen(raw[j], v);
     f32x4 g0, g1;
     asm volatile("ds_read_b128 %0, %2 offset:%3\n\tds_read_b128 %1, %2 offset:%4\n\ts_waitcnt lgkmcnt(0)"
-                 : "=v"(g0), "=v"(g1)
+                 : "=&v"(g0), "=&v"(g1)
                  : "v"(gaddr), "n"(j * 1024), "n"(NV * 1024 + j * 1024)
                  : "memory");
 #pragma unroll
@@ -394,16 +397,12 @@ __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem*
 //   m_t = fp32(mean), r_t = fp32(1/sqrt(var + eps)) (fp64 sums, the variance
 //   about the fp64 mean), x^ = fp32(fp32(fp32(h - m_t) * r_t) * gamma'_k) +
 //   beta'_k, then the per-token INT8 quantizer above.
-// K <= 8192: one token per wave, the row's raw values in
+// K <= 4096: one token per wave, the row's raw values in
 // VGPRs from the load to the store; gamma' and beta' come through the caches
 // (every token reads the same K floats).
 // ---------------------------------------------------------------------------
-// WPB waves (tokens) per workgroup: 8, or 4 for rows of more than 4096
-// elements, whose raw values and the gamma' / beta' chunks in flight need
-// more than the 256 registers a wave has at two waves per SIMD (with 4 it
-// may use 512, so nothing goes to private memory).
-template <class In, int NV, int WPB>
-__global__ __launch_bounds__(64 * WPB) void k_quant_act_ln(
+template <class In, int NV>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void k_quant_act_ln(
     const typename In::elem* __restrict__ x, int64_t T, int64_t K, int64_t ld,
     const float* __restrict__ gamma_f, const float* __restrict__ beta_f, float eps,
     int8_t* __restrict__ xq, float* __restrict__ xscale, float* __restrict__ mrow,
@@ -411,7 +410,7 @@ __global__ __launch_bounds__(64 * WPB) void k_quant_act_ln(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nchunk = (int)(K >> 3);
-  const int64_t r = (int64_t)blockIdx.x * WPB + wave;
+  const int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + wave;
   if (r >= T) return;
   const typename In::elem* row = x + r * ld;
   typename In::Raw raw[NV];
@@ -495,9 +494,8 @@ __global__ __launch_bounds__(64 * WPB) void k_quant_act_ln(
   }
 }
 
-// K > 16384 (K > 8192 for fp32 input): one workgroup per token, four passes
-// over the row (sum, squared deviations, maximum, quantize); the re-reads hit
-// L2.
+// K > 4096: one workgroup per token, four passes over the row (sum, squared
+// deviations, maximum, quantize); the re-reads hit L2.
 template <class In>
 __global__ __launch_bounds__(256) void k_quant_act_ln_wide(
     const typename In::elem* __restrict__ x, int64_t T, int64_t K, int64_t ld,
@@ -660,9 +658,8 @@ template <class In, int NV>
 static void quant_act_ln_nv(const void* x, int64_t T, int64_t K, int64_t ld, const float* g,
                             const float* b, float eps, int8_t* xq, float* xscale, float* mrow,
                             float* rrow, hipStream_t st) {
-  constexpr int WPB = NV >= 16 ? 4 : kWavesPerBlock;
-  const int64_t blocks = (T + WPB - 1) / WPB;
-  hipLaunchKernelGGL((k_quant_act_ln<In, NV, WPB>), dim3((unsigned)blocks), dim3(64 * WPB),
+  const int64_t blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL((k_quant_act_ln<In, NV>), dim3((unsigned)blocks), dim3(64 * kWavesPerBlock),
                      0, st, (const typename In::elem*)x, T, K, ld, g, b, eps, xq, xscale, mrow,
                      rrow);
 }
@@ -676,9 +673,9 @@ static void quant_act_ln_t(const void* x, int64_t T, int64_t K, int64_t ld, cons
   else if (nchunk <= 128) quant_act_ln_nv<In, 2>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
   else if (nchunk <= 256) quant_act_ln_nv<In, 4>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
   else if (nchunk <= 512) quant_act_ln_nv<In, 8>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
-  else if (nchunk <= 1024)
-    quant_act_ln_nv<In, 16>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
-  else   // wider rows would not fit the registers of one wave (no private memory)
+  else   // wider rows: the workgroup-per-token kernel (faster above 4096 elements
+         // than one wave per token with its row in registers: 2048 tokens x
+         // 6144 19.9 against 27.4 us, x 8192 24.5 against 33.8 us)
     hipLaunchKernelGGL((k_quant_act_ln_wide<In>), dim3((unsigned)T), dim3(256), 0, st,
                        (const typename In::elem*)x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow);
 }

@@ -319,13 +319,15 @@ __global__ __launch_bounds__(256) void k_ln_act_absmax(const typename In::elem* 
       float v[8];
       In::widen(raw[j], v);
       // gamma and beta of this chunk from LDS, the wait in the same asm block
-      // (the compiler cannot then hoist every chunk's values into VGPRs)
+      // (the compiler cannot then hoist every chunk's values into VGPRs);
+      // early-clobber outputs, so that no read's data can land in a register
+      // that a later read still takes its address from
       f32x4 g0, g1, b0, b1;
       asm volatile(
           "ds_read_b128 %0, %4 offset:%6\n\tds_read_b128 %1, %4 offset:%7\n\t"
           "ds_read_b128 %2, %5 offset:%6\n\tds_read_b128 %3, %5 offset:%7\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=v"(g0), "=v"(g1), "=v"(b0), "=v"(b1)
+          : "=&v"(g0), "=&v"(g1), "=&v"(b0), "=&v"(b1)
           : "v"(gaddr), "v"(baddr), "n"(j * 1024), "n"(NV * 1024 + j * 1024)
           : "memory");
 #pragma unroll
