@@ -31,8 +31,13 @@
 //    hardware deals workgroup ids round-robin over the 8 XCDs) take one
 //    contiguous range of tiles, grouped GROUP_T token panels at a time: they
 //    share activation and weight panels in their XCD's L2.
-//  * The bf16 epilogue stages each wave's tile in LDS and writes whole
-//    128-byte row segments.
+//  * Persistent: at most one workgroup per compute unit (two for the 4-wave
+//    tile), each walking the tiles blockIdx.x, blockIdx.x + gridDim.x, ....
+//    After a tile's K loop the next tile's first stages and scales are loaded
+//    into the free operand buffers while this tile's epilogue runs, so the
+//    next tile's load latency and the workgroup turnover are off the path.
+//  * The bf16 epilogue stages each 32 x 32 sub-tile in the wave's own LDS
+//    area (outside the operand buffers) and writes 64-byte row segments.
 #include "sq_common.h"
 #include "sq_internal.h"
 
@@ -121,18 +126,20 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
   constexpr int XL = BT / (RPL * NW), WL = BN / (RPL * NW);  // 1 KiB loads per wave per stage
   constexpr int LPS = XL + WL;              // loads per wave per stage
   constexpr int OPB = NS * (XS + WS);       // operand stages
-  constexpr int EPS = WTN * 2 + 16;         // epilogue: bytes per staged output row
-  constexpr int EPB = NW * WTT * EPS;       // epilogue: the waves' bf16 tiles
-  constexpr int SCO = OPB > EPB ? OPB : EPB;  // scales live after both
-  __shared__ __attribute__((aligned(1024))) int8_t smem[SCO + (BT + 2 * BN) * 4];
+  constexpr int NSC = BT + 2 * BN;          // one tile's token scales, channel scales, biases
+  constexpr int SCO = OPB;                  // two sets of them (this tile's, the next one's)
+  constexpr int ES = 32 * 2 + 16;           // epilogue: bytes per staged row of 32 bf16
+  constexpr int EPW = 32 * ES;              // epilogue: one wave's 32 x 32 sub-tile
+  constexpr int EPO = SCO + 2 * NSC * 4;
+  constexpr int LDSB = EPO + (OUT == OUT_BF16 ? NW * EPW : 0);
+  static_assert(LDSB <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[LDSB];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wt = wave % WGT, wn = wave / WGT;
   const int nt_t = (T + BT - 1) / BT, nt_n = (N + BN - 1) / BN;
-  int pid_t, pid_n;
-  tile_of(blockIdx.x, nt_t, nt_n, group_t, pid_t, pid_n);
-  const int t0 = pid_t * BT, n0 = pid_n * BN;
+  const int ntiles = nt_t * nt_n;
 
   int8_t* xs_l = smem;              // [NS][BT][BK]
   int8_t* ws_l = smem + NS * XS;    // [NS][BN][BK]
@@ -142,10 +149,20 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
   // Lane l of a 1 KiB load fills row RPL*b + l/CPR, chunk position l%CPR,
   // which holds the row's 16-byte K chunk (l%CPR) ^ swz(row); k0 goes in the
   // scalar offset.  With BK = 128 every load covers whole 128-byte lines.
-  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(xq + (int64_t)t0 * K), 0, min(BT, T - t0) * K, 0x00020000);
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(wq + (int64_t)n0 * K), 0, min(BN, N - n0) * K, 0x00020000);
+  // The workgroup walks the tiles blockIdx.x, blockIdx.x + gridDim.x, ...
+  int t0 = 0, n0 = 0;
+  __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)xq, 0, 0, 0x00020000);
+  __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void*)wq, 0, 0, 0x00020000);
+  auto set_tile = [&](int tile) {
+    int pid_t, pid_n;
+    tile_of(tile, nt_t, nt_n, group_t, pid_t, pid_n);
+    t0 = pid_t * BT;
+    n0 = pid_n * BN;
+    xr = __builtin_amdgcn_make_buffer_rsrc((void*)(xq + (int64_t)t0 * K), 0, min(BT, T - t0) * K,
+                                           0x00020000);
+    wr = __builtin_amdgcn_make_buffer_rsrc((void*)(wq + (int64_t)n0 * K), 0, min(BN, N - n0) * K,
+                                           0x00020000);
+  };
   const int lrow = lane / CPR, lchunk = lane % CPR;
   int xoff[XL], woff[WL];
 #pragma unroll
@@ -171,29 +188,48 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
     issue_rows<XL, NW>(xr, xs_l + buf * XS, xoff, wave, stage * BK, pad);
     issue_rows<WL, NW>(wr, ws_l + buf * WS, woff, wave, stage * BK, pad);
   };
+  const int nst = (K + BK - 1) / BK;
+  auto issue_first = [&]() {
+    static_for<NS>([&](auto s_) {
+      constexpr int sv = decltype(s_)::value;
+      if (sv < nst) issue(sv);
+    });
+  };
 
-  // the tile's scales and bias, staged once in their own LDS region (read
-  // after the K loop, whose barriers make them visible)
-  float* s_xs = reinterpret_cast<float*>(smem + SCO);   // [BT]
-  float* s_ws = s_xs + BT;                               // [BN]
-  float* s_b = s_ws + BN;                                // [BN]
+  // The tile's token scales, channel scales and biases: loaded into registers
+  // (before the tile's operand loads, so that waiting for them waits for
+  // nothing else), then written to LDS set p, where the epilogue reads them.
+  constexpr int SPT = (NSC + NTH - 1) / NTH;
   const bool has_bias = bias != nullptr;
-  if (OUT != OUT_I32) {
-    for (int i = threadIdx.x; i < BT; i += NTH) s_xs[i] = (t0 + i < T) ? xs[t0 + i] : 0.0f;
-    for (int i = threadIdx.x; i < BN; i += NTH) {
-      s_ws[i] = (n0 + i < N) ? ws[n0 + i] : 0.0f;
-      s_b[i] = (has_bias && n0 + i < N) ? bias[n0 + i] : 0.0f;
+  float nsc[SPT];
+  auto load_scales = [&]() {
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int i = threadIdx.x + u * NTH;
+      float v = 0.0f;
+      if (OUT != OUT_I32 && i < NSC) {
+        if (i < BT) {
+          if (t0 + i < T) v = xs[t0 + i];
+        } else if (i < BT + BN) {
+          if (n0 + i - BT < N) v = ws[n0 + i - BT];
+        } else if (has_bias && n0 + i - BT - BN < N) {
+          v = bias[n0 + i - BT - BN];
+        }
+      }
+      nsc[u] = v;
     }
-  }
+  };
+  auto store_scales = [&](int p) {
+    float* sc = reinterpret_cast<float*>(smem + SCO) + p * NSC;
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int i = threadIdx.x + u * NTH;
+      if (i < NSC) sc[i] = nsc[u];
+    }
+  };
 
   typedef typename std::conditional<F8, v16f, v16i>::type AccT;
   AccT acc[NTN][NTT];
-#pragma unroll
-  for (int i = 0; i < NTN; ++i)
-#pragma unroll
-    for (int j = 0; j < NTT; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
   // --- MFMA operands of k-step kk of a stage.  INT8: the 16-byte chunk
   // 2kk + h of the row (h = lane / 32), the K layout of
@@ -239,6 +275,33 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
       }
   };
 
+  int tile = blockIdx.x;
+  set_tile(tile);
+  load_scales();
+  issue_first();
+  store_scales(0);
+  // stage 0 landed: at most min(nst-1, NS-1) later stages still in flight
+  {
+    const int fly0 = min(nst - 1, NS - 1);
+    static_for<NS>([&](auto f_) {
+      constexpr int f = decltype(f_)::value;
+      if (fly0 == f) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(f * LPS) : "memory");
+    });
+  }
+  for (int r = 0;; ++r) {
+  if (r > 0) {
+    // the stages of this tile and the scales were loaded during the previous
+    // tile's epilogue, whose stores are in the same count: wait for all
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    store_scales(r & 1);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NTN; ++i)
+#pragma unroll
+    for (int j = 0; j < NTT; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
   // --- pipeline.  Stage s lives in LDS buffer s % NS.  In iteration s the
   // operands of k-step kk+1 are read while k-step kk multiplies; before the
   // last k-step every wave waits for stage s+1 to land (its own loads; the
@@ -248,20 +311,6 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
   // HALF: K % BK == BK / 2, the last stage holds half a stage of K, and its
   // loads of the chunks past K go outside the resources (zeros, no memory
   // access), so its last k-steps multiply zeros.  Otherwise K % BK == 0.
-  const int nst = (K + BK - 1) / BK;
-  static_for<NS>([&](auto s_) {
-    constexpr int sv = decltype(s_)::value;
-    if (sv < nst) issue(sv);
-  });
-  // stage 0 landed: at most min(nst-1, NS-1) later stages still in flight
-  {
-    const int fly0 = min(nst - 1, NS - 1);
-    static_for<NS>([&](auto f_) {
-      constexpr int f = decltype(f_)::value;
-      if (fly0 == f) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(f * LPS) : "memory");
-    });
-  }
-  __syncthreads();
   OpT fa[2][NTN], fb[2][NTT];
   frags(0, 0, fa[0], fb[0]);
   // one stage; FLY = stages still in flight after stage s+1 has landed
@@ -334,84 +383,115 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
     if (st == nst - 2 - f) step(st++, std::integral_constant<int, f>(), BF_());
   });
   step(st, IN(), BF_());
+  // every wave is done with the operand stages: the next tile's go there while
+  // this tile's epilogue runs
   __syncthreads();
+  const int ct0 = t0, cn0 = n0;
+  const int next = tile + (int)gridDim.x;
+  const bool more = next < ntiles;
+  if (more) {
+    set_tile(next);
+    load_scales();
+    issue_first();
+  }
+  const float* s_xs = reinterpret_cast<const float*>(smem + SCO) + (r & 1) * NSC;   // [BT]
+  const float* s_ws = s_xs + BT;                                                   // [BN]
+  const float* s_b = s_ws + BN;                                                    // [BN]
 
   // --- epilogue.  Lane l of tile (i, j): token t = .. + l%32; channels
   // n = .. + 8g + 4(l/32) + e for g, e in 0..3 hold acc[i][j][4g + e].
   // y = fp32(fp32(xs[t] * ws[n]) * fp32(acc)) + bias[n].
-  const bool full_tile = (t0 + BT <= T) && (n0 + BN <= N);
-  if (OUT == OUT_BF16) {
-    // Stage the wave's WTT x WTN bf16 tile in LDS (rows of 2*WTN bytes, padded
-    // to EPS), then write it out 16 bytes per lane along the row: each store
-    // covers whole rows of the wave's tile instead of 32 rows x 16 bytes.
-    int8_t* ep = smem + wave * WTT * EPS;
+  const bool full_tile = (ct0 + BT <= T) && (cn0 + BN <= N);
+  if constexpr (OUT == OUT_BF16) {
+    // Each 32 x 32 sub-tile is staged in the wave's own LDS area (rows of 64
+    // bytes, padded to ES) and written out 16 bytes per lane along the rows:
+    // each store covers 16 rows x 64 bytes instead of 32 rows x 16 bytes.  The
+    // lane's token scales and channel scales are read from LDS once; each
+    // channel scale serves the NTT token tiles.
+    int8_t* ep = smem + EPO + wave * EPW;
+    float xst[NTT];
 #pragma unroll
-    for (int j = 0; j < NTT; ++j) {
-      const int tw = j * 32 + frow;                  // row in the wave's tile
-      const float xst = s_xs[wt * WTT + tw];
+    for (int j = 0; j < NTT; ++j) xst[j] = s_xs[wt * WTT + j * 32 + frow];
+    const int rr = lane >> 2, cc = lane & 3;   // read-back: rows rr, rr + 16; chunk cc
+    auto stage = [&](auto bias_tag) {
+      constexpr bool B = decltype(bias_tag)::value;
 #pragma unroll
       for (int i = 0; i < NTN; ++i) {
+        f32x4 w4[4], b4[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int nw = i * 32 + g * 8 + fhalf * 4;   // column in the wave's tile
-          const f32x4 w4 = *reinterpret_cast<const f32x4*>(s_ws + wn * WTN + nw);
-          const f32x4 b4 = *reinterpret_cast<const f32x4*>(s_b + wn * WTN + nw);
-          float o[4];
+          w4[g] = *reinterpret_cast<const f32x4*>(s_ws + wn * WTN + i * 32 + g * 8 + fhalf * 4);
+          b4[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          if constexpr (B)
+            b4[g] = *reinterpret_cast<const f32x4*>(s_b + wn * WTN + i * 32 + g * 8 + fhalf * 4);
+        }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float sc = xst * w4[e];
-            const float v = sc * (float)acc[i][j][4 * g + e];
-            o[e] = has_bias ? v + b4[e] : v;
+        for (int j = 0; j < NTT; ++j) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float sc = xst[j] * w4[g][e];
+              const float v = sc * (float)acc[i][j][4 * g + e];
+              o[e] = B ? v + b4[g][e] : v;
+            }
+            u32x2 pk;
+            pk[0] = pack_bf16x2(o[0], o[1]);
+            pk[1] = pack_bf16x2(o[2], o[3]);
+            *reinterpret_cast<u32x2*>(ep + frow * ES + g * 16 + fhalf * 8) = pk;
           }
-          u32x2 pk;
-          pk[0] = pack_bf16x2(o[0], o[1]);
-          pk[1] = pack_bf16x2(o[2], o[3]);
-          *reinterpret_cast<u32x2*>(ep + tw * EPS + nw * 2) = pk;
+          // (no wait: a wave's LDS operations run in order, so these reads see
+          // the writes above; the wave reads only its own area)
+          u32x4 v[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            v[h] = *reinterpret_cast<const u32x4*>(ep + (h * 16 + rr) * ES + cc * 16);
+          const int tb = ct0 + wt * WTT + j * 32 + rr;
+          const int n = cn0 + wn * WTN + i * 32 + cc * 8;
+          uint16_t* dst = reinterpret_cast<uint16_t*>(yout) + (int64_t)tb * ldy + n;
+          if (full_tile) {
+            // non-temporal: the output is not read again here, and it then
+            // leaves no dirty lines in the caches to be written back under
+            // the next kernels' streams
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              __builtin_nontemporal_store(v[h], reinterpret_cast<u32x4*>(dst + (int64_t)h * 16 * ldy));
+          } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int t = tb + h * 16;
+              uint16_t* d = dst + (int64_t)h * 16 * ldy;
+              if (t < T && n + 8 <= N) {
+                __builtin_nontemporal_store(v[h], reinterpret_cast<u32x4*>(d));
+              } else if (t < T) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                  if (n + e < N) d[e] = (uint16_t)((v[h][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+              }
+            }
+          }
+          // (the next sub-tile's writes come after these reads: LDS
+          // operations of a wave run in order)
         }
       }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave reads only its own tile
-    constexpr int CPR = WTN / 8;          // 16-byte chunks per staged row
-    constexpr int RPI = 64 / CPR;         // rows per store instruction
-    const int rr = lane / CPR, cc = lane % CPR;
-    // (RPI * CPR < 64 when CPR does not divide 64, as for 96-channel wave
-    // tiles: the lanes past that, and the rows past the wave's tile in the
-    // last pass, store nothing)
-    const bool lane_on = lane < RPI * CPR;
-#pragma unroll 4
-    for (int r0 = 0; r0 < WTT; r0 += RPI) {
-      const int tw = r0 + rr;
-      if (!lane_on || tw >= WTT) continue;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(ep + tw * EPS + cc * 16);
-      const int t = t0 + wt * WTT + tw;
-      const int n = n0 + wn * WTN + cc * 8;
-      uint16_t* dst = reinterpret_cast<uint16_t*>(yout) + (int64_t)t * ldy + n;
-      if (full_tile || (t < T && n + 8 <= N)) {
-        // non-temporal: the output is not read again here, and it then leaves
-        // no dirty lines in the caches to be written back under the next
-        // kernels' streams
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
-      } else if (t < T) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (n + e < N) dst[e] = (uint16_t)((v[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-      }
-    }
-    return;
-  }
+    };
+    if (has_bias) stage(std::true_type());
+    else stage(std::false_type());
+  } else {
   // fp32 and int32 outputs: straight from the accumulator layout
   const bool full_i32 = full_tile && (OUT != OUT_I32 || (N & 3) == 0);
 #pragma unroll
   for (int j = 0; j < NTT; ++j) {
     const int tl = wt * WTT + j * 32 + frow;
-    const int t = t0 + tl;
+    const int t = ct0 + tl;
     const float xst = (OUT == OUT_I32) ? 0.0f : s_xs[tl];
 #pragma unroll
     for (int i = 0; i < NTN; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int nl = wn * WTN + i * 32 + g * 8 + fhalf * 4;
-        const int n = n0 + nl;
+        const int n = cn0 + nl;
         if (OUT == OUT_I32) {
           int32_t* dst = reinterpret_cast<int32_t*>(yout) + (int64_t)t * N + n;
           v4i o;
@@ -457,6 +537,10 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
       }
     }
   }
+  }
+  if (!more) break;
+  tile = next;
+  }   // tiles
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -468,8 +552,13 @@ template <int BT, int BN, int WGT, int WGN, int BK, int NS, bool F8, bool HALF>
 static void gemm_tile(const int8_t* xq, const float* xs, int T, int K, const int8_t* wq,
                       const float* ws, int N, const float* bias, void* y, int ldy, int out,
                       hipStream_t st) {
+  // persistent: at most as many workgroups as fit on the device at once
+  // (one per compute unit for the 8-wave tiles, whose LDS fills the unit);
+  // each walks the tiles blockIdx.x, blockIdx.x + gridDim.x, ...
   const int ntiles = ((T + BT - 1) / BT) * ((N + BN - 1) / BN);
-  const dim3 grid((unsigned)ntiles), block(64 * WGT * WGN);
+  const int per_cu = WGT * WGN == 4 ? 2 : 1;
+  const int resident = per_cu * cu_count();
+  const dim3 grid((unsigned)(ntiles < resident ? ntiles : resident)), block(64 * WGT * WGN);
   const int group_t = 4;
   if (out == OUT_BF16)
     hipLaunchKernelGGL((k_gemm_w8a8<BT, BN, WGT, WGN, BK, NS, OUT_BF16, F8, HALF>), grid, block, 0, st,
