@@ -258,9 +258,9 @@ GEMM_SHAPES = [(300, 520, 704), (256, 256, 4096), (513, 1000, 128), (1, 520, 704
                (300, 77, 704), (257, 1003, 128), (129, 4, 64), (2100, 3001, 256),
                (4096, 3001, 128),
                # more tiles than workgroups (each workgroup walks several tiles;
-               # the last round partial): 289 tiles of 256 x 256 and 270 of
-               # 128 x 256, ragged T and N
-               (4200, 4100, 192), (1044, 7427, 128)]
+               # the last round partial), ragged T and N: 363 tiles of 128 x 384,
+               # 377 of 256 x 256, 510 of 128 x 256; then 180 of 128 x 384
+               (4200, 4100, 192), (7179, 3091, 128), (6402, 2312, 192), (1044, 7427, 128)]
 
 
 @pytest.mark.parametrize("T,N,K", GEMM_SHAPES)
@@ -292,7 +292,8 @@ def test_gemm_extreme_accumulators(T, N, K):
 @pytest.mark.parametrize("with_bias", [False, True])
 @pytest.mark.parametrize("T,N,K", [(300, 520, 704), (16, 264, 512), (40, 77, 128), (512, 512, 256),
                                    (300, 77, 768), (257, 1003, 128), (129, 4, 64),
-                                   (2100, 3001, 256), (1500, 6000, 192), (4200, 4100, 128)])
+                                   (2100, 3001, 256), (1500, 6000, 192), (4200, 4100, 128),
+                                   (7179, 3091, 64), (6402, 2312, 128)])
 def test_gemm_epilogue(T, N, K, out, with_bias):
     rng = np.random.default_rng(T * N + K)
     q = rng.integers(-127, 128, (T, K), dtype=np.int8)

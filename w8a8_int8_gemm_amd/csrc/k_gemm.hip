@@ -629,25 +629,32 @@ static void gemm_sizes(const int8_t* xq, const float* xs, int64_t T, int64_t K, 
                        const float* ws, int64_t N, const float* bias, void* y, int64_t ldy,
                        int out, hipStream_t st) {
   const int it = (int)T, ik = (int)K, in = (int)N, il = (int)ldy;
-  // 256 x 256 tiles (8 waves) have the most reuse and win whenever they keep
-  // at least 3/4 of the compute units busy; below that 128 x 256 tiles (8
-  // waves), then 128 x 128 (4 waves), trade reuse for occupancy (measured on
-  // the 2048-token q|k|v, o, down and gate|up shapes).  Where 256 x 256 tiles
-  // do not fill one round but 128 x 384 tiles (8 waves of 64 x 96) fill more
-  // of it, the latter win: 2048 x 6144 x 4096 54 us against 62, 1536 x 6144 x
-  // 4096 46 against 62, 2048 x 6144 x 14336 155 against 173.
-  const int64_t busy = 3 * (int64_t)cu_count() / 4;
+  // The tile kernel is persistent, so a launch takes about (tile rounds) x
+  // (time of one tile); a partial last round costs a whole one.  Per tile,
+  // relative to 256 x 256 (8 waves of 128 x 64): 128 x 384 (8 waves of
+  // 64 x 96) 0.845, 128 x 256 (8 waves of 64 x 64) 0.7 -- measured on the
+  // decoder shapes (2048-4096 tokens, K = 4096 and 14336), where this picks
+  // the fastest of the three or one within noise of it, e.g. 4096 x 6144:
+  // 128 x 384 in 2 rounds 93.5 us against 256 x 256 in 1.5 rounds 106.7 us;
+  // 2048 x 4096: 128 x 256 37.5 us against 47.6.  With fewer 128 x 256 tiles
+  // than 3/4 of the compute units, 128 x 128 tiles (4 waves, two workgroups
+  // per unit) trade reuse for occupancy.
+  const int64_t cus = cu_count();
   const int64_t t256 = ((T + 255) / 256) * ((N + 255) / 256);
   const int64_t t128x256 = ((T + 127) / 128) * ((N + 255) / 256);
   const int64_t t128x384 = ((T + 127) / 128) * ((N + 383) / 384);
-  if (t256 < cu_count() && t128x384 >= busy && t128x384 <= cu_count() && t128x384 > t256)
-    gemm_tile_k<128, 384, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
-  else if (t256 >= busy)
-    gemm_tile_k<256, 256, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
-  else if (t128x256 >= busy)
-    gemm_tile_k<128, 256, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
-  else
+  auto cost = [&](int64_t tiles, int64_t per_tile_milli) {
+    return ((tiles + cus - 1) / cus) * per_tile_milli;
+  };
+  const int64_t c256 = cost(t256, 1000), c384 = cost(t128x384, 845), c128 = cost(t128x256, 700);
+  if (4 * t128x256 < 3 * cus)
     gemm_tile_k<128, 128, 2, 2, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+  else if (c256 <= c384 && c256 <= c128)
+    gemm_tile_k<256, 256, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+  else if (c384 <= c128)
+    gemm_tile_k<128, 384, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+  else
+    gemm_tile_k<128, 256, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
 }
 
 void launch_gemm(const int8_t* xq, const float* xs, int64_t T, int64_t K, const int8_t* wq,
