@@ -132,14 +132,18 @@ class HipTimer:
 
 def _kernel_hash() -> str:
     """Hash of the GEMM's device code: k_gemm.hip up to its host-launcher
-    section, and the device helpers of sq_common.h."""
+    section, and the device helpers of sq_common.h, with comments and
+    whitespace removed (a comment edit does not invalidate the counters)."""
+    import re
     h = hashlib.sha256()
     for f in ("k_gemm.hip", "sq_common.h"):
-        with open(os.path.join(ROOT, "w8a8_int8_gemm_amd", "csrc", f), "rb") as fh:
+        with open(os.path.join(ROOT, "w8a8_int8_gemm_amd", "csrc", f), encoding="utf-8") as fh:
             text = fh.read()
         if f == "k_gemm.hip":
-            text = text.split(b"// host launcher", 1)[0]
-        h.update(text)
+            text = text.split("// host launcher", 1)[0]
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

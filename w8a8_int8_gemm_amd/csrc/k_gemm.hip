@@ -26,7 +26,9 @@
 //    all 64 LDS banks.  For K % 128 == 64, INT8 stages 64 bytes in 4 buffers
 //    and FP8 ends on a half stage.
 //  * Operand reads of the next k-step are interleaved one-for-one with the
-//    MFMAs; one workgroup barrier per stage.
+//    MFMAs; one workgroup barrier per stage.  The first half of the waves
+//    issues every global -> LDS load; the other half, which sets the pace at
+//    the barriers, only reads operands and multiplies.
 //  * Tiles are ordered so that the workgroups that share an XCD (the
 //    hardware deals workgroup ids round-robin over the 8 XCDs) take one
 //    contiguous range of tiles, grouped GROUP_T token panels at a time: they
@@ -57,11 +59,12 @@ constexpr __host__ __device__ int swz(int row) {
   return (row / (256 / BK)) & (BK / 16 - 1);
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Bijective workgroup -> tile map.  Workgroup b runs on XCD b % 8; the
-// workgroups of XCD x get the contiguous tile range that precedes the ranges
-// of XCDs x+1..7.  Inside the range, tiles go GROUP_T token panels at a time.
+// Bijective map of the tile walk index b (blockIdx.x + r * gridDim.x) to a
+// tile.  Workgroup blockIdx.x runs on XCD blockIdx.x % 8; when r > 0 occurs,
+// gridDim.x is the number of resident workgroups, a multiple of the 8 XCDs,
+// so b % 8 is still the workgroup's XCD.  The workgroups of
+// XCD x get the contiguous tile range that precedes the ranges of XCDs
+// x+1..7.  Inside the range, tiles go GROUP_T token panels at a time.
 __device__ __forceinline__ void tile_of(int bid, int nt_t, int nt_n, int group_t, int& pid_t,
                                         int& pid_n) {
   const int ntiles = nt_t * nt_n;
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
   constexpr int RPL = 64 / CPR;             // rows per 1 KiB load
   constexpr int KB = F8 ? 64 : 32;          // bytes of K per MFMA (one k-step)
   constexpr int KS = BK / KB;               // k-steps per stage
-  constexpr int XL = BT / (RPL * NW), WL = BN / (RPL * NW);  // 1 KiB loads per wave per stage
+  constexpr int XL = BT / (RPL * NW), WL = BN / (RPL * NW);  // 1 KiB blocks per wave per stage
   constexpr int LPS = 2 * (XL + WL);        // loads per stage of each issuing wave
   constexpr int OPB = NS * (XS + WS);       // operand stages
   constexpr int NSC = BT + 2 * BN;          // one tile's token scales, channel scales, biases
