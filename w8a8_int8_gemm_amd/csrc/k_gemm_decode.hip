@@ -136,7 +136,6 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_decode(const int8_t* __restric
   int xbase[TB];
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) xbase[tb] = (tb * 16 + i16) * K + q * 16;
-  // operand read of k-step s: row i16's global chunk 4s + q
   // operand read of k-step s, row block b: row 16b + i16's global chunk 4s + q
   int rbase[STEPS];
 #pragma unroll
@@ -179,6 +178,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_decode(const int8_t* __restric
       }
     }
   };
+  // A stage is LPS loads: its LW direct-to-LDS weight loads, then its LX token
+  // loads into registers, all buffer loads.  Loads of one wave complete in
+  // issue order, so "at most LPS loads in flight" means every load of all
+  // but the newest stage has landed.
   int8_t* slot0 = ring;
   int8_t* slot1 = ring + SB;
   // stages 0 and 1 (a stage past ns is all outside: zeros, no traffic)
