@@ -19,7 +19,9 @@ from _gpu_util import DEV, f32, gpu_calibrate, gpu_prepare_weight, say, to_dev  
 
 
 @pytest.mark.parametrize("name,sizes", [("decode", dict(T=16, Tc=64, K=4096, N=4096)),
-                                        ("rmsnorm_qkv", dict(T=300, Tc=256, K=1024, N=640))])
+                                        ("rmsnorm_qkv", dict(T=300, Tc=256, K=1024, N=640)),
+                                        # several GEMM tiles per workgroup (363 of 128 x 384)
+                                        ("qproj_prefill", dict(T=4200, Tc=256, K=512, N=4104))])
 def test_linear_graph_replays_match_eager(name, sizes):
     wl = synth.WORKLOADS[name].with_sizes(**sizes)
     say(f"graph replay {name} {sizes}")

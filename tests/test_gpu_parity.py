@@ -275,6 +275,30 @@ def test_gemm_accumulators(T, N, K):
     np.testing.assert_array_equal(to_np(acc), oracle.int_gemm(q, qw))
 
 
+def test_gemm_two_launches_in_flight_on_two_streams():
+    """Two persistent GEMM launches, each with as many workgroups as the device
+    holds, queued on two streams at once: the workgroups of the second wait
+    for free compute units (no workgroup waits for another), and both results
+    equal the oracle."""
+    shapes = [(4200, 4100, 192), (7179, 3091, 128)]
+    rng = np.random.default_rng(11)
+    ops = []
+    for T, N, K in shapes:
+        q = rng.integers(-127, 128, (T, K), dtype=np.int8)
+        qw = rng.integers(-127, 128, (N, K), dtype=np.int8)
+        ops.append((q, qw, torch.empty((T, N), dtype=torch.int32, device=DEV)))
+    say("gemm two streams")
+    dq = [(to_dev(q), to_dev(qw)) for q, qw, _ in ops]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        for (xq, wq), (_, _, acc), st in zip(dq, ops, streams):
+            sq.sq_gemm_w8a8(xq, None, wq, None, None, acc_out=acc, stream=st)
+    torch.cuda.synchronize()
+    for q, qw, acc in ops:
+        np.testing.assert_array_equal(to_np(acc), oracle.int_gemm(q, qw))
+
+
 @pytest.mark.parametrize("T,N,K", [(2, 8, 65536), (65, 16, 65536)])
 def test_gemm_extreme_accumulators(T, N, K):
     q = np.full((T, K), 127, np.int8)
