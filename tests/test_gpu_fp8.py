@@ -88,6 +88,22 @@ def test_quant_act_fp8(T, K, norm, dt):
     np.testing.assert_array_equal(to_np(xq), q_ref)
 
 
+@pytest.mark.parametrize("T,K,dt,norm", [(6, 14336, "bf16", False), (3, 12288, "f32", True)])
+def test_quant_act_fp8_without_gamma(T, K, dt, norm):
+    """FP8 codes of rows that take the workgroup-per-token register kernel."""
+    rng = np.random.default_rng(3 * T + K)
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    x[:, rng.permutation(K)[:5]] *= 40
+    xin = synth.f32_to_bf16_bits(x) if dt == "bf16" else x
+    say(f"fp8 act without gamma T={T} K={K} {dt} norm={norm}")
+    xq, xs, rr = _u8((T, K)), f32(T), f32(T)
+    sq.sq_quant_act_fp8(to_dev(xin), None, xq, xs, norm=norm, row_rscale=rr if norm else None)
+    torch.cuda.synchronize()
+    q_ref, xs_ref, _ = oracle.quant_act_fp8(xin, None, norm=norm, r=to_np(rr) if norm else None)
+    np.testing.assert_array_equal(to_np(xs), xs_ref)
+    np.testing.assert_array_equal(to_np(xq), q_ref)
+
+
 def test_quant_act_fp8_ties_subnormals_and_zero_rows():
     say("fp8 act ties")
     tab = np.array([v for c, v in sorted({c: float(oracle.e4m3_decode(np.array([c], np.uint8))[0])

@@ -205,21 +205,31 @@ def test_quant_act(T, K, dt, norm):
         assert _ulps(r_gpu, r_own).max() <= 1
 
 
-@pytest.mark.parametrize("T,K", [(6, 14336), (3, 4096)])
-def test_quant_act_without_gamma(T, K):
-    """gamma_f = NULL (an unsmoothed linear): the factor 1 on both sides."""
+@pytest.mark.parametrize("T,K,dt,norm", [(6, 14336, "bf16", False), (3, 4096, "bf16", False),
+                                         (5, 16384, "bf16", True), (4, 12288, "f32", False),
+                                         (3, 9216, "f32", True), (2, 16384, "f32", False),
+                                         (3, 8256, "bf16", False)])
+def test_quant_act_without_gamma(T, K, dt, norm):
+    """gamma_f = NULL (an unsmoothed linear): the factor 1 on both sides.  Rows
+    of 8200-16384 values take the workgroup-per-token register kernel."""
     rng = np.random.default_rng(T + K)
     x = rng.standard_normal((T, K)).astype(np.float32)
     x[:, rng.permutation(K)[:5]] *= 40
-    xin = synth.f32_to_bf16_bits(x)
-    say(f"quant act without gamma T={T} K={K}")
+    if T > 2:
+        x[1] = 0.0                                   # a zero token
+    xin = synth.f32_to_bf16_bits(x) if dt == "bf16" else x
+    say(f"quant act without gamma T={T} K={K} {dt} norm={norm}")
     xq = torch.empty((T, K), dtype=torch.int8, device=DEV)
     xs = f32(T)
-    sq.sq_quant_act(to_dev(xin), None, xq, xs)
+    rr = f32(T) if norm else None
+    sq.sq_quant_act(to_dev(xin), None, xq, xs, norm=norm, row_rscale=rr)
     torch.cuda.synchronize()
-    q_ref, xs_ref, _ = oracle.quant_act(xin, np.ones(K, np.float32))
+    r_gpu = to_np(rr) if norm else None
+    q_ref, xs_ref, _ = oracle.quant_act(xin, np.ones(K, np.float32), norm=norm, r=r_gpu)
     np.testing.assert_array_equal(to_np(xs), xs_ref)
     np.testing.assert_array_equal(to_np(xq), q_ref)
+    if norm:
+        assert _ulps(r_gpu, oracle.rms_rscale(xin)).max() <= 1
 
 
 def test_quant_act_ties_and_fallback():

@@ -308,8 +308,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock, (quant_act_min_waves<In, NV, Q
 }
 
 // ---------------------------------------------------------------------------
-// K > 16384 (K > 8192 for fp32 input): one workgroup per token, three passes
-// over the row (sum of squares, max, quantize); the re-reads hit L2.
+// K > 16384: one workgroup per token, three passes over the row (sum of
+// squares, max, quantize); the re-reads hit L2.
 // ---------------------------------------------------------------------------
 template <class In, bool NORM, bool STATIC, int QF>
 __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem* __restrict__ x,
@@ -388,6 +388,103 @@ __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem*
       if (d > 0.0f && tie) c = quant8_div<STATIC>(xh, d);
     }
     *reinterpret_cast<u32x2*>(xq + r * K + ch * 8) = c;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Rows of up to 2048 chunks (16384 bf16 or fp32 values) that the one-wave
+// kernel does not take: one workgroup of 256 threads per token with the row in
+// registers, NC chunks per thread (chunk c * 256 + thread), every load issued
+// at once; x^ is formed once, and the maximum and the codes come from those
+// registers.  The same fp32 operations per element as the kernels above.
+// ---------------------------------------------------------------------------
+template <class In, int NC, bool NORM, bool STATIC, int QF>
+__global__ __launch_bounds__(256) void k_quant_act_row(const typename In::elem* __restrict__ x,
+                                                       int64_t T, int64_t K, int64_t ld,
+                                                       const float* __restrict__ gamma_f,
+                                                       float eps,
+                                                       const float* __restrict__ static_scale,
+                                                       int8_t* __restrict__ xq,
+                                                       float* __restrict__ xscale,
+                                                       float* __restrict__ rrow) {
+  __shared__ double red_d[4];
+  __shared__ float red_f[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nchunk = (int)(K >> 3);   // <= 256 * NC
+  const int64_t r = blockIdx.x;
+  const typename In::elem* row = x + r * ld;
+  typename In::Raw raw[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = c * 256 + threadIdx.x;
+    raw[c] = In::raw8_nt(row + (ch < nchunk ? ch : 0) * 8);   // read once
+  }
+  float rt = 1.0f;
+  if (NORM) {
+    double ss = 0.0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float v[8];
+      In::widen(raw[c], v);
+      if (c * 256 + (int)threadIdx.x < nchunk)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const double dv = (double)v[i];
+          ss = fma(dv, dv, ss);   // exact square, so the same as mul + add
+        }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red_d[wave] = ss;
+    __syncthreads();
+    ss = (red_d[0] + red_d[1]) + (red_d[2] + red_d[3]);
+    rt = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+    if (rrow != nullptr && threadIdx.x == 0) rrow[r] = rt;
+  }
+  float xh[NC][8];
+  float am = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = c * 256 + threadIdx.x;
+    float v[8];
+    In::widen(raw[c], v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float t = NORM ? v[i] * rt : v[i];
+      xh[c][i] = gamma_f ? t * gamma_f[(ch < nchunk ? ch : 0) * 8 + i] : t;
+    }
+    if (ch < nchunk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(xh[c][i]));
+  }
+  if (!STATIC) {
+    am = wave_max(am);
+    if (lane == 0) red_f[wave] = am;
+    __syncthreads();
+    am = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+  }
+  const float d = STATIC ? static_scale[0] : am / (QF == QF_FP8 ? 448.0f : 127.0f);
+  if (threadIdx.x == 0) xscale[r] = d;
+  const float rc = 1.0f / d;
+  const bool fast = d > 0.0f && rc <= 3.0e38f;
+  const float rlo = rc * (1.0f - 0x1p-20f), rhi = rc * (1.0f + 0x1p-20f);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = c * 256 + threadIdx.x;
+    if (ch >= nchunk) continue;
+    u32x2 q;
+    q[0] = 0u;
+    q[1] = 0u;
+    if constexpr (QF == QF_FP8) {
+      bool split = true;
+      if (fast) q = quant8_fp8_rc<STATIC>(xh[c], rlo, rhi, split);
+      if (split) q = quant8_fp8<STATIC>(xh[c], d);
+    } else {
+      bool tie = true;
+      if (fast) q = quant8<STATIC>(xh[c], rc, tie);
+      if (d > 0.0f && tie) q = quant8_div<STATIC>(xh[c], d);
+    }
+    *reinterpret_cast<u32x2*>(xq + r * K + ch * 8) = q;
   }
 }
 
@@ -602,11 +699,16 @@ static void quant_act_t(const void* x, int64_t T, int64_t K, int64_t ld, const f
   else if (nchunk <= 512) SQ_QA(8);
   else if (nchunk <= 1024) SQ_QA(16);
   else if (In::kBytes == 2 && nchunk <= 2048 && gamma_f != nullptr) {
-    // bf16 rows up to 16384 in VGPRs, gamma_f staged once per workgroup; the
-    // wide kernel reads gamma_f per token through the caches, which costs
-    // more than its extra row passes (104 vs 25 us, 2048 x 14336), but with
-    // no gamma_f its four waves per token win (23 vs 34 us)
+    // bf16 rows up to 16384 in VGPRs, gamma_f staged once per workgroup: a
+    // workgroup per token would read gamma_f per token through the caches
+    // (104 against 25 us, 2048 x 14336), but with no gamma_f its four waves
+    // per token win
     if constexpr (In::kBytes == 2) SQ_QA(32);
+  } else if (nchunk <= 2048) {
+    // a workgroup per token with the row in registers
+    hipLaunchKernelGGL((k_quant_act_row<In, 8, NORM, STATIC, QF>), dim3((unsigned)T), dim3(256), 0,
+                       st, (const typename In::elem*)x, T, K, ld, gamma_f, eps, sscale, xq, xscale,
+                       rrow);
   } else
     hipLaunchKernelGGL((k_quant_act_wide<In, NORM, STATIC, QF>), dim3((unsigned)T), dim3(256), 0, st,
                        (const typename In::elem*)x, T, K, ld, gamma_f, eps, sscale, xq, xscale,
