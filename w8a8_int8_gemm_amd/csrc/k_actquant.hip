@@ -672,6 +672,102 @@ __global__ __launch_bounds__(256) void k_quant_act_ln_wide(
   }
 }
 
+// LayerNorm rows of 4097-16384 values: one workgroup of 256 threads per
+// token with the row in registers (chunk c * 256 + thread, NC per thread, all
+// loads issued at once); the same operations and sum orders per thread as
+// k_quant_act_ln_wide, without its re-reads.
+template <class In, int NC>
+__global__ __launch_bounds__(256) void k_quant_act_ln_row(
+    const typename In::elem* __restrict__ x, int64_t T, int64_t K, int64_t ld,
+    const float* __restrict__ gamma_f, const float* __restrict__ beta_f, float eps,
+    int8_t* __restrict__ xq, float* __restrict__ xscale, float* __restrict__ mrow,
+    float* __restrict__ rrow) {
+  __shared__ double red_d[4];
+  __shared__ float red_f[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nchunk = (int)(K >> 3);   // <= 256 * NC
+  const int64_t r = blockIdx.x;
+  const typename In::elem* row = x + r * ld;
+  typename In::Raw raw[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = c * 256 + threadIdx.x;
+    raw[c] = In::raw8_nt(row + (ch < nchunk ? ch : 0) * 8);   // read once
+  }
+  auto block_sum = [&](double v) {
+    v = wave_sum(v);
+    __syncthreads();
+    if (lane == 0) red_d[wave] = v;
+    __syncthreads();
+    return (red_d[0] + red_d[1]) + (red_d[2] + red_d[3]);
+  };
+  double s1 = 0.0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float v[8];
+    In::widen(raw[c], v);
+    if (c * 256 + (int)threadIdx.x < nchunk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s1 += (double)v[i];
+  }
+  const double mu = block_sum(s1) / (double)K;
+  double s2 = 0.0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float v[8];
+    In::widen(raw[c], v);
+    if (c * 256 + (int)threadIdx.x < nchunk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double dd = (double)v[i] - mu;
+        s2 += dd * dd;
+      }
+  }
+  s2 = block_sum(s2);
+  const float mt = (float)mu;
+  const float rt = (float)(1.0 / sqrt(s2 / (double)K + (double)eps));
+  if (threadIdx.x == 0) {
+    if (mrow != nullptr) mrow[r] = mt;
+    if (rrow != nullptr) rrow[r] = rt;
+  }
+  float xh[NC][8];
+  float am = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = c * 256 + threadIdx.x;
+    const int cs = ch < nchunk ? ch : 0;
+    float v[8];
+    In::widen(raw[c], v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      xh[c][i] = (v[i] - mt) * rt * gamma_f[cs * 8 + i] + beta_f[cs * 8 + i];
+    if (ch < nchunk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(xh[c][i]));
+  }
+  am = wave_max(am);
+  if (lane == 0) red_f[wave] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+  const float d = am / 127.0f;
+  const float rc = 1.0f / d;
+  const bool fast = rc <= 3.0e38f;
+  if (threadIdx.x == 0) xscale[r] = d;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = c * 256 + threadIdx.x;
+    if (ch >= nchunk) continue;
+    u32x2 q;
+    q[0] = 0u;
+    q[1] = 0u;
+    bool tie = true;
+    if (fast) q = quant8(xh[c], rc, tie);
+    if (d > 0.0f && tie) q = quant8_div(xh[c], d);
+    *reinterpret_cast<u32x2*>(xq + r * K + ch * 8) = q;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------
@@ -705,10 +801,15 @@ static void quant_act_t(const void* x, int64_t T, int64_t K, int64_t ld, const f
     // per token win
     if constexpr (In::kBytes == 2) SQ_QA(32);
   } else if (nchunk <= 2048) {
-    // a workgroup per token with the row in registers
-    hipLaunchKernelGGL((k_quant_act_row<In, 8, NORM, STATIC, QF>), dim3((unsigned)T), dim3(256), 0,
-                       st, (const typename In::elem*)x, T, K, ld, gamma_f, eps, sscale, xq, xscale,
-                       rrow);
+    // a workgroup per token with the row in registers, chunks per thread
+    // sized to the row
+#define SQ_QAR(NC)                                                                            \
+  hipLaunchKernelGGL((k_quant_act_row<In, NC, NORM, STATIC, QF>), dim3((unsigned)T), dim3(256), \
+                     0, st, (const typename In::elem*)x, T, K, ld, gamma_f, eps, sscale, xq,   \
+                     xscale, rrow)
+    if (nchunk <= 1536) SQ_QAR(6);
+    else SQ_QAR(8);
+#undef SQ_QAR
   } else
     hipLaunchKernelGGL((k_quant_act_wide<In, NORM, STATIC, QF>), dim3((unsigned)T), dim3(256), 0, st,
                        (const typename In::elem*)x, T, K, ld, gamma_f, eps, sscale, xq, xscale,
@@ -775,9 +876,18 @@ static void quant_act_ln_t(const void* x, int64_t T, int64_t K, int64_t ld, cons
   else if (nchunk <= 128) quant_act_ln_nv<In, 2>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
   else if (nchunk <= 256) quant_act_ln_nv<In, 4>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
   else if (nchunk <= 512) quant_act_ln_nv<In, 8>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
-  else   // wider rows: the workgroup-per-token kernel (faster above 4096 elements
-         // than one wave per token with its row in registers: 2048 tokens x
-         // 6144 19.9 against 27.4 us, x 8192 24.5 against 33.8 us)
+  else if (nchunk <= 2048) {   // wider rows: a workgroup per token, chunks per
+                               // thread sized to the row
+    const int nc = (int)((nchunk + 255) / 256);
+#define SQ_LNR(NC)                                                                            \
+  hipLaunchKernelGGL((k_quant_act_ln_row<In, NC>), dim3((unsigned)T), dim3(256), 0, st,      \
+                     (const typename In::elem*)x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow)
+    if (nc <= 3) SQ_LNR(3);
+    else if (nc == 4) SQ_LNR(4);
+    else if (nc <= 6) SQ_LNR(6);
+    else SQ_LNR(8);
+#undef SQ_LNR
+  } else
     hipLaunchKernelGGL((k_quant_act_ln_wide<In>), dim3((unsigned)T), dim3(256), 0, st,
                        (const typename In::elem*)x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow);
 }
