@@ -206,7 +206,8 @@ def test_gemm_fp8_group_arithmetic():
 
 
 @pytest.mark.parametrize("T,N,K", [(200, 136, 4096), (1500, 4096, 128), (1800, 6104, 64),
-                                   (4200, 4100, 192), (7179, 3091, 128)])   # several tiles per workgroup
+                                   (4200, 4100, 192), (7179, 3091, 128),   # several tiles per
+                                   (4625, 4999, 128)])                     # workgroup
 def test_gemm_fp8_exact_when_every_partial_sum_is_representable(T, N, K):
     say(f"fp8 gemm exact small integers T={T} N={N} K={K}")
     rng = np.random.default_rng(42 + T)

@@ -268,9 +268,12 @@ GEMM_SHAPES = [(300, 520, 704), (256, 256, 4096), (513, 1000, 128), (1, 520, 704
                (300, 77, 704), (257, 1003, 128), (129, 4, 64), (2100, 3001, 256),
                (4096, 3001, 128),
                # more tiles than workgroups (each workgroup walks several tiles;
-               # the last round partial), ragged T and N: 363 tiles of 128 x 384,
-               # 377 of 256 x 256, 510 of 128 x 256; then 180 of 128 x 384
-               (4200, 4100, 192), (7179, 3091, 128), (6402, 2312, 192), (1044, 7427, 128)]
+               # the last round partial), ragged T and N: 374 tiles of 256 x 192,
+               # 380 of 256 x 256, 510 of 128 x 256, 506 of 128 x 384, 493 of
+               # 256 x 192; then one round: 242 tiles of 128 x 384, 195 of
+               # 256 x 192
+               (4200, 4100, 192), (4625, 4999, 64), (6402, 2312, 192), (2827, 8068, 64),
+               (7179, 3091, 128), (1290, 8068, 128), (1044, 7427, 128)]
 
 
 @pytest.mark.parametrize("T,N,K", GEMM_SHAPES)
@@ -327,7 +330,7 @@ def test_gemm_extreme_accumulators(T, N, K):
 @pytest.mark.parametrize("T,N,K", [(300, 520, 704), (16, 264, 512), (40, 77, 128), (512, 512, 256),
                                    (300, 77, 768), (257, 1003, 128), (129, 4, 64),
                                    (2100, 3001, 256), (1500, 6000, 192), (4200, 4100, 128),
-                                   (7179, 3091, 64), (6402, 2312, 128)])
+                                   (7179, 3091, 64), (6402, 2312, 128), (4625, 4999, 64)])
 def test_gemm_epilogue(T, N, K, out, with_bias):
     rng = np.random.default_rng(T * N + K)
     q = rng.integers(-127, 128, (T, K), dtype=np.int8)

@@ -23,8 +23,8 @@
 //    ... lds (HBM/L2 -> LDS without VGPRs).  A 1 KiB load instruction fills 8
 //    rows of 128 bytes; the 16-byte chunk c of row r is stored at chunk
 //    position c ^ swz(r), so the rows an MFMA operand read touches spread over
-//    all 64 LDS banks.  For K % 128 == 64, INT8 stages 64 bytes in 4 buffers
-//    and FP8 ends on a half stage.
+//    all 64 LDS banks.  For K % 128 == 64, INT8 stages 64 bytes in 4 buffers;
+//    FP8, and INT8 with 192-channel tiles, end on a half stage.
 //  * Operand reads of the next k-step are interleaved one-for-one with the
 //    MFMAs; one workgroup barrier per stage.  The first half of the waves
 //    issues every global -> LDS load; the other half, which sets the pace at
@@ -127,6 +127,7 @@ __global__ __launch_bounds__(64 * WGT * WGN) void k_gemm_w8a8(const int8_t* __re
   constexpr int KB = F8 ? 64 : 32;          // bytes of K per MFMA (one k-step)
   constexpr int KS = BK / KB;               // k-steps per stage
   constexpr int XL = BT / (RPL * NW), WL = BN / (RPL * NW);  // 1 KiB blocks per wave per stage
+  static_assert(BT % (RPL * NW) == 0 && BN % (RPL * NW) == 0, "whole 1 KiB blocks per wave");
   constexpr int LPS = 2 * (XL + WL);        // loads per stage of each issuing wave
   constexpr int OPB = NS * (XS + WS);       // operand stages
   constexpr int NSC = BT + 2 * BN;          // one tile's token scales, channel scales, biases
@@ -600,12 +601,15 @@ template <int BT, int BN, int WGT, int WGN, bool F8>
 static void gemm_tile_k(const int8_t* xq, const float* xs, int T, int K, const int8_t* wq,
                         const float* ws, int N, const float* bias, void* y, int ldy, int out,
                         hipStream_t st) {
+  // (64-byte stages need whole 1 KiB loads of 16 rows per wave: not so for
+  // 192-channel tiles, which end on a half stage as FP8 does)
+  constexpr bool blocks64 = BT % (16 * WGT * WGN) == 0 && BN % (16 * WGT * WGN) == 0;
   if (K % 128 == 0) {
     gemm_tile<BT, BN, WGT, WGN, 128, 2, F8, false>(xq, xs, T, K, wq, ws, N, bias, y, ldy, out, st);
   } else {
-    if constexpr (F8)
-      gemm_tile<BT, BN, WGT, WGN, 128, 2, true, true>(xq, xs, T, K, wq, ws, N, bias, y, ldy, out,
-                                                     st);
+    if constexpr (F8 || !blocks64)
+      gemm_tile<BT, BN, WGT, WGN, 128, 2, F8, true>(xq, xs, T, K, wq, ws, N, bias, y, ldy, out,
+                                                   st);
     else
       gemm_tile<BT, BN, WGT, WGN, 64, 4, false, false>(xq, xs, T, K, wq, ws, N, bias, y, ldy, out,
                                                       st);
@@ -634,26 +638,32 @@ static void gemm_sizes(const int8_t* xq, const float* xs, int64_t T, int64_t K, 
   const int it = (int)T, ik = (int)K, in = (int)N, il = (int)ldy;
   // The tile kernel is persistent, so a launch takes about (tile rounds) x
   // (time of one tile); a partial last round costs a whole one.  Per tile,
-  // relative to 256 x 256 (8 waves of 128 x 64): 128 x 384 (8 waves of
-  // 64 x 96) 0.845, 128 x 256 (8 waves of 64 x 64) 0.7 -- measured on the
-  // decoder shapes (2048-4096 tokens, K = 4096 and 14336), where this picks
-  // the fastest of the three or one within noise of it, e.g. 4096 x 6144:
-  // 128 x 384 in 2 rounds 93.5 us against 256 x 256 in 1.5 rounds 106.7 us;
-  // 2048 x 4096: 128 x 256 37.5 us against 47.6.  With fewer 128 x 256 tiles
+  // relative to 256 x 256 (8 waves of 128 x 64): 256 x 192 (8 waves of
+  // 64 x 96) 0.81, 128 x 384 (8 waves of 64 x 96) 0.845, 128 x 256 (8 waves
+  // of 64 x 64) 0.7 -- measured on the decoder shapes (2048-4096 tokens,
+  // K = 4096 and 14336), where this picks the fastest or one within noise of
+  // it, e.g. 4096 x 6144: 128 x 384 in 2 rounds 93.5 us against 256 x 256 in
+  // 1.5 rounds 106.7 us; 2048 x 4096: 128 x 256 37.5 us against 47.6;
+  // 2048 x 6144: 256 x 192 50.9 us against 128 x 384 53.2 (the same 256
+  // tiles, 15% more MACs per global->LDS load).  With fewer 128 x 256 tiles
   // than 3/4 of the compute units, 128 x 128 tiles (4 waves, two workgroups
   // per unit) trade reuse for occupancy.
   const int64_t cus = cu_count();
   const int64_t t256 = ((T + 255) / 256) * ((N + 255) / 256);
   const int64_t t128x256 = ((T + 127) / 128) * ((N + 255) / 256);
   const int64_t t128x384 = ((T + 127) / 128) * ((N + 383) / 384);
+  const int64_t t256x192 = ((T + 255) / 256) * ((N + 191) / 192);
   auto cost = [&](int64_t tiles, int64_t per_tile_milli) {
     return ((tiles + cus - 1) / cus) * per_tile_milli;
   };
   const int64_t c256 = cost(t256, 1000), c384 = cost(t128x384, 845), c128 = cost(t128x256, 700);
+  const int64_t c192 = cost(t256x192, 810);
   if (4 * t128x256 < 3 * cus)
     gemm_tile_k<128, 128, 2, 2, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
-  else if (c256 <= c384 && c256 <= c128)
+  else if (c256 <= c192 && c256 <= c384 && c256 <= c128)
     gemm_tile_k<256, 256, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
+  else if (c192 <= c384 && c192 <= c128)
+    gemm_tile_k<256, 192, 4, 2, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
   else if (c384 <= c128)
     gemm_tile_k<128, 384, 2, 4, F8>(xq, xs, it, ik, wq, ws, in, bias, y, il, out, st);
   else
