@@ -126,3 +126,34 @@ def test_static_linear_end_to_end(name, sizes):
     err = oracle.rel_error(ref, to_np(y))
     say(f"  static-step layer error {err:.4%}")
     assert err < 0.2
+
+
+@pytest.mark.parametrize("T,K,norm,dt", [(5, 12288, False, "bf16"), (4, 9216, True, "f32")])
+def test_static_codes_without_gamma_on_wide_rows(T, K, norm, dt):
+    """A fixed step, gamma_f = NULL, rows of 8200-16384 values (the
+    workgroup-per-token register kernel): INT8 and FP8 codes bit-exact,
+    quotients past the step's range clipped."""
+    rng = np.random.default_rng(5 * T + K)
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    x[:, rng.permutation(K)[:5]] *= 40
+    xin = synth.f32_to_bf16_bits(x) if dt == "bf16" else x
+    delta = np.float32(0.05)   # many quotients past 127 (and past 448 for FP8)
+    say(f"static without gamma T={T} K={K} norm={norm} {dt}")
+    d = torch.tensor([delta], dtype=torch.float32, device=DEV)
+    xq = torch.empty((T, K), dtype=torch.int8, device=DEV)
+    xs, rr = f32(T), f32(T)
+    sq.sq_quant_act_static(to_dev(xin), None, d, xq, xs, norm=norm,
+                           row_rscale=rr if norm else None)
+    xq8 = torch.empty((T, K), dtype=torch.uint8, device=DEV)
+    xs8, rr8 = f32(T), f32(T)
+    sq.sq_quant_act_static_fp8(to_dev(xin), None, d, xq8, xs8, norm=norm,
+                               row_rscale=rr8 if norm else None)
+    torch.cuda.synchronize()
+    r_gpu = to_np(rr) if norm else None
+    q_ref, xs_ref, _ = oracle.quant_act_static(xin, delta, None, norm=norm, r=r_gpu)
+    np.testing.assert_array_equal(to_np(xq), q_ref)
+    np.testing.assert_array_equal(to_np(xs), xs_ref)
+    q8_ref, xs8_ref, _ = oracle.quant_act_static_fp8(xin, delta, None, norm=norm,
+                                                     r=to_np(rr8) if norm else None)
+    np.testing.assert_array_equal(to_np(xq8), q8_ref)
+    np.testing.assert_array_equal(to_np(xs8), xs8_ref)
