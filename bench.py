@@ -779,7 +779,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only: the layer's multi-GPU "
+        print(json.dumps({"error": "bench.py measures one GPU only: the layer's multi-GPU "
                           "sharding is a design note, not built; run with --gpus 1"}))
         sys.exit(2)
 
