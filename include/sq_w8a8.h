@@ -333,6 +333,8 @@ sq_status sq_w8a8_linear_static_fp8(const void *x, sq_dtype x_dt, int64_t t, int
  * give no formula; here
  *   m_t = fp32(mu_t), r_t = fp32(1 / sqrt(var_t + eps)), mu_t and var_t the
  *         row's mean and mean squared deviation from mu_t, summed in fp64
+ *         (in one pass, shifted by the row's first value: m_t and r_t can
+ *         differ from a two-pass evaluation by one fp32 ulp)
  *   LN(h)[t,j] = fp32( fp32( fp32(h - m_t) * r_t ) * gamma_j ) + beta_j  (fp32)
  * sq_calibrate_ln: as sq_calibrate in norm mode with a[j] = max_t |LN(h)[t,j]|
  *   under the norm's own gamma and beta (NULL = ones / zeros); same flags.

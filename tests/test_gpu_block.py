@@ -58,6 +58,57 @@ def test_quant_act_ln(T, K, dt):
     np.testing.assert_array_equal(to_np(xq), q_ref)
 
 
+def _hard_ln_rows(K, dt, seed):
+    """Rows that stress one-pass statistics: a large offset against a small
+    spread, an extreme first element (the shift) over a near-zero mean, a
+    constant row, tiny and huge magnitudes, and exact +-1 alternation."""
+    rng = np.random.default_rng(seed)
+    rows = [
+        1000.0 + rng.normal(0, 1, K),                    # mean / spread ~ 500 in bf16
+        np.r_[3000.0, rng.normal(0, 1, K - 1)],          # the shift is a 3000-sigma outlier
+        np.r_[-rng.normal(0, 1, K - 1), 1e4][::-1],      # the shift is -1e4, the rest N(0,1)
+        np.full(K, 2.5),                                 # constant: var = 0 exactly
+        rng.normal(0, 1e-20, K),                         # tiny
+        rng.normal(0, 1e15, K) + 3e16,                   # huge with an offset
+        np.tile([1.0, -1.0], K // 2),                    # mean exactly 0
+        rng.standard_cauchy(K).clip(-1e6, 1e6),          # heavy tails
+    ]
+    h = np.stack(rows).astype(np.float32)
+    return synth.f32_to_bf16_bits(h) if dt == "bf16" else h
+
+
+@pytest.mark.parametrize("K,dt", [(512, "bf16"), (4096, "bf16"), (4096, "f32"), (12352, "bf16"),
+                                  (20480, "bf16"), (9216, "f32")])
+def test_ln_statistics_hard_rows(K, dt):
+    """The GPU takes the LayerNorm mean and variance in one pass of fp64 sums
+    shifted by the row's first element; on rows built to break such sums the
+    statistics stay within one fp32 ulp of the oracle's two-pass definition
+    (quantizer kernels of every width), the codes and steps are bit-exact
+    given the GPU's statistics, and the calibration maxima follow (narrow and
+    wide calibration kernels)."""
+    h = _hard_ln_rows(K, dt, K)
+    T = h.shape[0]
+    say(f"ln hard rows K={K} {dt}")
+    eps = 1e-5
+    gp = np.ones(K, np.float32)
+    bp = np.zeros(K, np.float32)
+    xq = torch.empty((T, K), dtype=torch.int8, device=DEV)
+    xs, m, r = f32(T), f32(T), f32(T)
+    sq.sq_quant_act_ln(to_dev(h), to_dev(gp), to_dev(bp), xq, xs, eps=eps, row_mean=m,
+                       row_rscale=r)
+    a = f32(K)
+    sq.sq_calibrate_ln(to_dev(h), None, 0.5, a, eps=eps)
+    torch.cuda.synchronize()
+    m_ref, r_ref = oracle.ln_stats(h, eps=eps)
+    assert _ulps(to_np(m), m_ref).max() <= 1, (to_np(m), m_ref)
+    assert _ulps(to_np(r), r_ref).max() <= 1, (to_np(r), r_ref)
+    q_ref, xs_ref, _, _ = oracle.quant_act_ln(h, gp, bp, eps=eps, mean=to_np(m), r=to_np(r))
+    np.testing.assert_array_equal(to_np(xs), xs_ref)
+    np.testing.assert_array_equal(to_np(xq), q_ref)
+    a_ref = oracle.act_absmax_ln(h, eps=eps)
+    np.testing.assert_allclose(to_np(a), a_ref, rtol=2.0 ** -20, atol=0)
+
+
 @pytest.mark.parametrize("K,dt", [(512, "bf16"), (4096, "bf16"), (1344, "f32"), (8192, "bf16"),
                                   (4096, "f32"), (8192, "f32")])
 def test_calibrate_and_fold_ln(K, dt):

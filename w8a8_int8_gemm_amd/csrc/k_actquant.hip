@@ -30,6 +30,7 @@
 // holds for every quotient below 128 in magnitude; at and above 128 the
 // rounded value clamps to +-127 whichever way it rounds.
 #include "sq_common.h"
+#include "sq_norm.h"
 #include "sq_internal.h"
 
 namespace sqk {
@@ -491,8 +492,9 @@ __global__ __launch_bounds__(256) void k_quant_act_row(const typename In::elem* 
 // ---------------------------------------------------------------------------
 // LayerNorm form ("SmoothQuant: Weight-Only vs W8A8", Integration with
 // Transformers: 1/s folded into the LayerNorm's gamma and beta):
-//   m_t = fp32(mean), r_t = fp32(1/sqrt(var + eps)) (fp64 sums, the variance
-//   about the fp64 mean), x^ = fp32(fp32(fp32(h - m_t) * r_t) * gamma'_k) +
+//   m_t = fp32(mean), r_t = fp32(1/sqrt(var + eps)) (one pass of fp64 sums
+//   shifted by the row's first element, ln_stats), x^ =
+//   fp32(fp32(fp32(h - m_t) * r_t) * gamma'_k) +
 //   beta'_k, then the per-token INT8 quantizer above.
 // K <= 4096: one token per wave, the row's raw values in
 // VGPRs from the load to the store; gamma' and beta' come through the caches
@@ -516,17 +518,15 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_quant_act_ln(
     const int ch = j * 64 + lane;
     raw[j] = In::raw8_nt(row + (ch < nchunk ? ch : 0) * 8);   // read once
   }
-  double s1 = 0.0;
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    float v[8];
-    In::widen(raw[j], v);
-    if (j * 64 + lane < nchunk)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s1 += (double)v[i];
+  // the norm's statistics in one pass, shifted by the row's first element
+  // (ln_stats)
+  double c;
+  {
+    float v0[8];
+    In::widen(raw[0], v0);
+    c = (double)__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v0[0])));
   }
-  const double mu = wave_sum(s1) / (double)K;
-  double s2 = 0.0;
+  double s1 = 0.0, s2 = 0.0;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     float v[8];
@@ -534,13 +534,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_quant_act_ln(
     if (j * 64 + lane < nchunk)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const double d = (double)v[i] - mu;
-        s2 += d * d;
+        const double d = (double)v[i] - c;
+        s1 += d;
+        s2 = fma(d, d, s2);
       }
   }
-  s2 = wave_sum(s2);
-  const float mt = (float)mu;
-  const float rt = (float)(1.0 / sqrt(s2 / (double)K + (double)eps));
+  float mt, rt;
+  ln_stats(c, wave_sum(s1), wave_sum(s2), K, eps, mt, rt);
   if (lane == 0) {
     if (mrow != nullptr) mrow[r] = mt;
     if (rrow != nullptr) rrow[r] = rt;
@@ -613,27 +613,29 @@ __global__ __launch_bounds__(256) void k_quant_act_ln_wide(
     __syncthreads();
     return (red_d[0] + red_d[1]) + (red_d[2] + red_d[3]);
   };
-  double s1 = 0.0;
-  for (int64_t ch = threadIdx.x; ch < nchunk; ch += 256) {
-    float v[8];
-    In::load8(row + ch * 8, v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s1 += (double)v[i];
+  // the norm's statistics in one pass, shifted by the row's first element
+  // (ln_stats)
+  double c;
+  {
+    float v0[8];
+    In::load8(row, v0);
+    c = (double)v0[0];
   }
-  const double mu = block_sum(s1) / (double)K;
-  double s2 = 0.0;
+  double s1 = 0.0, s2 = 0.0;
   for (int64_t ch = threadIdx.x; ch < nchunk; ch += 256) {
     float v[8];
     In::load8(row + ch * 8, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const double dd = (double)v[i] - mu;
-      s2 += dd * dd;
+      const double dd = (double)v[i] - c;
+      s1 += dd;
+      s2 = fma(dd, dd, s2);
     }
   }
+  s1 = block_sum(s1);
   s2 = block_sum(s2);
-  const float mt = (float)mu;
-  const float rt = (float)(1.0 / sqrt(s2 / (double)K + (double)eps));
+  float mt, rt;
+  ln_stats(c, s1, s2, K, eps, mt, rt);
   if (threadIdx.x == 0) {
     if (mrow != nullptr) mrow[r] = mt;
     if (rrow != nullptr) rrow[r] = rt;
@@ -702,17 +704,15 @@ __global__ __launch_bounds__(256) void k_quant_act_ln_row(
     __syncthreads();
     return (red_d[0] + red_d[1]) + (red_d[2] + red_d[3]);
   };
-  double s1 = 0.0;
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    float v[8];
-    In::widen(raw[c], v);
-    if (c * 256 + (int)threadIdx.x < nchunk)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s1 += (double)v[i];
+  // the norm's statistics in one pass, shifted by the row's first element
+  // (ln_stats)
+  double sh;
+  {
+    float v0[8];
+    In::load8(row, v0);
+    sh = (double)v0[0];
   }
-  const double mu = block_sum(s1) / (double)K;
-  double s2 = 0.0;
+  double s1 = 0.0, s2 = 0.0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     float v[8];
@@ -720,13 +720,15 @@ __global__ __launch_bounds__(256) void k_quant_act_ln_row(
     if (c * 256 + (int)threadIdx.x < nchunk)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const double dd = (double)v[i] - mu;
-        s2 += dd * dd;
+        const double dd = (double)v[i] - sh;
+        s1 += dd;
+        s2 = fma(dd, dd, s2);
       }
   }
+  s1 = block_sum(s1);
   s2 = block_sum(s2);
-  const float mt = (float)mu;
-  const float rt = (float)(1.0 / sqrt(s2 / (double)K + (double)eps));
+  float mt, rt;
+  ln_stats(sh, s1, s2, K, eps, mt, rt);
   if (threadIdx.x == 0) {
     if (mrow != nullptr) mrow[r] = mt;
     if (rrow != nullptr) rrow[r] = rt;

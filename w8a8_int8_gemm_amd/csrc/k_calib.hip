@@ -20,6 +20,7 @@
 // wave, then across the workgroup, then with one unsigned atomic max per
 // column (max is order-free, so the result is exact and deterministic).
 #include "sq_common.h"
+#include "sq_norm.h"
 #include "sq_internal.h"
 
 namespace sqk {
@@ -224,8 +225,9 @@ __global__ __launch_bounds__(256) void k_rms_act_absmax(const typename In::elem*
 
 // ---------------------------------------------------------------------------
 // LayerNorm-mode calibration absmax, K <= 4096.  Same row-per-wave layout.
-// Per row: the fp64 mean, the fp64 sum of squared deviations from it,
-// m_t = fp32(mean) and r_t = fp32(1/sqrt(var + eps)); then every element's
+// Per row: the fp64 mean and variance (one pass of sums shifted by the row's
+// first element, ln_stats), m_t = fp32(mean) and r_t = fp32(1/sqrt(var +
+// eps)); then every element's
 // norm output x = fp32(fp32(fp32(h - m_t) * r_t) * gamma_j) + beta_j, exactly
 // as the norm forms it, and the running maximum of |x| per column -- one
 // value per column in registers (tracking the maximum and minimum of the
@@ -274,7 +276,6 @@ __global__ __launch_bounds__(256) void k_ln_act_absmax(const typename In::elem* 
   for (int j = 0; j < NV; ++j)
 #pragma unroll
     for (int i = 0; i < 8; ++i) mx[j][i] = 0.0f;
-  const double dK = (double)K;
   for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < rows; r += (int64_t)gridDim.x * 4) {
     typename In::Raw raw[NV];
     const typename In::elem* row = h + r * ld;
@@ -283,21 +284,16 @@ __global__ __launch_bounds__(256) void k_ln_act_absmax(const typename In::elem* 
       const int ch = j * 64 + lane;
       raw[j] = In::raw8_nt(row + (ch < nchunk ? ch : 0) * 8);   // read once
     }
-    double s1 = 0.0;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      float v[8];
-      In::widen(raw[j], v);
-      if (j * 64 + lane < nchunk)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s1 += (double)v[i];
+    // one pass of shifted fp64 sums (ln_stats), shifted by the row's first
+    // element; against sums about the mean in a second pass: 16384 x 4096
+    // 52.7 -> 44.9 us, 65536 x 4096 153.6 -> 126.5 us, same maxima
+    double c;
+    {
+      float v0[8];
+      In::widen(raw[0], v0);
+      c = (double)__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v0[0])));
     }
-    const double mu = wave_sum(s1) / dK;
-    // keep only the raw values alive between the passes (each pass widens
-    // them again): otherwise the compiler keeps every value's fp64 form
-#pragma unroll
-    for (int j = 0; j < NV; ++j) In::opaque(raw[j]);
-    double s2 = 0.0;
+    double s1 = 0.0, s2 = 0.0;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       float v[8];
@@ -305,13 +301,13 @@ __global__ __launch_bounds__(256) void k_ln_act_absmax(const typename In::elem* 
       if (j * 64 + lane < nchunk)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const double d = (double)v[i] - mu;
-          s2 += d * d;
+          const double d = (double)v[i] - c;
+          s1 += d;
+          s2 = fma(d, d, s2);
         }
     }
-    s2 = wave_sum(s2);
-    const float mt = (float)mu;
-    const float rt = (float)(1.0 / sqrt(s2 / dK + (double)eps));
+    float mt, rt;
+    ln_stats(c, wave_sum(s1), wave_sum(s2), K, eps, mt, rt);
 #pragma unroll
     for (int j = 0; j < NV; ++j) In::opaque(raw[j]);
     static_for<NV>([&](auto jc) {
@@ -392,6 +388,42 @@ __device__ __forceinline__ double wide_row_sum(const typename In::elem* row, int
   return wave_sum(acc);
 }
 
+// the LayerNorm statistics' shifted sums over the row (ln_stats): s1 =
+// sum(v - c), s2 = sum((v - c)^2), in one pass with the same load pattern
+template <class In>
+__device__ __forceinline__ void wide_row_shifted_sums(const typename In::elem* row, int64_t nchunk,
+                                                      int lane, double c, double& s1,
+                                                      double& s2) {
+  double a1 = 0.0, a2 = 0.0;
+  auto add8 = [&](const float (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double d = (double)v[i] - c;
+      a1 += d;
+      a2 = fma(d, d, a2);
+    }
+  };
+  int64_t ch = lane;
+  for (; ch + 3 * 64 < nchunk; ch += 4 * 64) {
+    typename In::Raw raw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) raw[u] = In::raw8(row + (ch + u * 64) * 8);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float v[8];
+      In::widen(raw[u], v);
+      add8(v);
+    }
+  }
+  for (; ch < nchunk; ch += 64) {
+    float v[8];
+    In::load8(row + ch * 8, v);
+    add8(v);
+  }
+  s1 = wave_sum(a1);
+  s2 = wave_sum(a2);
+}
+
 template <class In>
 __global__ __launch_bounds__(512) void k_rms_act_absmax_wide(const typename In::elem* __restrict__ h,
                                                              int64_t rows, int64_t K, int64_t ld,
@@ -426,8 +458,8 @@ __global__ __launch_bounds__(512) void k_rms_act_absmax_wide(const typename In::
   }
 }
 
-// LayerNorm form of the wide path: the mean, then the squared deviations from
-// it (two fp64 passes over the row), then the slice's running maximum and
+// LayerNorm form of the wide path: the mean and variance (one pass of shifted
+// fp64 sums over the row, ln_stats), then the slice's running maximum and
 // minimum of n = fp32(fp32(h - m_t) * r_t) as ordered bits in LDS; gamma and
 // beta are applied once per column at the end (f(n) monotone, as in
 // k_ln_act_absmax).
@@ -452,18 +484,17 @@ __global__ __launch_bounds__(512) void k_ln_act_absmax_wide(const typename In::e
   }
   __syncthreads();
   const int64_t nchunk = K >> 3;
-  const double dK = (double)K;
   bool any = false;
   for (int64_t r = (int64_t)blockIdx.x * 8 + wave; r < rows; r += (int64_t)gridDim.x * 8) {
     any = true;
     const typename In::elem* row = h + r * ld;
-    const double mu = wide_row_sum<In>(row, nchunk, lane, [](double d) { return d; }) / dK;
-    const double s2 = wide_row_sum<In>(row, nchunk, lane, [mu](double d) {
-      const double e = d - mu;
-      return e * e;
-    });
-    const float mt = (float)mu;
-    const float rt = (float)(1.0 / sqrt(s2 / dK + (double)eps));
+    // the norm's statistics in one pass, shifted by the row's first element
+    float v0[8];
+    In::load8(row, v0);
+    double s1, s2;
+    wide_row_shifted_sums<In>(row, nchunk, lane, (double)v0[0], s1, s2);
+    float mt, rt;
+    ln_stats((double)v0[0], s1, s2, K, eps, mt, rt);
     for (int ch = lane; ch < (cw >> 3); ch += 64) {
       float v[8];
       In::load8(row + c_lo + (int64_t)ch * 8, v);
