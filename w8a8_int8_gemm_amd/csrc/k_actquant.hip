@@ -517,9 +517,9 @@ __global__ __launch_bounds__(256) void k_quant_act_row(const typename In::elem* 
 //   shifted by the row's first element, ln_stats), x^ =
 //   fp32(fp32(fp32(h - m_t) * r_t) * gamma'_k) +
 //   beta'_k, then the per-token INT8 quantizer above.
-// K <= 4096: one token per wave, the row's raw values in
+// K <= 2048: one token per wave, the row's raw values in
 // VGPRs from the load to the store; gamma' and beta' come through the caches
-// (every token reads the same K floats).
+// (every token reads the same K floats).  Wider rows: k_quant_act_ln_row.
 // ---------------------------------------------------------------------------
 template <class In, int NV>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void k_quant_act_ln(
@@ -908,6 +908,17 @@ static void quant_act_ln_t(const void* x, int64_t T, int64_t K, int64_t ld, cons
                            const float* b, float eps, int8_t* xq, float* xscale, float* mrow,
                            float* rrow, hipStream_t st) {
   const int64_t nchunk = K / 8;
+#define SQ_LNR(NC)                                                                            \
+  hipLaunchKernelGGL((k_quant_act_ln_row<In, NC>), dim3((unsigned)T), dim3(256), 0, st,      \
+                     (const typename In::elem*)x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow)
+  // Rows of 2049-4096 values: a workgroup per token (gamma' and beta' come
+  // through the caches either way, and four waves share each row's chain).
+  // µs, wave / workgroup per token, 4096 values: 16 tokens 8.3 / 4.7, 256
+  // 8.5 / 5.1, 1024 9.1 / 6.3, 2048 10.7 / 9.5, 8192 34.7 / 30.5.
+  if (nchunk > 256 && nchunk <= 512) {
+    SQ_LNR(2);
+    return;
+  }
   if (nchunk <= 64) quant_act_ln_nv<In, 1>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
   else if (nchunk <= 128) quant_act_ln_nv<In, 2>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
   else if (nchunk <= 256) quant_act_ln_nv<In, 4>(x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow, st);
@@ -915,17 +926,14 @@ static void quant_act_ln_t(const void* x, int64_t T, int64_t K, int64_t ld, cons
   else if (nchunk <= 2048) {   // wider rows: a workgroup per token, chunks per
                                // thread sized to the row
     const int nc = (int)((nchunk + 255) / 256);
-#define SQ_LNR(NC)                                                                            \
-  hipLaunchKernelGGL((k_quant_act_ln_row<In, NC>), dim3((unsigned)T), dim3(256), 0, st,      \
-                     (const typename In::elem*)x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow)
     if (nc <= 3) SQ_LNR(3);
     else if (nc == 4) SQ_LNR(4);
     else if (nc <= 6) SQ_LNR(6);
     else SQ_LNR(8);
-#undef SQ_LNR
   } else
     hipLaunchKernelGGL((k_quant_act_ln_wide<In>), dim3((unsigned)T), dim3(256), 0, st,
                        (const typename In::elem*)x, T, K, ld, g, b, eps, xq, xscale, mrow, rrow);
+#undef SQ_LNR
 }
 
 void launch_quant_act_ln(const void* x, bool bf16, int64_t T, int64_t K, int64_t ld,
