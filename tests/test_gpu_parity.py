@@ -172,13 +172,13 @@ def test_quant_weight_zero_column():
 # ---------------------------------------------------------------------------
 
 # K past 8192: a workgroup per token, the row in registers up to 16384 (whole
-# and ragged chunk counts), three passes over the row beyond; up to 256 tokens
+# and ragged chunk counts), three passes over the row beyond; up to 4096 tokens
 # of 4096-16384 values also take a workgroup per token (both sides of that
-# bound at 256 / 257 tokens)
+# bound at 4096 / 4097 tokens)
 QACT_CASES = [(37, 256, "f32"), (300, 4096, "bf16"), (129, 8192, "bf16"), (3, 320, "bf16"),
               (5, 16384, "bf16"), (64, 1024, "f32"), (11, 14336, "bf16"), (4, 8256, "bf16"),
-              (7, 10304, "f32"), (3, 24576, "bf16"), (256, 4096, "bf16"), (257, 4096, "bf16"),
-              (200, 4096, "f32"), (16, 12288, "bf16")]
+              (7, 10304, "f32"), (3, 24576, "bf16"), (256, 4096, "bf16"), (1000, 4096, "bf16"),
+              (200, 4096, "f32"), (16, 12288, "bf16"), (4096, 4096, "bf16"), (4097, 4096, "bf16")]
 
 
 @pytest.mark.parametrize("norm", [False, True])

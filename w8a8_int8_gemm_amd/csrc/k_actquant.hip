@@ -442,6 +442,24 @@ __global__ __launch_bounds__(256) void k_quant_act_row(const typename In::elem* 
     const int ch = c * 256 + threadIdx.x;
     raw[c] = In::raw8_nt(row + (ch < nchunk ? ch : 0) * 8);   // read once
   }
+  // gamma_f of the thread's chunks, two 16-byte loads each, in flight with
+  // the row (read element by element, each load waited for in turn, they
+  // cost 2048 x 4096 19.8 -> 7.0 us)
+  f32x4 gv[NC][2];
+  if (gamma_f != nullptr) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int ch = c * 256 + threadIdx.x;
+      const float* gp = gamma_f + (ch < nchunk ? ch : 0) * 8;
+      gv[c][0] = *reinterpret_cast<const f32x4*>(gp);
+      gv[c][1] = *reinterpret_cast<const f32x4*>(gp + 4);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) gv[c][0] = gv[c][1] = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+  }
+  // (keep every load here, ahead of their first use)
+  __builtin_amdgcn_sched_barrier(0);
   float rt = 1.0f;
   if (NORM) {
     double ss = 0.0;
@@ -473,7 +491,7 @@ __global__ __launch_bounds__(256) void k_quant_act_row(const typename In::elem* 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float t = NORM ? v[i] * rt : v[i];
-      xh[c][i] = gamma_f ? t * gamma_f[(ch < nchunk ? ch : 0) * 8 + i] : t;
+      xh[c][i] = t * (i < 4 ? gv[c][0][i] : gv[c][1][i - 4]);   // exact when gamma_f is NULL
     }
     if (ch < nchunk)
 #pragma unroll
@@ -814,13 +832,15 @@ static void quant_act_t(const void* x, int64_t T, int64_t K, int64_t ld, const f
   hipLaunchKernelGGL((k_quant_act_row<In, NC, NORM, STATIC, QF>), dim3((unsigned)T), dim3(256), \
                      0, st, (const typename In::elem*)x, T, K, ld, gamma_f, eps, sscale, xq,   \
                      xscale, rrow)
-  // Few tokens of 4096-16384 values: a workgroup per token (four waves share
-  // the row, gamma_f through the caches) instead of a wave per token, which
-  // leaves most of the chip idle and each wave a long serial row (µs, one
-  // wave / workgroup per token: 16 x 8192 8.1 / 6.5, 64 x 4096 5.5 / 4.8,
-  // 256 x 4096 5.7 / 5.1, 64 x 14336 13.5 / 10.3; from 512 tokens up the
-  // wave per token wins: 512 x 4096 RMSNorm 7.5 / 7.7, 1024 x 4096 6.7 / 10.7)
-  if (T <= 256 && nchunk >= 512 && nchunk <= 2048) {
+  // Up to 4096 tokens of 4096-16384 values: a workgroup per token (four
+  // waves share the row, gamma_f through the caches) instead of a wave per
+  // token, which leaves much of the chip idle at few tokens and gives each
+  // wave a long serial row (µs, one wave / workgroup per token: 16 x 8192
+  // 6.5 / 4.2, 512 x 4096 RMSNorm 7.3 / 4.5, 1024 x 4096 6.6 / 4.5, 2048 x
+  // 4096 7.6 / 7.0, 4096 x 4096 12.3 / 12.1, 1024 x 14336 RMSNorm 23.0 /
+  // 13.9); at 8192 tokens the wave per token, which stages gamma_f once per
+  // eight tokens, wins (8192 x 4096 20.5 / 21.2)
+  if (T <= 4096 && nchunk >= 512 && nchunk <= 2048) {
     if (nchunk <= 512) SQ_QAR(2);
     else if (nchunk <= 1024) SQ_QAR(4);
     else if (nchunk <= 1536) SQ_QAR(6);
