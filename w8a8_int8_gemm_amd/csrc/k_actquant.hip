@@ -736,6 +736,9 @@ __global__ __launch_bounds__(256) void k_quant_act_ln_row(
     const int ch = c * 256 + threadIdx.x;
     raw[c] = In::raw8_nt(row + (ch < nchunk ? ch : 0) * 8);   // read once
   }
+  // (every row load issued before the first is used: otherwise the scheduler
+  // waits for each chunk before issuing the next; 8192 x 4096 33.1 -> 32.0 us)
+  __builtin_amdgcn_sched_barrier(0);
   auto block_sum = [&](double v) {
     v = wave_sum(v);
     __syncthreads();
