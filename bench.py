@@ -41,6 +41,8 @@ if ROOT not in sys.path:
 
 METRIC = "W8A8 smoothed linear TOPS + % of MI355X INT8 MFMA peak (T=8192,K=N=4096)"
 PEAK_INT8_TOPS = 5000.0     # MI355X dense INT8 MFMA, 5.0 POP/s
+PEAK_SCLK_GHZ = 2.4         # the shader clock that peak is quoted at
+N_XCD, N_SIMD = 8, 1024     # MI355X: 8 XCDs, 256 compute units x 4 SIMDs
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA, 5.0 PFLOP/s
 WORKLOAD = "qproj_prefill"
@@ -147,17 +149,32 @@ def _kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(gemm_launch_bytes_alg: float):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
+def _counters():
+    """The committed rocprofv3 counter record of the GEMM, if it was taken on
+    the current kernel source; else {}."""
     try:
         with open(COUNTERS) as f:
             c = json.load(f)
     except (OSError, ValueError):
-        return None
-    if c.get("kernel_source_sha256_16") != _kernel_hash():
-        return None
-    return c.get("hbm_bytes_per_launch")
+        return {}
+    return c if c.get("kernel_source_sha256_16") == _kernel_hash() else {}
+
+
+def _traffic(gemm_launch_bytes_alg: float):
+    """HBM bytes per GEMM launch from the committed counter record, or None."""
+    return _counters().get("hbm_bytes_per_launch")
+
+
+def _clock_fields(achieved_tops: float) -> dict:
+    """The shader clock the counter pass observed over a GEMM launch
+    (GRBM_GUI_ACTIVE cycles per XCD / launch time), the INT8 peak at that
+    clock, this run's fraction of it, and the share of cycles MFMA-busy."""
+    c = _counters()
+    if "sclk_ghz" not in c:
+        return {"sclk_ghz": None}
+    peak = PEAK_INT8_TOPS * c["sclk_ghz"] / PEAK_SCLK_GHZ
+    return {"sclk_ghz": c["sclk_ghz"], "peak_at_sclk": peak, "frac_at_sclk": achieved_tops / peak,
+            "mfma_busy": c.get("mfma_busy")}
 
 
 def _rocpd_rows(db):
@@ -183,6 +200,7 @@ def _short(name: str) -> str:
 def rocpd_summary(dbs: str, counters_json=None) -> None:
     """Text summary of rocprofv3 result databases (durations in microseconds)."""
     fetch = write = copy_fetch = copy_write = None
+    grbm = mfma = gemm_us = None
     for db in dbs.split(","):
         rows = _rocpd_rows(db)
         print(f"# {db}")
@@ -200,16 +218,27 @@ def rocpd_summary(dbs: str, counters_json=None) -> None:
                 copy_fetch = v * 1024.0
             if "neg_kernel" in kn and cn == "WRITE_SIZE":
                 copy_write = v * 1024.0
+            if "k_gemm_w8a8<256, 256" in kn and cn == "GRBM_GUI_ACTIVE":
+                grbm, gemm_us = v, d / 1e3
+            if "k_gemm_w8a8<256, 256" in kn and cn == "SQ_VALU_MFMA_BUSY_CYCLES":
+                mfma = v
     if counters_json and fetch is not None and write is not None and copy_fetch and copy_write:
         probe = float(os.environ.get("COPY_PROBE_BYTES", 256 << 20))
         ff, wf = probe / copy_fetch, probe / copy_write
         rec = {"kernel_source_sha256_16": _kernel_hash(), "fetch_factor": ff, "write_factor": wf,
                "fetch_bytes_per_launch": fetch * ff, "write_bytes_per_launch": write * wf,
                "hbm_bytes_per_launch": fetch * ff + write * wf}
+        if grbm and mfma and gemm_us:
+            cyc = grbm / N_XCD                          # GPU cycles per XCD over a launch
+            rec["sclk_ghz"] = cyc / (gemm_us * 1e3)
+            rec["mfma_busy"] = mfma / N_SIMD / cyc
         with open(counters_json, "w") as f:
             json.dump(rec, f, indent=1)
         print(f"# scale factors: fetch {ff:.3f} write {wf:.3f}; GEMM HBM bytes per launch "
               f"{rec['hbm_bytes_per_launch'] / 2**20:.1f} MiB -> {counters_json}")
+        if "sclk_ghz" in rec:
+            print(f"# GEMM: {rec['sclk_ghz']:.2f} GHz average shader clock, "
+                  f"{rec['mfma_busy']:.1%} of cycles MFMA-busy")
 
 
 def alpha_sweep(sq, torch, inp, wl, x_cal, x, w, bias, dev, sample=256):
@@ -913,6 +942,7 @@ def main():
     g_ach = ops / gemm_s / 1e12
     roofline = {"bound": "mfma", "achieved": g_ach, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                 "frac": g_ach / PEAK_INT8_TOPS, "traffic": _traffic(T * K + N * K + 2.0 * T * N),
+                **_clock_fields(g_ach),
                 "kernel": "k_gemm_w8a8 (sq_gemm_w8a8)",
                 "algorithmic": f"2*T*K*N = {ops:.4g} int8 ops per launch"}
     linear_s = (kern_ms["quant_act"] + kern_ms["gemm"]) * 1e-3

@@ -35,3 +35,23 @@ def test_committed_gemm_counters_match_the_gemm_source():
     assert rec["kernel_source_sha256_16"] == bench._kernel_hash(), (
         "k_gemm.hip changed since the FETCH_SIZE / WRITE_SIZE passes: retake them")
     assert rec["hbm_bytes_per_launch"] > 112 * 2**20   # at least the algorithmic bytes
+
+
+def test_clock_fields_from_the_counter_record(monkeypatch):
+    """The roofline's clock fields: the INT8 peak scaled to the observed shader
+    clock, and the run's fraction of it; absent record -> sclk_ghz None."""
+    import bench
+    monkeypatch.setattr(bench, "_counters", lambda: {"sclk_ghz": 1.8, "mfma_busy": 0.67})
+    f = bench._clock_fields(2250.0)
+    assert abs(f["peak_at_sclk"] - 5000.0 * 1.8 / 2.4) < 1e-9
+    assert abs(f["frac_at_sclk"] - 2250.0 / 3750.0) < 1e-12
+    assert f["mfma_busy"] == 0.67
+    monkeypatch.setattr(bench, "_counters", lambda: {})
+    assert bench._clock_fields(2250.0) == {"sclk_ghz": None}
+
+
+def test_committed_counter_record_has_a_plausible_clock():
+    import bench
+    c = bench._counters()
+    assert 1.0 < c["sclk_ghz"] <= bench.PEAK_SCLK_GHZ
+    assert 0.0 < c["mfma_busy"] <= 1.0
