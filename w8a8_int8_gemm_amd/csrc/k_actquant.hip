@@ -414,10 +414,11 @@ __global__ __launch_bounds__(256) void k_quant_act_wide(const typename In::elem*
 }
 
 // ---------------------------------------------------------------------------
-// Rows of up to 2048 chunks (16384 bf16 or fp32 values) that the one-wave
-// kernel does not take: one workgroup of 256 threads per token with the row in
-// registers, NC chunks per thread (chunk c * 256 + thread), every load issued
-// at once; x^ is formed once, and the maximum and the codes come from those
+// Rows of 512-2048 chunks (4096-16384 values) at up to 4096 tokens, and wider
+// rows up to 2048 chunks that the one-wave kernel does not take: one workgroup
+// of 256 threads per token with the row in registers, NC chunks per thread
+// (chunk c * 256 + thread), every load of the row and of gamma_f issued at
+// once; x^ is formed once, and the maximum and the codes come from those
 // registers.  The same fp32 operations per element as the kernels above.
 // ---------------------------------------------------------------------------
 template <class In, int NC, bool NORM, bool STATIC, int QF>
@@ -858,10 +859,9 @@ static void quant_act_t(const void* x, int64_t T, int64_t K, int64_t ld, const f
   else if (nchunk <= 512) SQ_QA(8);
   else if (nchunk <= 1024) SQ_QA(16);
   else if (In::kBytes == 2 && nchunk <= 2048 && gamma_f != nullptr) {
-    // bf16 rows up to 16384 in VGPRs, gamma_f staged once per workgroup: a
-    // workgroup per token would read gamma_f per token through the caches
-    // (104 against 25 us, 2048 x 14336), but with no gamma_f its four waves
-    // per token win
+    // past 4096 tokens, bf16 rows up to 16384 in VGPRs with gamma_f staged in
+    // LDS once per eight tokens, rather than read per token through the
+    // caches; with no gamma_f the workgroup per token below
     if constexpr (In::kBytes == 2) SQ_QA(32);
   } else if (nchunk <= 2048) {
     // a workgroup per token with the row in registers, chunks per thread
