@@ -183,9 +183,16 @@ def _rocpd_rows(db):
     names = {r[0] for r in con.execute("select name from sqlite_master where type='view'")}
     out = {"trace": [], "pmc": []}
     if "kernels" in names:
-        out["trace"] = list(con.execute(
-            "select name, count(*), avg(duration), min(duration), max(duration) from kernels "
-            "group by name order by sum(duration) desc"))
+        durs = {}
+        for n, d in con.execute("select name, duration from kernels"):
+            durs.setdefault(n, []).append(d)
+        rows = []
+        for n, ds in durs.items():
+            ds.sort()
+            m = len(ds) // 2
+            med = ds[m] if len(ds) % 2 else 0.5 * (ds[m - 1] + ds[m])
+            rows.append((n, len(ds), sum(ds) / len(ds), ds[0], ds[-1], med, sum(ds)))
+        out["trace"] = [r[:6] for r in sorted(rows, key=lambda r: -r[6])]
     if "counters_collection" in names:
         out["pmc"] = list(con.execute(
             "select kernel_name, counter_name, avg(value), count(*), avg(duration) "
@@ -205,9 +212,11 @@ def rocpd_summary(dbs: str, counters_json=None) -> None:
         rows = _rocpd_rows(db)
         print(f"# {db}")
         if rows["trace"] and not rows["pmc"]:
-            print(f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
-            for n, c, a, lo, hi in rows["trace"]:
-                print(f"{_short(n):70s} {c:6d} {a / 1e3:10.2f} {lo / 1e3:10.2f} {hi / 1e3:10.2f}")
+            print(f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} "
+                  f"{'median_us':>10s}")
+            for n, c, a, lo, hi, med in rows["trace"]:
+                print(f"{_short(n):70s} {c:6d} {a / 1e3:10.2f} {lo / 1e3:10.2f} {hi / 1e3:10.2f} "
+                      f"{med / 1e3:10.2f}")
         for kn, cn, v, c, d in rows["pmc"]:
             print(f"{_short(kn):70s} {cn:28s} {v:18.1f}  n={c:<4d} avg_us={d / 1e3:.2f}")
             if "k_gemm_w8a8" in kn and cn == "FETCH_SIZE":

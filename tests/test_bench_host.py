@@ -55,3 +55,25 @@ def test_committed_counter_record_has_a_plausible_clock():
     c = bench._counters()
     assert 1.0 < c["sclk_ghz"] <= bench.PEAK_SCLK_GHZ
     assert 0.0 < c["mfma_busy"] <= 1.0
+
+
+def test_rocpd_summary_trace_table(tmp_path, capsys):
+    """The kernel-trace summary: calls, mean, min, max and median per kernel,
+    slowest total first (a database with the kernels view rocprofv3 writes)."""
+    import sqlite3
+    import bench
+    db = tmp_path / "t.db"
+    con = sqlite3.connect(db)
+    con.execute("create table k(name text, duration real)")
+    con.executemany("insert into k values (?, ?)",
+                    [("a", 1000.0), ("a", 3000.0), ("a", 2600.0), ("b", 500.0), ("b", 700.0)])
+    con.execute("create view kernels as select * from k")
+    con.commit()
+    con.close()
+    bench.rocpd_summary(str(db))
+    lines = capsys.readouterr().out.splitlines()
+    assert lines[1].split()[-1] == "median_us"
+    a = lines[2].split()
+    assert a[0] == "a" and a[1:] == ["3", "2.20", "1.00", "3.00", "2.60"]
+    b = lines[3].split()
+    assert b[0] == "b" and b[1:] == ["2", "0.60", "0.50", "0.70", "0.60"]
